@@ -1,0 +1,134 @@
+"""Narrow storage formats used by the layer -- oracle side (test infrastructure).
+
+* OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits; no
+  infinities; 0x7F/0xFF are NaN; largest finite magnitude 448.  The row-FP8
+  card ("Inkling 2 Small FP8 for AMD MI300X", "Precision and files") uses the
+  FNUZ flavour with max 240 on MI300X; the flavour native to gfx950 is OCP, so
+  the divisor used throughout is 448 (reading recorded in the design notes).
+* bfloat16: the top 16 bits of an IEEE binary32.
+* INT4: signed codes in [-8, 7] stored as nibble = code + 8, eight consecutive
+  codes per little-endian 32-bit word with the first code in the least
+  significant nibble ("wstewart3/Inkling-Small-W4A8-G128", §7 "Recover and
+  physically pack INT4", packing bullets).  Viewed as bytes this is two codes
+  per byte, first code in the low nibble.
+
+Rounding is round-to-nearest-even everywhere (the pages do not name a rounding
+mode; RNE is the IEEE default).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+E4M3_NAN_CODES = (0x7F, 0xFF)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 byte, as float64 (NaN for 0x7F / 0xFF).
+
+    normal (exponent field e >= 1): (-1)^s * 2^(e-7) * (1 + m/8)
+    subnormal (e == 0):             (-1)^s * 2^(-6) * (m/8)
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    val = np.where(s == 1, -mag, mag)
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return val.astype(np.float64)
+
+
+# all 127 non-negative finite values, indexed by their code 0x00..0x7E (ascending)
+_E4M3_POS = e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest E4M3 code to each finite value, ties to the even code, saturating.
+
+    The representable non-negative values in increasing order have increasing
+    codes 0x00..0x7E, and the least significant code bit is the least significant
+    mantissa bit, so "ties to even" means "ties to the even code".  Magnitudes at
+    or above 448 saturate to 448 (0x7E) because E4M3 has no infinity.  The sign
+    bit is kept, so a negative value that rounds to zero encodes as 0x80.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    if np.isnan(v).any():
+        raise ValueError("e4m3_encode: NaN input")
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    hi = np.searchsorted(_E4M3_POS, a, side="left")          # first table value >= a
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    exact = _E4M3_POS[hi] == a
+    pick_hi = exact | (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    neg = np.signbit(v)
+    return np.where(neg, code | 0x80, code).astype(np.uint8)
+
+
+def fp32(v) -> np.ndarray:
+    """Round to IEEE binary32 (RNE) and return as float64."""
+    return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def bf16_round(v) -> np.ndarray:
+    """Round float64 values to the bfloat16 grid, RNE, in one step (no double rounding).
+
+    v = m * 2^e with 0.5 <= |m| < 1; bfloat16 keeps 8 significant bits, so the
+    result is rint(m * 2^8) * 2^(e-8).  (Overflow and subnormals do not occur for
+    the magnitudes this layer produces.)
+    """
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def bf16_bits(v) -> np.ndarray:
+    """uint16 bit pattern of values already on the bfloat16 grid."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_from_bits(u) -> np.ndarray:
+    u = np.asarray(u, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------- INT4
+INT4_MIN, INT4_MAX = -8, 7
+GROUP = 128
+
+
+def pack_int4(codes) -> np.ndarray:
+    """Codes int [..., K] in [-8, 7] -> bytes uint8 [..., K/2].
+
+    nibble = code + 8; byte b holds codes 2b (low nibble) and 2b+1 (high nibble),
+    which is the little-endian byte view of eight codes per 32-bit word with the
+    first code in the least significant nibble.
+    """
+    c = np.asarray(codes)
+    if c.shape[-1] % 2:
+        raise ValueError("pack_int4: K must be even")
+    if (c < INT4_MIN).any() or (c > INT4_MAX).any():
+        raise ValueError("pack_int4: code outside [-8, 7]")
+    nib = (c.astype(np.int64) + 8).astype(np.uint8)
+    return (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed) -> np.ndarray:
+    """Bytes uint8 [..., K/2] -> codes int8 [..., K] (inverse of pack_int4)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    lo = (p & 0xF).astype(np.int8) - 8
+    hi = (p >> 4).astype(np.int8) - 8
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def int32_words(packed) -> np.ndarray:
+    """Little-endian 32-bit words of packed INT4 bytes ([..., K/2] -> [..., K/8])."""
+    p = np.ascontiguousarray(np.asarray(packed, dtype=np.uint8))
+    return p.view("<u4").astype(np.uint32)

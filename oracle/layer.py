@@ -1,0 +1,355 @@
+"""The quantized MoE expert layer -- oracle side (TEST INFRASTRUCTURE ONLY).
+
+Plain NumPy, float64 for every value that is not stored in a narrow format.
+The oracle *emulates the quantized pipeline exactly*: it reproduces every
+integer and every stored narrow value (expert ids, permutation, INT4 codes and
+their fp32 scales, E4M3 codes and their fp32 scales, every bfloat16 rounding
+point) and computes every dot product in float64 from those exact values.
+
+Sources (page title, section):
+  * "wstewart3/Inkling-Small-W4A8-G128", §1 settings table: symmetric INT4
+    weights in groups of 128; dynamic FP8 input activations, one scale per
+    token; 256 routed + 2 shared experts; hidden 4096, expert width 2048.
+  * same page, §6 "Why this checkpoint also needed recovery": a [2048, 4096]
+    projection carries scales [2048, 32], i.e. one scale per (output row,
+    128-wide group along the input dimension).
+  * same page, §7 "Recover and physically pack INT4": code range [-8, 7] and the
+    nibble packing (see ``formats``).
+  * same page, intro: INT4 weights with FP8 activations so that the FP8 matrix
+    cores stay in use -- the products are FP8 x INT4, accumulated per group.
+  * "Inkling-512k-NVFP4-AQLM-hybrid", intro: 256 routed experts per layer, 6
+    active; "On-disk tensor format": w13 = fused gate|up, w2 = down.
+  * "Inkling 2 Small FP8 for AMD MI300X", "Precision and files": expert weights
+    FP8 with one fp32 scale per output channel, scale = max|row| / fmax, and
+    dynamic per-token FP8 activations; scale tensor [n_experts, out_channels].
+
+Readings where the pages are silent (each listed in the design notes):
+  routing is softmax over the k selected logits (softmax-then-top-k with
+  renormalization), ties broken toward the lower expert index; the FP8 scale
+  divisor is 448 (OCP E4M3 on gfx950); INT4 scale = max|group| / 7 with RNE
+  rounding and clamp to [-8, 7]; scales are fp32; the gate/up epilogue is
+  h = bf16(silu(g) * u) rounded once; o and y are bf16; the combine is
+  y_t = bf16(sum_j w_tj * o_tj + shared_t) summed in slot order.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import (E4M3_MAX, GROUP, bf16_round, e4m3_decode, e4m3_encode,
+                      fp32, pack_int4, unpack_int4)
+
+# ----------------------------------------------------------------- a1: routing
+
+
+def route_topk(logits, k: int, bias=None, renormalize: bool = True):
+    """Top-k expert selection and routing weights.
+
+    s = logits (+ bias, one fp32 addition); the k largest s per token, ties
+    broken toward the lower expert index, listed best first.  Weights:
+    renormalize=True  -> w_j = exp(s_j - s_max) / sum over the k selected
+    renormalize=False -> w_j = exp(s_j - s_max) / sum over all E experts
+    Returns ids int32 [T, k] and weights float64 [T, k].
+    """
+    s = np.asarray(logits, dtype=np.float32)
+    if bias is not None:
+        s = (s + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
+    s = s.astype(np.float64)
+    T, E = s.shape
+    if not 1 <= k <= E:
+        raise ValueError("k out of range")
+    # stable sort on -s keeps equal scores in increasing expert order
+    order = np.argsort(-s, axis=1, kind="stable")
+    ids = order[:, :k].astype(np.int32)
+    sel = np.take_along_axis(s, ids.astype(np.int64), axis=1)
+    smax = s.max(axis=1, keepdims=True)
+    num = np.exp(sel - smax)
+    den = num.sum(axis=1, keepdims=True) if renormalize else np.exp(s - smax).sum(axis=1, keepdims=True)
+    return ids, num / den
+
+# ------------------------------------------------ a2 / a5: per-token FP8 quant
+
+
+def quant_fp8_per_token(x):
+    """Dynamic per-row FP8 quantization.
+
+    amax_t = max_k |x[t,k]|; s_t = fl32(amax_t / 448); q = E4M3(fl32(x / s_t)).
+    Both divisions are IEEE binary32 divisions (the decision that produces an
+    integer code is taken in the kernel's precision).  A zero row gets s = 0 and
+    all codes 0x00.  x must hold values exactly representable in fp32.
+    Returns q uint8 [M, K] and s float32 [M].
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x32)):
+        raise ValueError("non-finite input")
+    amax = np.abs(x32).max(axis=1)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    q = np.zeros(x32.shape, dtype=np.uint8)
+    nz = s > 0
+    if nz.any():
+        ratio = (x32[nz] / s[nz][:, None]).astype(np.float32)
+        q[nz] = e4m3_encode(ratio)
+    return q, s
+
+
+def dequant_fp8_rows(q, s) -> np.ndarray:
+    """q * s per row, float64 (used by the brute-force pins)."""
+    return e4m3_decode(q) * np.asarray(s, dtype=np.float64)[:, None]
+
+# ------------------------------------------------------ a9: INT4 g128 packing
+
+
+def quantize_int4_g128(w):
+    """Symmetric INT4 quantization in groups of 128 along the last (input) axis.
+
+    For each row n and group g: a = max|W[n, g]|; s = fl32(a / 7);
+    c = clamp(rint(fl32(W / s)), -8, 7) with rint = round half to even;
+    a zero group gets s = 0 and codes 0.
+    Returns codes int8 [rows, K] and scales float32 [rows, K/128].
+    """
+    w32 = np.asarray(w, dtype=np.float32)
+    rows, K = w32.shape
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    G = K // GROUP
+    wg = w32.reshape(rows, G, GROUP)
+    a = np.abs(wg).max(axis=2)
+    s = (a / np.float32(7.0)).astype(np.float32)
+    c = np.zeros(wg.shape, dtype=np.int8)
+    nz = s > 0
+    ratio = (wg[nz] / s[nz][:, None]).astype(np.float32)
+    c[nz] = np.clip(np.rint(ratio.astype(np.float64)), -8, 7).astype(np.int8)
+    return c.reshape(rows, K), s
+
+
+def pack_int4_g128(w):
+    """quantize_int4_g128 followed by the storage packing: bytes [rows, K/2], scales."""
+    codes, s = quantize_int4_g128(w)
+    return pack_int4(codes), s
+
+# ------------------------------------------------ a8 weights: row-scaled FP8
+
+
+def quant_fp8_per_row_weights(w):
+    """Row-scaled FP8 expert weights: one fp32 scale per output channel.
+
+    Identical arithmetic to the per-token activation quantization applied to
+    the rows of W [rows, K]: s_row = fl32(max|row| / 448), wq = E4M3(fl32(W / s)).
+    """
+    return quant_fp8_per_token(w)
+
+# -------------------------------------------------------------- a3: permute
+
+
+def permute_plan(ids, E: int):
+    """Group the (token, slot) rows by expert.
+
+    Row r = t*k + j carries expert ids[t, j].  Rows are ordered by expert, and
+    within an expert by increasing r (a stable counting sort).
+      counts[e]        rows routed to expert e
+      offsets[E+1]     exclusive prefix sum of counts
+      sorted_rows[p]   the row r placed at position p
+      row_pos[r]       the position p of row r (inverse permutation)
+      active           experts with counts > 0, increasing
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    if flat.size and (flat.min() < 0 or flat.max() >= E):
+        raise ValueError("expert id out of range")
+    counts = np.bincount(flat, minlength=E).astype(np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    sorted_rows = np.argsort(flat, kind="stable").astype(np.int64)
+    row_pos = np.empty_like(sorted_rows)
+    row_pos[sorted_rows] = np.arange(flat.size)
+    active = np.nonzero(counts)[0]
+    return {"counts": counts, "offsets": offsets, "sorted_rows": sorted_rows,
+            "row_pos": row_pos, "active": active}
+
+
+def gather_rows(x_q, x_s, sorted_rows, k: int):
+    """xp_q[p] = x_q[sorted_rows[p] // k], xp_s likewise."""
+    tok = np.asarray(sorted_rows) // k
+    return np.asarray(x_q)[tok], np.asarray(x_s)[tok]
+
+# --------------------------------------------------- a4 / a6: grouped GEMMs
+
+
+def w4a8_rows(a_q, a_s, experts, codes_of, scales_of):
+    """W4A8 expert products for a list of rows.
+
+    For row p routed to expert e = experts[p] and output column n:
+      P_g  = sum_{k in group g} dec(a_q[p, k]) * c[e, n, k]     (exact in fp64)
+      acc  = sum_g s_w[e, n, g] * P_g
+      out  = s_a[p] * acc
+    codes_of(e) -> int codes [N, K]; scales_of(e) -> fp32 [N, K/128].
+    Returns float64 [rows, N].
+    """
+    a_q = np.asarray(a_q)
+    experts = np.asarray(experts)
+    a = e4m3_decode(a_q)                                         # [r, K]
+    out = None
+    for e in np.unique(experts):
+        rows = np.nonzero(experts == e)[0]
+        c = np.asarray(codes_of(int(e)), dtype=np.float64)       # [N, K]
+        s_w = np.asarray(scales_of(int(e)), dtype=np.float64)    # [N, G]
+        N, K = c.shape
+        G = K // GROUP
+        A = a[rows].reshape(len(rows), G, GROUP).transpose(1, 0, 2)   # [G, r, 128]
+        C = c.reshape(N, G, GROUP).transpose(1, 2, 0)                 # [G, 128, N]
+        partial = np.matmul(A, C)                                     # [G, r, N]
+        acc = np.einsum("grn,ng->rn", partial, s_w)
+        if out is None:
+            out = np.zeros((a_q.shape[0], N), dtype=np.float64)
+        out[rows] = np.asarray(a_s, dtype=np.float64)[rows][:, None] * acc
+    return out
+
+
+def fp8row_rows(a_q, a_s, experts, wq_of, srow_of):
+    """Row-scaled FP8 expert products for a list of rows.
+
+    out[p, n] = s_a[p] * s_row[e, n] * sum_k dec(a_q[p, k]) * dec(wq[e, n, k]).
+    """
+    a_q = np.asarray(a_q)
+    experts = np.asarray(experts)
+    a = e4m3_decode(a_q)
+    out = None
+    for e in np.unique(experts):
+        rows = np.nonzero(experts == e)[0]
+        wdec = e4m3_decode(wq_of(int(e)))                         # [N, K]
+        srow = np.asarray(srow_of(int(e)), dtype=np.float64)      # [N]
+        dot = a[rows] @ wdec.T
+        if out is None:
+            out = np.zeros((a_q.shape[0], wdec.shape[0]), dtype=np.float64)
+        out[rows] = np.asarray(a_s, dtype=np.float64)[rows][:, None] * dot * srow[None, :]
+    return out
+
+# ------------------------------------------------------ a4 epilogue: SwiGLU
+
+
+def silu(z):
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def silu_mul(o13):
+    """h = bf16(silu(g) * u) with g = o13[:, :I] (gate rows first) and u = o13[:, I:].
+
+    One rounding to bfloat16; g and u themselves are not rounded.  Parity unpinned
+    beyond tolerance for the GPU side (its exp differs from float64 by ulps).
+    """
+    o13 = np.asarray(o13, dtype=np.float64)
+    I = o13.shape[1] // 2
+    return bf16_round(silu(o13[:, :I]) * o13[:, I:])
+
+# ------------------------------------------------------------- a7: combine
+
+
+def combine(o, row_pos, w, k: int, shared=None):
+    """y_t = bf16( sum_{j=0}^{k-1} w[t, j] * o[row_pos[t*k + j]] + shared_t )."""
+    o = np.asarray(o, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    T = w.shape[0]
+    rp = np.asarray(row_pos).reshape(T, k)
+    y = np.zeros((T, o.shape[1]), dtype=np.float64)
+    for j in range(k):
+        y += w[:, j:j + 1] * o[rp[:, j]]
+    if shared is not None:
+        y += np.asarray(shared, dtype=np.float64)
+    return bf16_round(y)
+
+# ------------------------------------------------------ a10: shared experts
+
+
+def shared_mlp(x, ws13, ws2):
+    """bf16 SwiGLU MLP: h = bf16(silu(x Wg^T) * (x Wu^T)); shared = bf16(h Ws2^T).
+
+    ws13 [2S, H] holds the gate rows then the up rows; ws2 [H, S].  All inputs
+    are bfloat16 values; products are accumulated in float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    o13 = x @ np.asarray(ws13, dtype=np.float64).T
+    h = silu_mul(o13)
+    return bf16_round(h @ np.asarray(ws2, dtype=np.float64).T)
+
+# ---------------------------------------------------------- the whole layer
+
+
+def moe_layer(x, logits, k: int, w13=None, w2=None, bias=None, renormalize=True,
+              packed13=None, scales13=None, packed2=None, scales2=None,
+              fp8row=False, ws13=None, ws2=None):
+    """Route -> quantize x -> permute -> gate/up GEMM + SiLU -> quantize h ->
+    down GEMM -> combine (+ shared experts).  Returns every intermediate.
+
+    Weights are given either full precision (w13 [E, 2I, H], w2 [E, H, I]) and
+    quantized here, or already quantized (packed13/scales13, packed2/scales2).
+    With fp8row=True the full-precision weights are quantized row-wise to FP8.
+    """
+    x = np.asarray(x)
+    T, H = x.shape
+    E = np.asarray(logits).shape[1]
+    res = {}
+    ids, w = route_topk(logits, k, bias=bias, renormalize=renormalize)
+    res["topk_ids"], res["topk_w"] = ids, w
+    xq, xs = quant_fp8_per_token(x)
+    res["x_q"], res["x_s"] = xq, xs
+    plan = permute_plan(ids, E)
+    res.update(plan)
+    xp_q, xp_s = gather_rows(xq, xs, plan["sorted_rows"], k)
+    res["xp_q"], res["xp_s"] = xp_q, xp_s
+    experts = np.repeat(np.arange(E), plan["counts"])
+
+    if fp8row:
+        q13, s13, q2, s2 = {}, {}, {}, {}
+        for e in plan["active"]:
+            q13[e], s13[e] = quant_fp8_per_row_weights(w13[e])
+            q2[e], s2[e] = quant_fp8_per_row_weights(w2[e])
+        o13 = fp8row_rows(xp_q, xp_s, experts, lambda e: q13[e], lambda e: s13[e])
+    else:
+        if packed13 is None:
+            c13, c2, sc13, sc2 = {}, {}, {}, {}
+            for e in plan["active"]:
+                c13[e], sc13[e] = quantize_int4_g128(w13[e])
+                c2[e], sc2[e] = quantize_int4_g128(w2[e])
+            codes13, codes2 = (lambda e: c13[e]), (lambda e: c2[e])
+            sf13, sf2 = (lambda e: sc13[e]), (lambda e: sc2[e])
+        else:
+            codes13 = lambda e: unpack_int4(packed13[e])  # noqa: E731
+            codes2 = lambda e: unpack_int4(packed2[e])  # noqa: E731
+            sf13 = lambda e: scales13[e]  # noqa: E731
+            sf2 = lambda e: scales2[e]  # noqa: E731
+        o13 = w4a8_rows(xp_q, xp_s, experts, codes13, sf13)
+    res["o13"] = o13
+    h = silu_mul(o13)
+    res["h"] = h
+    hq, hs = quant_fp8_per_token(h)
+    res["h_q"], res["h_s"] = hq, hs
+    if fp8row:
+        o = fp8row_rows(hq, hs, experts, lambda e: q2[e], lambda e: s2[e])
+    else:
+        o = w4a8_rows(hq, hs, experts, codes2, sf2)
+    o = bf16_round(o)
+    res["o"] = o
+    shared = None
+    if ws13 is not None:
+        shared = shared_mlp(x, ws13, ws2)
+        res["shared"] = shared
+    res["y"] = combine(o, plan["row_pos"], w, k, shared)
+    return res
+
+
+def unquantized_layer(x, logits, k, w13, w2, bias=None, renormalize=True):
+    """Sanity reference without any quantization (float64 throughout).  Never gates
+    a test; used to log the quantization error."""
+    x = np.asarray(x, dtype=np.float64)
+    ids, w = route_topk(logits, k, bias=bias, renormalize=renormalize)
+    T, H = x.shape
+    y = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            o13 = np.asarray(w13[e], dtype=np.float64) @ x[t]
+            I = o13.shape[0] // 2
+            h = silu(o13[:I]) * o13[I:]
+            y[t] += w[t, j] * (np.asarray(w2[e], dtype=np.float64) @ h)
+    return y
