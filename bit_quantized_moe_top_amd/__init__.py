@@ -1,0 +1,281 @@
+"""Python binding of libmoeq, the quantized MoE expert layer for MI355X (gfx950).
+
+Argument marshalling only: every function below checks dtypes/shapes, allocates
+outputs with torch (device memory and streams are all torch is used for), and
+calls the C ABI declared in include/moeq.h, which enqueues the HIP kernels on the
+current torch stream.  No computation happens here, and there is no fallback:
+if libmoeq.so is missing, importing this package raises ImportError.
+
+Build the library first:  python bit_quantized_moe_top_amd/build.py
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "lib", "MOEQ_F32", "MOEQ_BF16", "EPI_NONE", "EPI_SILU_MUL", "TILE_M",
+    "MAX_EXPERTS", "MAX_TOPK", "MoeqError", "moe_abi_version", "moe_status_string",
+    "moe_plan_size", "moe_route_topk", "quant_fp8_per_token", "moe_permute", "pack_int4_g128",
+    "moe_grouped_gemm_w4a8", "moe_grouped_gemm_fp8row", "moe_combine", "moe_shared_gemm_bf16",
+    "plan_fields", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoeq.so")
+
+MOEQ_F32, MOEQ_BF16 = 0, 1
+EPI_NONE, EPI_SILU_MUL = 0, 1
+TILE_M = 64
+MAX_EXPERTS, MAX_TOPK = 1024, 8
+PLAN_HEADER = 16
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes); the exact list of entry points in include/moeq.h
+_SIGNATURES = {
+    "moe_abi_version": (_I, []),
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_plan_size": (_SZ, [_I, _I]),
+    "moe_route_topk": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "quant_fp8_per_token": (_I, [_P, _I, _I64, _I, _I64, _P, _P, _P]),
+    "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _P, _SZ, _P]),
+    "pack_int4_g128": (_I, [_P, _I64, _I, _P, _P, _P]),
+    "moe_grouped_gemm_w4a8": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
+    "moe_grouped_gemm_fp8row": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
+    "moe_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
+    "moe_shared_gemm_bf16": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run: python bit_quantized_moe_top_amd/build.py")
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
+lib = _load()
+
+
+class MoeqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {lib.moe_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoeqError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _req(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def moe_abi_version() -> int:
+    return lib.moe_abi_version()
+
+
+def moe_status_string(status: int) -> str:
+    return lib.moe_status_string(status).decode()
+
+
+def moe_plan_size(E: int, R: int) -> int:
+    return lib.moe_plan_size(E, R)
+
+
+def plan_fields(plan: torch.Tensor, E: int, R: int) -> dict:
+    """Views of the plan's arrays (the layout documented in include/moeq.h)."""
+    max_tiles = (R + TILE_M - 1) // TILE_M + min(E, R)
+    o = PLAN_HEADER
+    f = {"header": plan[:PLAN_HEADER]}
+    for name, n in (("offsets", E + 1), ("sorted_rows", R), ("row_pos", R), ("active", E),
+                    ("tile_expert", max_tiles), ("tile_row0", max_tiles)):
+        f[name] = plan[o:o + n]
+        o += n
+    return f
+
+
+# ----------------------------------------------------------------------- calls
+def moe_route_topk(logits: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None,
+                   renormalize: bool = True, ids: Optional[torch.Tensor] = None,
+                   weights: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    _req(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    if bias is not None:
+        _req(bias, "bias", torch.float32, 1)
+    if ids is None:
+        ids = torch.empty(T, k, dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    _check("moe_route_topk", lib.moe_route_topk(_ptr(logits), _ptr(bias), T, E, k,
+                                                1 if renormalize else 0, _ptr(ids), _ptr(weights),
+                                                _stream(logits.device)))
+    return ids, weights
+
+
+def quant_fp8_per_token(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+                        scale: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _req(x, "x", x.dtype)
+    K = x.shape[-1]
+    x2 = x.reshape(-1, K)
+    M = x2.shape[0]
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    dt = MOEQ_BF16 if x.dtype == torch.bfloat16 else MOEQ_F32
+    _check("quant_fp8_per_token", lib.quant_fp8_per_token(_ptr(x2), dt, M, K, K, _ptr(q),
+                                                          _ptr(scale), _stream(x.device)))
+    return q, scale
+
+
+def moe_permute(topk_ids: torch.Tensor, E: int, x_q: Optional[torch.Tensor] = None,
+                x_s: Optional[torch.Tensor] = None, plan: Optional[torch.Tensor] = None,
+                xp_q: Optional[torch.Tensor] = None, xp_s: Optional[torch.Tensor] = None):
+    """Returns (plan int32 tensor, xp_q, xp_s) -- the last two None without x_q."""
+    _req(topk_ids, "topk_ids", torch.int32, 2)
+    T, k = topk_ids.shape
+    R = T * k
+    dev = topk_ids.device
+    nbytes = moe_plan_size(E, R)
+    if plan is None:
+        plan = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device=dev)
+    H = 0
+    if x_q is not None:
+        _req(x_q, "x_q", torch.uint8, 2)
+        _req(x_s, "x_s", torch.float32, 1)
+        H = x_q.shape[1]
+        if xp_q is None:
+            xp_q = torch.empty(R, H, dtype=torch.uint8, device=dev)
+        if xp_s is None:
+            xp_s = torch.empty(R, dtype=torch.float32, device=dev)
+    _check("moe_permute", lib.moe_permute(_ptr(topk_ids), T, k, E, _ptr(x_q), _ptr(x_s), H,
+                                          _ptr(xp_q), _ptr(xp_s), _ptr(plan), plan.numel() * 4,
+                                          _stream(dev)))
+    return plan, xp_q, xp_s
+
+
+def pack_int4_g128(w: torch.Tensor, packed: Optional[torch.Tensor] = None,
+                   scales: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """w [..., K] fp32 -> packed uint8 [..., K/2], scales fp32 [..., K/128]."""
+    _req(w, "w", torch.float32)
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    if packed is None:
+        packed = torch.empty(*w.shape[:-1], K // 2, dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(*w.shape[:-1], K // 128, dtype=torch.float32, device=w.device)
+    _check("pack_int4_g128", lib.pack_int4_g128(_ptr(w), rows, K, _ptr(packed), _ptr(scales),
+                                                _stream(w.device)))
+    return packed, scales
+
+
+def _gemm(fn_name: str, a_q, a_s, plan, E, w, w_scale, N, K, epilogue, out_dtype, out):
+    _req(a_q, "a_q", torch.uint8, 2)
+    _req(a_s, "a_s", torch.float32, 1)
+    _req(plan, "plan", torch.int32, 1)
+    R = a_q.shape[0]
+    if a_q.shape[1] != K:
+        raise ValueError("a_q has the wrong K")
+    n_out = N // 2 if epilogue == EPI_SILU_MUL else N
+    if out is None:
+        out = torch.empty(R, n_out, dtype=out_dtype, device=a_q.device)
+    odt = MOEQ_BF16 if out.dtype == torch.bfloat16 else MOEQ_F32
+    fn = getattr(lib, fn_name)
+    _check(fn_name, fn(_ptr(a_q), _ptr(a_s), _ptr(plan), E, R, _ptr(w), _ptr(w_scale), N, K,
+                       epilogue, _ptr(out), odt, _stream(a_q.device)))
+    return out
+
+
+def moe_grouped_gemm_w4a8(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Tensor,
+                          w_packed: torch.Tensor, w_scales: torch.Tensor,
+                          epilogue: int = EPI_NONE, out_dtype=torch.bfloat16,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """w_packed [E, N, K/2] uint8, w_scales [E, N, K/128] fp32."""
+    _req(w_packed, "w_packed", torch.uint8, 3)
+    _req(w_scales, "w_scales", torch.float32, 3)
+    E, N, K2 = w_packed.shape
+    if tuple(w_scales.shape) != (E, N, 2 * K2 // 128):
+        raise ValueError("w_scales shape does not match w_packed")
+    return _gemm("moe_grouped_gemm_w4a8", a_q, a_s, plan, E, w_packed, w_scales, N, 2 * K2,
+                 epilogue, out_dtype, out)
+
+
+def moe_grouped_gemm_fp8row(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Tensor,
+                            w_fp8: torch.Tensor, w_row_scale: torch.Tensor,
+                            epilogue: int = EPI_NONE, out_dtype=torch.bfloat16,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """w_fp8 [E, N, K] uint8 (E4M3 bytes), w_row_scale [E, N] fp32."""
+    _req(w_fp8, "w_fp8", torch.uint8, 3)
+    _req(w_row_scale, "w_row_scale", torch.float32, 2)
+    E, N, K = w_fp8.shape
+    if tuple(w_row_scale.shape) != (E, N):
+        raise ValueError("w_row_scale shape does not match w_fp8")
+    return _gemm("moe_grouped_gemm_fp8row", a_q, a_s, plan, E, w_fp8, w_row_scale, N, K,
+                 epilogue, out_dtype, out)
+
+
+def moe_combine(o: torch.Tensor, plan: torch.Tensor, topk_w: torch.Tensor,
+                shared: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None):
+    _req(o, "o", torch.bfloat16, 2)
+    _req(plan, "plan", torch.int32, 1)
+    _req(topk_w, "topk_w", torch.float32, 2)
+    T, k = topk_w.shape
+    H = o.shape[1]
+    if shared is not None:
+        _req(shared, "shared", torch.bfloat16, 2)
+    if y is None:
+        y = torch.empty(T, H, dtype=torch.bfloat16, device=o.device)
+    _check("moe_combine", lib.moe_combine(_ptr(o), _ptr(plan), _ptr(topk_w), _ptr(shared), T, k, H,
+                                          _ptr(y), _stream(o.device)))
+    return y
+
+
+def moe_shared_gemm_bf16(a: torch.Tensor, w: torch.Tensor, epilogue: int = EPI_NONE,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _req(a, "a", torch.bfloat16, 2)
+    _req(w, "w", torch.bfloat16, 2)
+    M, K = a.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("K mismatch")
+    if out is None:
+        out = torch.empty(M, N // 2 if epilogue == EPI_SILU_MUL else N, dtype=torch.bfloat16,
+                          device=a.device)
+    _check("moe_shared_gemm_bf16", lib.moe_shared_gemm_bf16(_ptr(a), _ptr(w), M, N, K, epilogue,
+                                                            _ptr(out), _stream(a.device)))
+    return out
+
+
+from .layer import MoELayer  # noqa: E402,F401  (composition of the calls above)

@@ -1,0 +1,172 @@
+// C ABI of libmoeq (declared in include/moeq.h): argument validation, the
+// gfx950 device check, and the kernel launches on the caller's stream.
+//
+// Validation happens before any HIP call, so argument errors are reported on a
+// machine without a GPU.  No entry point allocates, frees or synchronizes.
+#include <string.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// per-device result of the architecture check: 0 unknown, 1 gfx950, -1 other
+int g_device_ok[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOEQ_ERR_DEVICE;
+  if (dev < kMaxDevices && g_device_ok[dev] != 0) return g_device_ok[dev] > 0 ? MOEQ_OK : MOEQ_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOEQ_ERR_DEVICE;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_device_ok[dev] = ok ? 1 : -1;
+  return ok ? MOEQ_OK : MOEQ_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int launch_status(hipError_t err) { return err == hipSuccess ? MOEQ_OK : MOEQ_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOEQ_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOEQ_OK: return "ok";
+    case MOEQ_ERR_INVALID_ARG: return "invalid argument";
+    case MOEQ_ERR_UNSUPPORTED: return "unsupported size";
+    case MOEQ_ERR_WORKSPACE: return "plan buffer too small";
+    case MOEQ_ERR_DEVICE: return "no gfx950 device";
+    case MOEQ_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_plan_size(int E, int R) {
+  if (E <= 0 || R < 0) return 0;
+  return moeq::plan_words(E, R) * sizeof(int32_t);
+}
+
+int moe_route_topk(const float* logits, const float* bias, int T, int E, int k, int renormalize,
+                   int32_t* topk_ids, float* topk_w, void* stream) {
+  if (T < 0 || E <= 0 || k <= 0) return MOEQ_ERR_INVALID_ARG;
+  if (T > 0 && (!logits || !topk_ids || !topk_w)) return MOEQ_ERR_INVALID_ARG;
+  if (k > E) return MOEQ_ERR_INVALID_ARG;
+  if (E > MOEQ_MAX_EXPERTS || k > MOEQ_MAX_TOPK) return MOEQ_ERR_UNSUPPORTED;
+  if (T == 0) return MOEQ_OK;
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_route_topk(logits, bias, T, E, k, renormalize, topk_ids,
+                                               topk_w, as_stream(stream)));
+}
+
+int quant_fp8_per_token(const void* x, int x_dtype, int64_t M, int K, int64_t ld_x, uint8_t* q,
+                        float* scale, void* stream) {
+  if (M < 0 || K <= 0 || ld_x < K) return MOEQ_ERR_INVALID_ARG;
+  if (x_dtype != MOEQ_F32 && x_dtype != MOEQ_BF16) return MOEQ_ERR_INVALID_ARG;
+  if (M > 0 && (!x || !q || !scale)) return MOEQ_ERR_INVALID_ARG;
+  if (K % 8 != 0 || ld_x % 8 != 0) return MOEQ_ERR_UNSUPPORTED;
+  if (M > 0 && (!aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 7u))) return MOEQ_ERR_INVALID_ARG;
+  if (M == 0) return MOEQ_OK;
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_quant_fp8(x, x_dtype, M, K, ld_x, q, scale, as_stream(stream)));
+}
+
+int moe_permute(const int32_t* topk_ids, int T, int k, int E, const uint8_t* x_q, const float* x_s,
+                int H, uint8_t* xp_q, float* xp_s, void* plan, size_t plan_bytes, void* stream) {
+  if (T < 0 || k <= 0 || E <= 0 || !plan) return MOEQ_ERR_INVALID_ARG;
+  if (E > MOEQ_MAX_EXPERTS || k > MOEQ_MAX_TOPK) return MOEQ_ERR_UNSUPPORTED;
+  if (int64_t(T) * k > 0x3FFFFFFF) return MOEQ_ERR_UNSUPPORTED;
+  if (T > 0 && !topk_ids) return MOEQ_ERR_INVALID_ARG;
+  const int R = T * k;
+  const bool gather = x_q != nullptr || x_s != nullptr;
+  if (gather) {
+    if (!x_q || !x_s || !xp_q || !xp_s || H <= 0) return MOEQ_ERR_INVALID_ARG;
+    if (H % 16 != 0) return MOEQ_ERR_UNSUPPORTED;
+    if (!aligned16(x_q) || !aligned16(xp_q)) return MOEQ_ERR_INVALID_ARG;
+  }
+  if (plan_bytes < moe_plan_size(E, R)) return MOEQ_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(plan) & 3u) return MOEQ_ERR_INVALID_ARG;
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_permute(topk_ids, T, k, E, gather ? x_q : nullptr, x_s, H, xp_q,
+                                            xp_s, plan, as_stream(stream)));
+}
+
+int pack_int4_g128(const float* w, int64_t rows, int K, uint8_t* packed, float* scales,
+                   void* stream) {
+  if (rows < 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;
+  if (K % 128 != 0) return MOEQ_ERR_UNSUPPORTED;
+  if (rows > 0 && (!w || !packed || !scales)) return MOEQ_ERR_INVALID_ARG;
+  if (rows > 0 && (!aligned16(w) || (reinterpret_cast<uintptr_t>(packed) & 3u)))
+    return MOEQ_ERR_INVALID_ARG;
+  if (rows == 0) return MOEQ_OK;
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_pack_int4(w, rows, K, packed, scales, as_stream(stream)));
+}
+
+static int gemm_common(int wfmt, const uint8_t* a_q, const float* a_s, const void* plan, int E,
+                       int R, const uint8_t* w, const float* w_scale, int N, int K, int epilogue,
+                       void* out, int out_dtype, void* stream) {
+  if (R < 0 || E <= 0 || N <= 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;
+  if (epilogue != MOEQ_EPI_NONE && epilogue != MOEQ_EPI_SILU_MUL) return MOEQ_ERR_INVALID_ARG;
+  if (out_dtype != MOEQ_F32 && out_dtype != MOEQ_BF16) return MOEQ_ERR_INVALID_ARG;
+  if (epilogue == MOEQ_EPI_SILU_MUL && out_dtype != MOEQ_BF16) return MOEQ_ERR_INVALID_ARG;
+  if (E > MOEQ_MAX_EXPERTS) return MOEQ_ERR_UNSUPPORTED;
+  if (K % 128 != 0 || N % 128 != 0) return MOEQ_ERR_UNSUPPORTED;
+  if (int64_t(N / 128) * moeq::plan_max_tiles(E, R) > 0x7FFFFFF0) return MOEQ_ERR_UNSUPPORTED;
+  if (R > 0 && (!a_q || !a_s || !plan || !w || !w_scale || !out)) return MOEQ_ERR_INVALID_ARG;
+  if (R > 0 && (!aligned16(a_q) || !aligned16(w))) return MOEQ_ERR_INVALID_ARG;
+  if (R == 0) return MOEQ_OK;
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_grouped_gemm(wfmt, a_q, a_s, plan, E, R, w, w_scale, N, K,
+                                                 epilogue, out, out_dtype, as_stream(stream)));
+}
+
+int moe_grouped_gemm_w4a8(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
+                          const uint8_t* w_packed, const float* w_scales, int N, int K,
+                          int epilogue, void* out, int out_dtype, void* stream) {
+  return gemm_common(moeq::kW4G128, a_q, a_s, plan, E, R, w_packed, w_scales, N, K, epilogue, out,
+                     out_dtype, stream);
+}
+
+int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
+                            const uint8_t* w_fp8, const float* w_row_scale, int N, int K,
+                            int epilogue, void* out, int out_dtype, void* stream) {
+  return gemm_common(moeq::kFp8Row, a_q, a_s, plan, E, R, w_fp8, w_row_scale, N, K, epilogue, out,
+                     out_dtype, stream);
+}
+
+int moe_combine(const uint16_t* o, const void* plan, const float* topk_w, const uint16_t* shared,
+                int T, int k, int H, uint16_t* y, void* stream) {
+  if (T < 0 || k <= 0 || H <= 0) return MOEQ_ERR_INVALID_ARG;
+  if (k > MOEQ_MAX_TOPK) return MOEQ_ERR_UNSUPPORTED;
+  if (H % 8 != 0) return MOEQ_ERR_UNSUPPORTED;
+  if (int64_t(T) * ((H / 8 + 255) / 256) > 0x7FFFFFFF) return MOEQ_ERR_UNSUPPORTED;
+  if (T > 0 && (!o || !plan || !topk_w || !y)) return MOEQ_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(o) || !aligned16(y) || (shared && !aligned16(shared))))
+    return MOEQ_ERR_INVALID_ARG;
+  if (T == 0) return MOEQ_OK;
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_combine(o, plan, topk_w, shared, T, k, H, y, as_stream(stream)));
+}
+
+int moe_shared_gemm_bf16(const uint16_t* a, const uint16_t* w, int M, int N, int K, int epilogue,
+                         uint16_t* out, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;
+  if (epilogue != MOEQ_EPI_NONE && epilogue != MOEQ_EPI_SILU_MUL) return MOEQ_ERR_INVALID_ARG;
+  if (K % 32 != 0 || N % 128 != 0) return MOEQ_ERR_UNSUPPORTED;
+  if (int64_t((M + 127) / 128) * (N / 128) > 0x7FFFFFFF) return MOEQ_ERR_UNSUPPORTED;
+  if (M > 0 && (!a || !w || !out)) return MOEQ_ERR_INVALID_ARG;
+  if (M > 0 && (!aligned16(a) || !aligned16(w))) return MOEQ_ERR_INVALID_ARG;
+  if (M == 0) return MOEQ_OK;
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_shared_gemm_bf16(a, w, M, N, K, epilogue, out,
+                                                     as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// moe_combine kernel: one thread per 8 consecutive hidden columns of one token.
+// y[t, c] = bf16( sum_j w[t, j] * o[row_pos[t*k + j], c] + shared[t, c] ), fp32
+// accumulation in slot order j = 0..k-1, then the shared-expert addend.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moeq {
+
+namespace {
+
+__device__ __forceinline__ void bf16x8_to_f32(const uint4& u, float (&v)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = u2f(w[i] << 16);
+    v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
+  }
+}
+
+__global__ void __launch_bounds__(256)
+combine_kernel(const uint16_t* __restrict__ o, const int32_t* __restrict__ plan,
+               const float* __restrict__ w, const uint16_t* __restrict__ shared, int T, int k,
+               int H, uint16_t* __restrict__ y) {
+  const int chunks = (H / 8 + 255) / 256;
+  const int t = blockIdx.x / chunks;
+  const int c = ((blockIdx.x - t * chunks) * 256 + threadIdx.x) * 8;
+  if (c >= H) return;
+  const int E = plan[kPlanE];
+  const PlanView pv = plan_view(const_cast<int32_t*>(plan), E, T * k);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int j = 0; j < k; ++j) {
+    const int p = pv.row_pos[t * k + j];
+    if (p < 0) continue;
+    const float wt = w[t * k + j];
+    float v[8];
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(o + int64_t(p) * H + c), v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wt, v[i], acc[i]);
+  }
+  if (shared) {
+    float v[8];
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(shared + int64_t(t) * H + c), v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+  }
+  uint4 out;
+  out.x = uint32_t(f32_to_bf16(acc[0])) | (uint32_t(f32_to_bf16(acc[1])) << 16);
+  out.y = uint32_t(f32_to_bf16(acc[2])) | (uint32_t(f32_to_bf16(acc[3])) << 16);
+  out.z = uint32_t(f32_to_bf16(acc[4])) | (uint32_t(f32_to_bf16(acc[5])) << 16);
+  out.w = uint32_t(f32_to_bf16(acc[6])) | (uint32_t(f32_to_bf16(acc[7])) << 16);
+  *reinterpret_cast<uint4*>(y + int64_t(t) * H + c) = out;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const uint16_t* o, const void* plan, const float* w,
+                          const uint16_t* shared, int T, int k, int H, uint16_t* y,
+                          hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  dim3 grid(unsigned((H / 8 + 255) / 256) * unsigned(T));
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, o, static_cast<const int32_t*>(plan),
+                     w, shared, T, k, H, y);
+  return hipGetLastError();
+}
+
+}  // namespace moeq

@@ -1,0 +1,78 @@
+// Launchers of the libmoeq kernels.  Arguments are validated by the C-ABI layer
+// (api.hip) before any of these is called; each returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moeq.h"
+
+namespace moeq {
+
+// plan word offsets (see moe_plan_size in moeq.h)
+constexpr int kPlanHeader = 16;
+enum PlanWord { kPlanR = 0, kPlanE = 1, kPlanActive = 2, kPlanTiles = 3, kPlanT = 4, kPlanK = 5,
+                kPlanDropped = 6 };
+
+struct PlanView {
+  int32_t* base;
+  int32_t* offsets;      // [E+1]
+  int32_t* sorted_rows;  // [R]
+  int32_t* row_pos;      // [R]
+  int32_t* active;       // [E]
+  int32_t* tile_expert;  // [max_tiles]
+  int32_t* tile_row0;    // [max_tiles]
+  int max_tiles;
+};
+
+__host__ __device__ inline int plan_max_tiles(int E, int R) {
+  return (R + MOEQ_TILE_M - 1) / MOEQ_TILE_M + (E < R ? E : R);
+}
+
+__host__ __device__ inline PlanView plan_view(void* plan, int E, int R) {
+  PlanView v;
+  v.base = static_cast<int32_t*>(plan);
+  v.offsets = v.base + kPlanHeader;
+  v.sorted_rows = v.offsets + (E + 1);
+  v.row_pos = v.sorted_rows + R;
+  v.active = v.row_pos + R;
+  v.tile_expert = v.active + E;
+  v.max_tiles = plan_max_tiles(E, R);
+  v.tile_row0 = v.tile_expert + v.max_tiles;
+  return v;
+}
+
+__host__ __device__ inline size_t plan_words(int E, int R) {
+  return size_t(kPlanHeader) + size_t(E + 1) + 2 * size_t(R) + size_t(E) +
+         2 * size_t(plan_max_tiles(E, R));
+}
+
+hipError_t launch_route_topk(const float* logits, const float* bias, int T, int E, int k,
+                             int renormalize, int32_t* ids, float* w, hipStream_t stream);
+
+hipError_t launch_quant_fp8(const void* x, int x_dtype, int64_t M, int K, int64_t ld_x,
+                            uint8_t* q, float* scale, hipStream_t stream);
+
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, const uint8_t* x_q,
+                          const float* x_s, int H, uint8_t* xp_q, float* xp_s, void* plan,
+                          hipStream_t stream);
+
+hipError_t launch_pack_int4(const float* w, int64_t rows, int K, uint8_t* packed, float* scales,
+                            hipStream_t stream);
+
+// weight formats of the grouped GEMM
+enum WeightFormat { kW4G128 = 0, kFp8Row = 1 };
+
+hipError_t launch_grouped_gemm(int wfmt, const uint8_t* a_q, const float* a_s, const void* plan,
+                               int E, int R, const uint8_t* w, const float* w_scale, int N, int K,
+                               int epilogue, void* out, int out_dtype, hipStream_t stream);
+
+// E is read from the plan header on the device.
+hipError_t launch_combine(const uint16_t* o, const void* plan, const float* w,
+                          const uint16_t* shared, int T, int k, int H, uint16_t* y,
+                          hipStream_t stream);
+
+hipError_t launch_shared_gemm_bf16(const uint16_t* a, const uint16_t* w, int M, int N, int K,
+                                   int epilogue, uint16_t* out, hipStream_t stream);
+
+}  // namespace moeq

@@ -1,0 +1,67 @@
+// pack_int4_g128 kernel.  16 consecutive lanes own one 128-wide group: each lane
+// loads 8 consecutive fp32 weights (32 B), the group's max |w| is reduced over
+// the 16 lanes, s = max/7 (IEEE division), codes = clamp(rne(w / s), -8, 7), and
+// each lane stores its 8 codes as one little-endian 32-bit word of nibbles
+// (code + 8, first code in the least significant nibble).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moeq {
+
+namespace {
+
+__global__ void __launch_bounds__(256)
+pack_int4_kernel(const float* __restrict__ w, int64_t n_groups, int groups_per_row,
+                 uint32_t* __restrict__ packed, float* __restrict__ scales) {
+  const int64_t gid = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const bool valid = gid < n_groups;
+  float v[8];
+  float amax = 0.0f;
+  if (valid) {
+    // group gid covers w[gid*128 .. gid*128+127] (rows are contiguous, K = 128*groups_per_row)
+    const float4* p = reinterpret_cast<const float4*>(w + gid * 128 + sub * 8);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+  if (!valid) return;
+  const float s = __fdiv_rn(amax, 7.0f);
+  uint32_t word = 0x88888888u;           // all-zero codes
+  if (s > 0.0f) {
+    word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float c = rintf(__fdiv_rn(v[i], s));
+      c = fminf(fmaxf(c, -8.0f), 7.0f);
+      word |= uint32_t(int(c) + 8) << (4 * i);
+    }
+  }
+  packed[gid * 16 + sub] = word;
+  if (sub == 0) scales[gid] = s;
+  (void)groups_per_row;
+}
+
+}  // namespace
+
+hipError_t launch_pack_int4(const float* w, int64_t rows, int K, uint8_t* packed, float* scales,
+                            hipStream_t stream) {
+  const int64_t n_groups = rows * (K / 128);
+  if (n_groups == 0) return hipSuccess;
+  const int64_t kMaxGrid = 0x7FFFFFFF;
+  for (int64_t g0 = 0; g0 < n_groups; g0 += kMaxGrid * 16) {
+    const int64_t ng = (n_groups - g0 < kMaxGrid * 16) ? (n_groups - g0) : kMaxGrid * 16;
+    hipLaunchKernelGGL(pack_int4_kernel, dim3(unsigned((ng + 15) / 16)), dim3(256), 0, stream,
+                       w + g0 * 128, ng, K / 128, reinterpret_cast<uint32_t*>(packed + g0 * 64),
+                       scales + g0);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace moeq

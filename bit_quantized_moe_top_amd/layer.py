@@ -1,0 +1,103 @@
+"""One quantized MoE expert layer as a fixed sequence of libmoeq calls.
+
+    route -> quantize x -> permute -> gate/up GEMM (+SiLU) -> quantize h
+          -> down GEMM -> combine (+ shared experts)
+
+Only orchestration lives here: buffers are torch allocations, reused across
+calls with the same token count, and every step is a C-ABI call into libmoeq.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import (EPI_NONE, EPI_SILU_MUL, moe_combine, moe_grouped_gemm_fp8row,
+               moe_grouped_gemm_w4a8, moe_permute, moe_plan_size, moe_route_topk,
+               moe_shared_gemm_bf16, pack_int4_g128, quant_fp8_per_token)
+
+
+class MoELayer:
+    """Routed experts (W4A8 INT4-g128 or row-scaled FP8) plus optional bf16 shared experts.
+
+    Weights: w13 [E, 2I, H] (gate rows then up rows), w2 [E, H, I].
+    """
+
+    def __init__(self, H: int, I: int, E: int, k: int, weight_format: str = "w4a8",
+                 renormalize: bool = True, device="cuda"):
+        if weight_format not in ("w4a8", "fp8row"):
+            raise ValueError(weight_format)
+        self.H, self.I, self.E, self.k = H, I, E, k
+        self.weight_format = weight_format
+        self.renormalize = renormalize
+        self.device = torch.device(device)
+        self.w13 = self.s13 = self.w2 = self.s2 = None
+        self.ws13 = self.ws2 = None
+        self._bufs = {}
+
+    # --------------------------------------------------------------- weights
+    def set_weights(self, w13, s13, w2, s2):
+        """Already-quantized weights (packed INT4 + group scales, or E4M3 + row scales)."""
+        self.w13, self.s13, self.w2, self.s2 = w13, s13, w2, s2
+
+    def quantize_weights(self, w13_f32: torch.Tensor, w2_f32: torch.Tensor):
+        """Quantize fp32 weights on the device with the library's own kernels."""
+        if self.weight_format == "w4a8":
+            self.w13, self.s13 = pack_int4_g128(w13_f32)
+            self.w2, self.s2 = pack_int4_g128(w2_f32)
+        else:
+            self.w13, self.s13 = quant_fp8_per_token(w13_f32)
+            self.w2, self.s2 = quant_fp8_per_token(w2_f32)
+
+    def set_shared(self, ws13: Optional[torch.Tensor], ws2: Optional[torch.Tensor]):
+        self.ws13, self.ws2 = ws13, ws2
+
+    # ---------------------------------------------------------------- buffers
+    def buffers(self, T: int) -> dict:
+        b = self._bufs.get(T)
+        if b is None:
+            H, I, E, k, d = self.H, self.I, self.E, self.k, self.device
+            R = T * k
+            b = {
+                "ids": torch.empty(T, k, dtype=torch.int32, device=d),
+                "w": torch.empty(T, k, dtype=torch.float32, device=d),
+                "x_q": torch.empty(T, H, dtype=torch.uint8, device=d),
+                "x_s": torch.empty(T, dtype=torch.float32, device=d),
+                "plan": torch.empty((moe_plan_size(E, R) + 3) // 4, dtype=torch.int32, device=d),
+                "xp_q": torch.empty(R, H, dtype=torch.uint8, device=d),
+                "xp_s": torch.empty(R, dtype=torch.float32, device=d),
+                "h": torch.empty(R, I, dtype=torch.bfloat16, device=d),
+                "h_q": torch.empty(R, I, dtype=torch.uint8, device=d),
+                "h_s": torch.empty(R, dtype=torch.float32, device=d),
+                "o": torch.empty(R, H, dtype=torch.bfloat16, device=d),
+                "y": torch.empty(T, H, dtype=torch.bfloat16, device=d),
+            }
+            if self.ws13 is not None:
+                S = self.ws2.shape[1]
+                b["sh_h"] = torch.empty(T, S, dtype=torch.bfloat16, device=d)
+                b["shared"] = torch.empty(T, H, dtype=torch.bfloat16, device=d)
+            self._bufs[T] = b
+        return b
+
+    # ---------------------------------------------------------------- forward
+    def forward(self, x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                return_all: bool = False):
+        T = x.shape[0]
+        b = self.buffers(T)
+        gemm = moe_grouped_gemm_w4a8 if self.weight_format == "w4a8" else moe_grouped_gemm_fp8row
+        moe_route_topk(logits, self.k, bias, self.renormalize, ids=b["ids"], weights=b["w"])
+        quant_fp8_per_token(x, q=b["x_q"], scale=b["x_s"])
+        moe_permute(b["ids"], self.E, b["x_q"], b["x_s"], plan=b["plan"], xp_q=b["xp_q"],
+                    xp_s=b["xp_s"])
+        gemm(b["xp_q"], b["xp_s"], b["plan"], self.w13, self.s13, EPI_SILU_MUL, out=b["h"])
+        quant_fp8_per_token(b["h"], q=b["h_q"], scale=b["h_s"])
+        gemm(b["h_q"], b["h_s"], b["plan"], self.w2, self.s2, EPI_NONE, out=b["o"])
+        shared = None
+        if self.ws13 is not None:
+            xb = x if x.dtype == torch.bfloat16 else x.to(torch.bfloat16)
+            moe_shared_gemm_bf16(xb, self.ws13, EPI_SILU_MUL, out=b["sh_h"])
+            shared = moe_shared_gemm_bf16(b["sh_h"], self.ws2, EPI_NONE, out=b["shared"])
+        moe_combine(b["o"], b["plan"], b["w"], shared, y=b["y"])
+        return b if return_all else b["y"]
+
+    __call__ = forward

@@ -1,0 +1,247 @@
+/*
+ * moeq.h -- C ABI of libmoeq, the quantized mixture-of-experts expert layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (one sparse MoE layer of an Inkling-Small-shaped model):
+ *   route     moe_route_topk        logits -> top-k expert ids and weights
+ *   quantize  quant_fp8_per_token   x -> OCP E4M3 codes + one fp32 scale per row
+ *   permute   moe_permute           group the (token, slot) rows by expert
+ *   gate/up   moe_grouped_gemm_w4a8 (epilogue SILU_MUL)   -> h (bf16)
+ *   quantize  quant_fp8_per_token   h -> E4M3 codes + scales
+ *   down      moe_grouped_gemm_w4a8 (epilogue NONE)      -> o (bf16)
+ *   combine   moe_combine           y_t = sum_j w_tj * o_tj (+ shared_t)
+ * with the row-scaled FP8 expert variant (moe_grouped_gemm_fp8row), the offline
+ * weight packer (pack_int4_g128) and the dense bf16 shared-expert GEMM
+ * (moe_shared_gemm_bf16).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers unless stated otherwise.  The library never
+ *    allocates, frees or retains them; every buffer is owned by the caller.
+ *  - All work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *    void*; NULL means the default stream).  No call synchronizes the stream.
+ *    Inputs must stay valid until the enqueued work has completed.
+ *  - Matrices are row-major and contiguous unless a leading dimension is given.
+ *  - Every call returns MOEQ_OK (0) or an error code.  Arguments are validated
+ *    before any HIP call is made, so argument errors are reported even on a
+ *    machine without a GPU.  MOEQ_ERR_DEVICE means the current device is not
+ *    gfx950; MOEQ_ERR_LAUNCH means a kernel launch failed.
+ *  - Every call is deterministic: repeated calls on the same inputs produce
+ *    bit-identical outputs (no floating-point atomics).
+ *  - Values named "bf16" are raw bfloat16 bit patterns (uint16); "E4M3" values
+ *    are raw OCP FP8 E4M3 bytes (uint8; max 448; 0x7F/0xFF are NaN).
+ *
+ * Sources (page title, section) for what each call computes are cited per
+ * function.  Where the pages are silent the call documents the reading used.
+ */
+#ifndef MOEQ_H
+#define MOEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOEQ_ABI_VERSION 1
+
+/* status codes */
+#define MOEQ_OK               0
+#define MOEQ_ERR_INVALID_ARG  1  /* null pointer, non-positive size, misalignment, inconsistent sizes */
+#define MOEQ_ERR_UNSUPPORTED  2  /* a size outside what the kernels implement (see each call) */
+#define MOEQ_ERR_WORKSPACE    3  /* plan buffer too small */
+#define MOEQ_ERR_DEVICE       4  /* no device, or the current device is not gfx950 */
+#define MOEQ_ERR_LAUNCH       5  /* a kernel launch failed (hipGetLastError) */
+
+/* element types */
+#define MOEQ_F32   0
+#define MOEQ_BF16  1
+
+/* GEMM epilogues */
+#define MOEQ_EPI_NONE      0  /* out[p, n] = acc[p, n]                                   */
+#define MOEQ_EPI_SILU_MUL  1  /* out[p, i] = silu(acc[p, i]) * acc[p, N/2 + i], i < N/2  */
+
+/* Rows of one GEMM tile.  The permutation plan lists the tiles of this height. */
+#define MOEQ_TILE_M 64
+
+/* Library limits. */
+#define MOEQ_MAX_EXPERTS 1024
+#define MOEQ_MAX_TOPK    8
+
+int         moe_abi_version(void);
+const char* moe_status_string(int status);
+
+/*
+ * Bytes of the permutation plan for E experts and R = T*k routed rows.
+ *
+ * Plan layout (int32 words), written by moe_permute and read by the GEMMs and
+ * the combine; callers may read it but must not modify it:
+ *   [0] R   [1] E   [2] n_active   [3] n_tiles   [4] T   [5] k
+ *   [6] number of ids outside [0, E) that were dropped   [7..15] reserved
+ *   offsets     [E+1]      offsets[e] = first sorted position of expert e
+ *   sorted_rows [R]        sorted position p -> routed row r = t*k + j
+ *   row_pos     [R]        routed row r -> sorted position p (-1 if dropped)
+ *   active      [E]        experts with at least one row, increasing (n_active used)
+ *   tile_expert [max_tiles] expert of each MOEQ_TILE_M-row tile (n_tiles used)
+ *   tile_row0   [max_tiles] first sorted position of each tile
+ * with max_tiles = ceil(R / MOEQ_TILE_M) + min(E, R).  Returns 0 for E <= 0 or R < 0.
+ */
+size_t moe_plan_size(int E, int R);
+
+/*
+ * moe_route_topk -- top-k routing.
+ *
+ * Inkling routes each token to 6 of its 256 routed experts
+ * ("Inkling-512k-NVFP4-AQLM-hybrid", intro).  The routing function itself is
+ * not on the pages; the reading implemented: s = logits + bias (one fp32
+ * addition; bias may be NULL); the k largest s per token, ties to the lower
+ * expert index, written best first; weights w_j = exp(s_j - s_max) divided by
+ * the sum over the k selected experts (renormalize != 0) or over all E experts
+ * (renormalize == 0).
+ *
+ *   logits    [T, E] fp32, finite       bias  [E] fp32 or NULL
+ *   topk_ids  [T, k] int32 (out)        topk_w [T, k] fp32 (out)
+ * Limits: 1 <= E <= MOEQ_MAX_EXPERTS, 1 <= k <= min(E, MOEQ_MAX_TOPK), T >= 0.
+ */
+int moe_route_topk(const float* logits, const float* bias, int T, int E, int k,
+                   int renormalize, int32_t* topk_ids, float* topk_w, void* stream);
+
+/*
+ * quant_fp8_per_token -- dynamic per-row FP8 quantization.
+ *
+ * One scale per token row ("wstewart3/Inkling-Small-W4A8-G128", section 1
+ * settings table: dynamic FP8 input activations, token strategy; "Inkling 2
+ * Small FP8 for AMD MI300X", "Precision and files": per-token dynamic
+ * activations and scale = max(abs(row)) / fmax).  gfx950's FP8 is OCP E4M3,
+ * so fmax = 448:
+ *   amax = max_k |x[m, k]|;  scale[m] = fp32(amax / 448);
+ *   q[m, k] = E4M3_RNE_saturating(fp32(x[m, k] / scale[m]))   (IEEE divisions)
+ * A row of zeros gets scale 0 and codes 0x00.  Also used for the row-scaled
+ * FP8 expert weights (rows = output channels), which is the same arithmetic.
+ *
+ *   x      [M, K] fp32 or bf16 (x_dtype), row stride ld_x elements, finite
+ *   q      [M, K] E4M3 (out, row stride K)      scale [M] fp32 (out)
+ * Limits: M >= 0, K >= 8, K % 8 == 0, ld_x >= K, ld_x % 8 == 0, x 16-byte aligned.
+ */
+int quant_fp8_per_token(const void* x, int x_dtype, int64_t M, int K, int64_t ld_x,
+                        uint8_t* q, float* scale, void* stream);
+
+/*
+ * moe_permute -- stable counting sort of the routed rows by expert, and the
+ * optional gather of the quantized activations into that order.
+ *
+ * Needed so that each expert's rows form one contiguous block for the grouped
+ * GEMM (the pages name fused grouped-GEMM kernels: "Inkling-512k-NVFP4-AQLM-
+ * hybrid", intro and "Serving").  Row r = t*k + j carries expert topk_ids[t, j];
+ * rows are ordered by expert and, within one expert, by increasing r.
+ *
+ *   topk_ids [T, k] int32
+ *   x_q [T, H] E4M3 and x_s [T] fp32, or both NULL (plan only)
+ *   xp_q [R, H] E4M3 (out): xp_q[p] = x_q[sorted_rows[p] / k]; xp_s [R] likewise
+ *   plan (out), plan_bytes >= moe_plan_size(E, T*k)
+ * Ids outside [0, E) are dropped (counted in plan word 6, row_pos = -1).
+ * Limits: T >= 0, 1 <= k <= MOEQ_MAX_TOPK, 1 <= E <= MOEQ_MAX_EXPERTS,
+ * H % 16 == 0 when gathering, x_q / xp_q 16-byte aligned.
+ */
+int moe_permute(const int32_t* topk_ids, int T, int k, int E,
+                const uint8_t* x_q, const float* x_s, int H,
+                uint8_t* xp_q, float* xp_s, void* plan, size_t plan_bytes, void* stream);
+
+/*
+ * pack_int4_g128 -- symmetric INT4 quantization in groups of 128 along K and
+ * the physical packing (offline weight preparation).
+ *
+ * Groups of 128 along the input dimension ("wstewart3/Inkling-Small-W4A8-G128",
+ * section 1 settings table; section 6: a [2048, 4096] projection has scales
+ * [2048, 32]).  Codes in [-8, 7], stored as nibble = code + 8, eight codes per
+ * little-endian int32 word with the first code in the least significant nibble
+ * (same page, section 7 "Recover and physically pack INT4").  The scale rule is
+ * not on the pages; the reading implemented:
+ *   s = fp32(max|group| / 7);  c = clamp(rne(fp32(w / s)), -8, 7);  s = 0 -> c = 0
+ *
+ *   w        [rows, K] fp32 (rows = experts * output channels), finite
+ *   packed   [rows, K/2] bytes (out) -- the byte view of [rows, K/8] int32 words
+ *   scales   [rows, K/128] fp32 (out)
+ * Limits: rows >= 0, K % 128 == 0, w 16-byte aligned.
+ */
+int pack_int4_g128(const float* w, int64_t rows, int K, uint8_t* packed, float* scales,
+                   void* stream);
+
+/*
+ * moe_grouped_gemm_w4a8 -- grouped GEMM over the routed experts with INT4 g128
+ * weights and FP8 activations.
+ *
+ * INT4 weights with FP8 activations keep the FP8 matrix cores in use
+ * ("wstewart3/Inkling-Small-W4A8-G128", intro; section 1 settings table).  For
+ * sorted row p of expert e (per the plan) and output column n:
+ *   acc[p, n] = sum_g s_w[e, n, g] * sum_{k in group g} E4M3(a_q[p, k]) * c[e, n, k]
+ *   v[p, n]   = a_s[p] * acc[p, n]
+ * The INT4 codes are converted exactly to E4M3 and multiplied on the FP8 MFMA
+ * units; each 128-wide group's fp32 partial sum is scaled by its group scale.
+ * Epilogue NONE: out[p, n] = v[p, n]  ([R, N], out_dtype bf16 or fp32).
+ * Epilogue SILU_MUL (w13 = gate rows then up rows, "Inkling-512k-NVFP4-AQLM-
+ * hybrid", "On-disk tensor format"): out[p, i] = bf16(silu(v[p, i]) * v[p, N/2+i])
+ * ([R, N/2], out_dtype must be bf16).
+ *
+ *   a_q [R, K] E4M3, a_s [R] fp32 -- rows in plan order
+ *   plan from moe_permute with the same E and R
+ *   w_packed [E, N, K/2] (pack_int4_g128 layout), w_scales [E, N, K/128] fp32
+ * Limits: K % 128 == 0, N % 128 == 0, R >= 0, 1 <= E <= MOEQ_MAX_EXPERTS;
+ * a_q and w_packed 16-byte aligned.
+ */
+int moe_grouped_gemm_w4a8(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
+                          const uint8_t* w_packed, const float* w_scales, int N, int K,
+                          int epilogue, void* out, int out_dtype, void* stream);
+
+/*
+ * moe_grouped_gemm_fp8row -- grouped GEMM with row-scaled FP8 expert weights.
+ *
+ * Expert weights E4M3 with one fp32 scale per output channel, scale tensor
+ * [n_experts, out_channels] ("Inkling 2 Small FP8 for AMD MI300X", "Precision
+ * and files"):
+ *   v[p, n] = a_s[p] * s_row[e, n] * sum_k E4M3(a_q[p, k]) * E4M3(w[e, n, k])
+ * Epilogues as for moe_grouped_gemm_w4a8.
+ *
+ *   w_fp8 [E, N, K] E4M3, w_row_scale [E, N] fp32
+ * Limits: K % 128 == 0, N % 128 == 0; a_q and w_fp8 16-byte aligned.
+ */
+int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
+                            const uint8_t* w_fp8, const float* w_row_scale, int N, int K,
+                            int epilogue, void* out, int out_dtype, void* stream);
+
+/*
+ * moe_combine -- weighted sum of each token's expert outputs.
+ *
+ * Not on the pages; the reading implemented (fp32 accumulation in slot order):
+ *   y[t, c] = bf16( sum_{j=0}^{k-1} w[t, j] * o[row_pos[t*k + j], c] + shared[t, c] )
+ * Rows dropped by moe_permute contribute nothing.
+ *
+ *   o [R, H] bf16 in plan order;  topk_w [T, k] fp32;  shared [T, H] bf16 or NULL
+ *   y [T, H] bf16 (out)
+ * Limits: H % 8 == 0; o, shared and y 16-byte aligned.
+ */
+int moe_combine(const uint16_t* o, const void* plan, const float* topk_w, const uint16_t* shared,
+                int T, int k, int H, uint16_t* y, void* stream);
+
+/*
+ * moe_shared_gemm_bf16 -- dense bf16 GEMM for the shared experts.
+ *
+ * Inkling-Small keeps its 2 shared experts per sparse layer in BF16
+ * ("wstewart3/Inkling-Small-W4A8-G128", section 1: "retained ... shared-expert
+ * parameters" stay BF16; section 7 dry-run table: unquantized shared gate/up
+ * pairs).  out = epilogue(a @ w^T) with fp32 accumulation:
+ *   NONE:     out[m, n] = bf16(acc[m, n])                       [M, N]
+ *   SILU_MUL: out[m, i] = bf16(silu(acc[m, i]) * acc[m, N/2+i])  [M, N/2]
+ *
+ *   a [M, K] bf16, w [N, K] bf16 (out, in orientation)
+ * Limits: M >= 0, K % 64 == 0, N % 128 == 0; a and w 16-byte aligned.
+ */
+int moe_shared_gemm_bf16(const uint16_t* a, const uint16_t* w, int M, int N, int K, int epilogue,
+                         uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEQ_H */

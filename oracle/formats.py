@@ -43,18 +43,7 @@ def e4m3_decode(codes) -> np.ndarray:
 _E4M3_POS = e4m3_decode(np.arange(0x7F, dtype=np.uint8))
 
 
-def e4m3_encode(v) -> np.ndarray:
-    """Nearest E4M3 code to each finite value, ties to the even code, saturating.
-
-    The representable non-negative values in increasing order have increasing
-    codes 0x00..0x7E, and the least significant code bit is the least significant
-    mantissa bit, so "ties to even" means "ties to the even code".  Magnitudes at
-    or above 448 saturate to 448 (0x7E) because E4M3 has no infinity.  The sign
-    bit is kept, so a negative value that rounds to zero encodes as 0x80.
-    """
-    v = np.asarray(v, dtype=np.float64)
-    if np.isnan(v).any():
-        raise ValueError("e4m3_encode: NaN input")
+def _e4m3_encode_block(v):
     a = np.minimum(np.abs(v), E4M3_MAX)
     hi = np.searchsorted(_E4M3_POS, a, side="left")          # first table value >= a
     hi = np.minimum(hi, 0x7E)
@@ -64,8 +53,27 @@ def e4m3_encode(v) -> np.ndarray:
     exact = _E4M3_POS[hi] == a
     pick_hi = exact | (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
     code = np.where(pick_hi, hi, lo).astype(np.uint8)
-    neg = np.signbit(v)
-    return np.where(neg, code | 0x80, code).astype(np.uint8)
+    return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
+
+
+def e4m3_encode(v, block: int = 1 << 19) -> np.ndarray:
+    """Nearest E4M3 code to each finite value, ties to the even code, saturating.
+
+    The representable non-negative values in increasing order have increasing
+    codes 0x00..0x7E, and the least significant code bit is the least significant
+    mantissa bit, so "ties to even" means "ties to the even code".  Magnitudes at
+    or above 448 saturate to 448 (0x7E) because E4M3 has no infinity.  The sign
+    bit is kept, so a negative value that rounds to zero encodes as 0x80.
+    (Values are processed in blocks only to bound temporary memory.)
+    """
+    v = np.asarray(v, dtype=np.float64)
+    if np.isnan(v).any():
+        raise ValueError("e4m3_encode: NaN input")
+    flat = v.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for i in range(0, flat.size, block):
+        out[i:i + block] = _e4m3_encode_block(flat[i:i + block])
+    return out.reshape(v.shape)
 
 
 def fp32(v) -> np.ndarray:

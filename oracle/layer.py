@@ -69,7 +69,7 @@ def route_topk(logits, k: int, bias=None, renormalize: bool = True):
 # ------------------------------------------------ a2 / a5: per-token FP8 quant
 
 
-def quant_fp8_per_token(x):
+def quant_fp8_per_token(x, block_rows: int = 512):
     """Dynamic per-row FP8 quantization.
 
     amax_t = max_k |x[t,k]|; s_t = fl32(amax_t / 448); q = E4M3(fl32(x / s_t)).
@@ -77,17 +77,23 @@ def quant_fp8_per_token(x):
     integer code is taken in the kernel's precision).  A zero row gets s = 0 and
     all codes 0x00.  x must hold values exactly representable in fp32.
     Returns q uint8 [M, K] and s float32 [M].
+    (Rows are processed in blocks only to bound temporary memory.)
     """
     x32 = np.asarray(x, dtype=np.float32)
     if not np.all(np.isfinite(x32)):
         raise ValueError("non-finite input")
-    amax = np.abs(x32).max(axis=1)
-    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-    q = np.zeros(x32.shape, dtype=np.uint8)
-    nz = s > 0
-    if nz.any():
-        ratio = (x32[nz] / s[nz][:, None]).astype(np.float32)
-        q[nz] = e4m3_encode(ratio)
+    M, K = x32.shape
+    q = np.zeros((M, K), dtype=np.uint8)
+    s = np.zeros(M, dtype=np.float32)
+    for r0 in range(0, M, block_rows):
+        xb = x32[r0:r0 + block_rows]
+        amax = np.abs(xb).max(axis=1)
+        sb = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+        s[r0:r0 + block_rows] = sb
+        nz = np.nonzero(sb > 0)[0]
+        if nz.size:
+            ratio = (xb[nz] / sb[nz][:, None]).astype(np.float32)
+            q[r0 + nz] = e4m3_encode(ratio)
     return q, s
 
 
@@ -98,18 +104,8 @@ def dequant_fp8_rows(q, s) -> np.ndarray:
 # ------------------------------------------------------ a9: INT4 g128 packing
 
 
-def quantize_int4_g128(w):
-    """Symmetric INT4 quantization in groups of 128 along the last (input) axis.
-
-    For each row n and group g: a = max|W[n, g]|; s = fl32(a / 7);
-    c = clamp(rint(fl32(W / s)), -8, 7) with rint = round half to even;
-    a zero group gets s = 0 and codes 0.
-    Returns codes int8 [rows, K] and scales float32 [rows, K/128].
-    """
-    w32 = np.asarray(w, dtype=np.float32)
+def _quantize_int4_block(w32):
     rows, K = w32.shape
-    if K % GROUP:
-        raise ValueError("K must be a multiple of 128")
     G = K // GROUP
     wg = w32.reshape(rows, G, GROUP)
     a = np.abs(wg).max(axis=2)
@@ -117,8 +113,29 @@ def quantize_int4_g128(w):
     c = np.zeros(wg.shape, dtype=np.int8)
     nz = s > 0
     ratio = (wg[nz] / s[nz][:, None]).astype(np.float32)
-    c[nz] = np.clip(np.rint(ratio.astype(np.float64)), -8, 7).astype(np.int8)
+    c[nz] = np.clip(np.rint(ratio), -8, 7).astype(np.int8)
     return c.reshape(rows, K), s
+
+
+def quantize_int4_g128(w, block_rows: int = 512):
+    """Symmetric INT4 quantization in groups of 128 along the last (input) axis.
+
+    For each row n and group g: a = max|W[n, g]|; s = fl32(a / 7);
+    c = clamp(rint(fl32(W / s)), -8, 7) with rint = round half to even;
+    a zero group gets s = 0 and codes 0.
+    Returns codes int8 [rows, K] and scales float32 [rows, K/128].
+    (Rows are processed in blocks only to bound temporary memory.)
+    """
+    w32 = np.asarray(w, dtype=np.float32)
+    rows, K = w32.shape
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    codes = np.empty((rows, K), dtype=np.int8)
+    scales = np.empty((rows, K // GROUP), dtype=np.float32)
+    for r0 in range(0, rows, block_rows):
+        codes[r0:r0 + block_rows], scales[r0:r0 + block_rows] = _quantize_int4_block(
+            w32[r0:r0 + block_rows])
+    return codes, scales
 
 
 def pack_int4_g128(w):

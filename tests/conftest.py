@@ -27,3 +27,11 @@ def gpu():
         pytest.skip("no GPU")
     import torch
     return torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    # name the case on stdout before any GPU work starts (survives a lost box)
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu-case] {request.node.nodeid}", flush=True)
+    yield

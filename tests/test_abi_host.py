@@ -1,0 +1,105 @@
+"""Host-side checks of libmoeq: it loads, exports every entry point declared in
+include/moeq.h, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import bit_quantized_moe_top_amd as mq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moeq.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, DEVICE, LAUNCH = range(6)
+FAKE = ctypes.c_void_p(4096)          # a non-null, aligned address never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    body = text[text.index('extern "C" {'):]
+    text_no_comments = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text_no_comments,
+                      flags=re.M)
+
+
+def test_header_and_binding_agree():
+    names = declared_functions()
+    assert len(names) == 11
+    assert set(names) == set(mq.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    handle = ctypes.CDLL(mq.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(handle, name), name
+
+
+def test_version_and_status_strings():
+    assert mq.moe_abi_version() == 1
+    assert mq.moe_status_string(0) == "ok"
+    for s in range(1, 6):
+        assert mq.moe_status_string(s) not in ("ok", "unknown status")
+    assert mq.moe_status_string(99) == "unknown status"
+
+
+def test_plan_size_formula():
+    for E, R in [(8, 32), (256, 24), (256, 12288), (384, 12288), (1, 0)]:
+        max_tiles = (R + 63) // 64 + min(E, R)
+        words = 16 + (E + 1) + 2 * R + E + 2 * max_tiles
+        assert mq.moe_plan_size(E, R) == 4 * words
+    assert mq.moe_plan_size(0, 5) == 0 and mq.moe_plan_size(4, -1) == 0
+
+
+def test_argument_errors_are_reported_without_a_gpu():
+    L = mq.lib
+    N = None
+    # route
+    assert L.moe_route_topk(N, N, 1, 8, 2, 1, FAKE, FAKE, N) == INVALID
+    assert L.moe_route_topk(FAKE, N, 1, 8, 9, 1, FAKE, FAKE, N) == INVALID        # k > E
+    assert L.moe_route_topk(FAKE, N, 1, 2048, 2, 1, FAKE, FAKE, N) == UNSUPPORTED  # E > 1024
+    assert L.moe_route_topk(FAKE, N, 1, 64, 9, 1, FAKE, FAKE, N) == UNSUPPORTED    # k > 8
+    assert L.moe_route_topk(N, N, 0, 8, 2, 1, N, N, N) == OK                        # empty
+    # quant
+    assert L.quant_fp8_per_token(FAKE, 1, 4, 12, 12, FAKE, FAKE, N) == UNSUPPORTED  # K % 8
+    assert L.quant_fp8_per_token(FAKE, 7, 4, 16, 16, FAKE, FAKE, N) == INVALID      # dtype
+    assert L.quant_fp8_per_token(FAKE, 1, 4, 16, 8, FAKE, FAKE, N) == INVALID       # ld < K
+    assert L.quant_fp8_per_token(ctypes.c_void_p(4100), 1, 4, 16, 16, FAKE, FAKE, N) == INVALID
+    assert L.quant_fp8_per_token(N, 1, 0, 16, 16, N, N, N) == OK
+    # permute
+    small = mq.moe_plan_size(8, 32) - 4
+    assert L.moe_permute(FAKE, 16, 2, 8, N, N, 0, N, N, FAKE, small, N) == WORKSPACE
+    assert L.moe_permute(FAKE, 16, 2, 8, FAKE, N, 64, FAKE, FAKE, FAKE, 1 << 20, N) == INVALID
+    assert L.moe_permute(FAKE, 16, 2, 8, FAKE, FAKE, 24, FAKE, FAKE, FAKE, 1 << 20, N) == UNSUPPORTED
+    assert L.moe_permute(FAKE, 16, 9, 8, N, N, 0, N, N, FAKE, 1 << 20, N) == UNSUPPORTED
+    # pack
+    assert L.pack_int4_g128(FAKE, 4, 100, FAKE, FAKE, N) == UNSUPPORTED
+    assert L.pack_int4_g128(N, 4, 128, FAKE, FAKE, N) == INVALID
+    # grouped GEMMs
+    for fn in (L.moe_grouped_gemm_w4a8, L.moe_grouped_gemm_fp8row):
+        assert fn(FAKE, FAKE, FAKE, 8, 32, FAKE, FAKE, 100, 256, 0, FAKE, 1, N) == UNSUPPORTED
+        assert fn(FAKE, FAKE, FAKE, 8, 32, FAKE, FAKE, 256, 200, 0, FAKE, 1, N) == UNSUPPORTED
+        assert fn(FAKE, FAKE, FAKE, 8, 32, FAKE, FAKE, 256, 256, 1, FAKE, 0, N) == INVALID
+        assert fn(FAKE, FAKE, FAKE, 8, 32, FAKE, FAKE, 256, 256, 5, FAKE, 1, N) == INVALID
+        assert fn(N, FAKE, FAKE, 8, 32, FAKE, FAKE, 256, 256, 0, FAKE, 1, N) == INVALID
+        assert fn(N, N, N, 8, 0, N, N, 256, 256, 0, N, 1, N) == OK
+    # combine / shared
+    assert L.moe_combine(FAKE, FAKE, FAKE, N, 4, 2, 12, FAKE, N) == UNSUPPORTED
+    assert L.moe_combine(FAKE, N, FAKE, N, 4, 2, 16, FAKE, N) == INVALID
+    assert L.moe_shared_gemm_bf16(FAKE, FAKE, 4, 100, 64, 0, FAKE, N) == UNSUPPORTED
+    assert L.moe_shared_gemm_bf16(FAKE, FAKE, 4, 128, 48, 0, FAKE, N) == UNSUPPORTED
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="would launch on fake pointers")
+def test_valid_call_without_gpu_reports_device_error():
+    L = mq.lib
+    assert L.moe_route_topk(FAKE, None, 4, 8, 2, 1, FAKE, FAKE, None) == DEVICE
+    assert L.moe_combine(FAKE, FAKE, FAKE, None, 4, 2, 16, FAKE, None) == DEVICE
+
+
+def test_python_binding_raises_on_bad_input():
+    with pytest.raises(TypeError):
+        mq.moe_route_topk(torch.zeros(2, 8, dtype=torch.float64), 2)
+    with pytest.raises(ValueError):
+        mq.moe_route_topk(torch.zeros(2, 8), 2)        # host tensor
