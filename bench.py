@@ -103,43 +103,33 @@ def time_layer(cfg, n_sets, steps, warmup, dev, dominant="gate_up"):
         distinct.append(len(torch.unique(ids)))
     torch.cuda.synchronize()
 
-    # Per-step launch timing of the gate/up grouped GEMM with events on the
-    # stream it runs on (the current torch stream).
-    gemm_ev = []
-    orig = mq.moe_grouped_gemm_w4a8 if cfg.weight_format == "w4a8" else mq.moe_grouped_gemm_fp8row
-    import bit_quantized_moe_top_amd.layer as lmod
-    name = "moe_grouped_gemm_w4a8" if cfg.weight_format == "w4a8" else "moe_grouped_gemm_fp8row"
-
-    def timed_gemm(*a, **kw):
-        if kw.get("epilogue", mq.EPI_NONE) == mq.EPI_SILU_MUL and timing[0]:
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            out = orig(*a, **kw)
-            e.record()
-            gemm_ev.append((s, e))
-            return out
-        return orig(*a, **kw)
-
-    timing = [False]
-    setattr(lmod, name, timed_gemm)
-    try:
-        for i in range(warmup):
-            layer, inp = layers[i % n_sets]
-            layer.forward(inp["x"], inp["logits"], inp["bias"])
-        torch.cuda.synchronize()
-        timing[0] = True
-        t0 = time.perf_counter()
-        for i in range(steps):
-            layer, inp = layers[i % n_sets]
-            layer.forward(inp["x"], inp["logits"], inp["bias"])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        timing[0] = False
-    finally:
-        setattr(lmod, name, orig)
+    # Warm up, then time `steps` whole-layer passes (wall clock between device
+    # synchronizations) and, in a second identical pass, each call's launch
+    # duration with events on the stream it runs on (the current torch stream).
+    for i in range(warmup):
+        layer, inp = layers[i % n_sets]
+        layer.forward(inp["x"], inp["logits"], inp["bias"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        layer, inp = layers[i % n_sets]
+        layer.forward(inp["x"], inp["logits"], inp["bias"])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = []
+    for i in range(steps):
+        layer, inp = layers[i % n_sets]
+        layer.forward(inp["x"], inp["logits"], inp["bias"], events=ev)
+    torch.cuda.synchronize()
+    per_call = {}
+    for name, s, e in ev:
+        per_call.setdefault(name, []).append(s.elapsed_time(e))
+    per_call_us = {k: 1e3 * sum(v) / len(v) for k, v in per_call.items()}
+    gemm_ev = [(s, e) for name, s, e in ev if name == "gemm_gate_up"]
     gemm_ms = sum(s.elapsed_time(e) for s, e in gemm_ev) / max(1, len(gemm_ev))
     steps_distinct = [distinct[i % n_sets] for i in range(steps)]
     return {"wall_s": wall, "ms_per_step": 1e3 * wall / steps, "gemm13_ms": gemm_ms,
+            "per_call_us": per_call_us,
             "distinct_mean": sum(steps_distinct) / steps, "distinct_per_set": distinct,
             "layers": layers}
 
@@ -240,6 +230,7 @@ def main():
                      "avg_launch_us": round(g13_ms * 1e3, 3),
                      "bytes_per_launch": D * w13b},
         "layer_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "per_call_us": {k: round(v, 2) for k, v in res["per_call_us"].items()},
     }
     layers = res.pop("layers")
     if not args.no_cpu_baseline and cfg.name == "decode":
@@ -265,6 +256,7 @@ def main():
             "weight_GBps": round(pbytes / (pms * 1e-3) / 1e9, 1),
             "gate_up_gemm_us": round(pres["gemm13_ms"] * 1e3, 2),
             "gate_up_gemm_GBps": round(pres["distinct_mean"] * pw13 / (pres["gemm13_ms"] * 1e-3) / 1e9, 1),
+            "per_call_us": {k: round(v, 2) for k, v in pres["per_call_us"].items()},
         }
     out["host"] = platform.node()
     print(json.dumps(out), flush=True)

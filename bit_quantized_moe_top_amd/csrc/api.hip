@@ -120,7 +120,7 @@ static int gemm_common(int wfmt, const uint8_t* a_q, const float* a_s, const voi
   if (K % 128 != 0 || N % 128 != 0) return MOEQ_ERR_UNSUPPORTED;
   if (int64_t(N / 128) * moeq::plan_max_tiles(E, R) > 0x7FFFFFF0) return MOEQ_ERR_UNSUPPORTED;
   if (R > 0 && (!a_q || !a_s || !plan || !w || !w_scale || !out)) return MOEQ_ERR_INVALID_ARG;
-  if (R > 0 && (!aligned16(a_q) || !aligned16(w))) return MOEQ_ERR_INVALID_ARG;
+  if (R > 0 && (!aligned16(a_q) || !aligned16(w) || !aligned16(w_scale))) return MOEQ_ERR_INVALID_ARG;
   if (R == 0) return MOEQ_OK;
   if (int rc = check_device()) return rc;
   return launch_status(moeq::launch_grouped_gemm(wfmt, a_q, a_s, plan, E, R, w, w_scale, N, K,

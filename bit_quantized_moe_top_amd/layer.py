@@ -81,23 +81,40 @@ class MoELayer:
 
     # ---------------------------------------------------------------- forward
     def forward(self, x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor] = None,
-                return_all: bool = False):
+                return_all: bool = False, events: Optional[list] = None):
+        """y = layer(x).  With `events` (a list), each call is bracketed by a pair of
+        timing events on the current stream, appended as (name, start, end)."""
         T = x.shape[0]
         b = self.buffers(T)
         gemm = moe_grouped_gemm_w4a8 if self.weight_format == "w4a8" else moe_grouped_gemm_fp8row
-        moe_route_topk(logits, self.k, bias, self.renormalize, ids=b["ids"], weights=b["w"])
-        quant_fp8_per_token(x, q=b["x_q"], scale=b["x_s"])
-        moe_permute(b["ids"], self.E, b["x_q"], b["x_s"], plan=b["plan"], xp_q=b["xp_q"],
-                    xp_s=b["xp_s"])
-        gemm(b["xp_q"], b["xp_s"], b["plan"], self.w13, self.s13, EPI_SILU_MUL, out=b["h"])
-        quant_fp8_per_token(b["h"], q=b["h_q"], scale=b["h_s"])
-        gemm(b["h_q"], b["h_s"], b["plan"], self.w2, self.s2, EPI_NONE, out=b["o"])
+
+        def step(name, fn, *args, **kw):
+            if events is None:
+                return fn(*args, **kw)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            r = fn(*args, **kw)
+            e.record()
+            events.append((name, s, e))
+            return r
+
+        step("route", moe_route_topk, logits, self.k, bias, self.renormalize, ids=b["ids"],
+             weights=b["w"])
+        step("quant_x", quant_fp8_per_token, x, q=b["x_q"], scale=b["x_s"])
+        step("permute", moe_permute, b["ids"], self.E, b["x_q"], b["x_s"], plan=b["plan"],
+             xp_q=b["xp_q"], xp_s=b["xp_s"])
+        step("gemm_gate_up", gemm, b["xp_q"], b["xp_s"], b["plan"], self.w13, self.s13,
+             epilogue=EPI_SILU_MUL, out=b["h"])
+        step("quant_h", quant_fp8_per_token, b["h"], q=b["h_q"], scale=b["h_s"])
+        step("gemm_down", gemm, b["h_q"], b["h_s"], b["plan"], self.w2, self.s2,
+             epilogue=EPI_NONE, out=b["o"])
         shared = None
         if self.ws13 is not None:
             xb = x if x.dtype == torch.bfloat16 else x.to(torch.bfloat16)
-            moe_shared_gemm_bf16(xb, self.ws13, EPI_SILU_MUL, out=b["sh_h"])
-            shared = moe_shared_gemm_bf16(b["sh_h"], self.ws2, EPI_NONE, out=b["shared"])
-        moe_combine(b["o"], b["plan"], b["w"], shared, y=b["y"])
+            step("shared_gate_up", moe_shared_gemm_bf16, xb, self.ws13, EPI_SILU_MUL, out=b["sh_h"])
+            shared = step("shared_down", moe_shared_gemm_bf16, b["sh_h"], self.ws2, EPI_NONE,
+                          out=b["shared"])
+        step("combine", moe_combine, b["o"], b["plan"], b["w"], shared, y=b["y"])
         return b if return_all else b["y"]
 
     __call__ = forward

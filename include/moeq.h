@@ -188,7 +188,7 @@ int pack_int4_g128(const float* w, int64_t rows, int K, uint8_t* packed, float* 
  *   plan from moe_permute with the same E and R
  *   w_packed [E, N, K/2] (pack_int4_g128 layout), w_scales [E, N, K/128] fp32
  * Limits: K % 128 == 0, N % 128 == 0, R >= 0, 1 <= E <= MOEQ_MAX_EXPERTS;
- * a_q and w_packed 16-byte aligned.
+ * a_q, w_packed and w_scales 16-byte aligned.
  */
 int moe_grouped_gemm_w4a8(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
                           const uint8_t* w_packed, const float* w_scales, int N, int K,
@@ -204,7 +204,7 @@ int moe_grouped_gemm_w4a8(const uint8_t* a_q, const float* a_s, const void* plan
  * Epilogues as for moe_grouped_gemm_w4a8.
  *
  *   w_fp8 [E, N, K] E4M3, w_row_scale [E, N] fp32
- * Limits: K % 128 == 0, N % 128 == 0; a_q and w_fp8 16-byte aligned.
+ * Limits: K % 128 == 0, N % 128 == 0; a_q, w_fp8 and w_row_scale 16-byte aligned.
  */
 int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
                             const uint8_t* w_fp8, const float* w_row_scale, int N, int K,
