@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="weight sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time only eager launches (default: also replay captured graphs)")
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed", "fp8row"])
     return ap.parse_args()
 
@@ -90,7 +92,7 @@ def build_sets(cfg, n_sets, dev):
     return layers
 
 
-def time_layer(cfg, n_sets, steps, warmup, dev, dominant="gate_up"):
+def time_layer(cfg, n_sets, steps, warmup, dev, graph=False):
     """Times `steps` layer passes; returns timings and the dominant GEMM's launch time."""
     import torch
 
@@ -116,6 +118,25 @@ def time_layer(cfg, n_sets, steps, warmup, dev, dominant="gate_up"):
         layer.forward(inp["x"], inp["logits"], inp["bias"])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    graph_ms = None
+    if graph:
+        # the same steps replayed from one captured graph per weight set (the
+        # launches of a step, recorded once; no host work per launch)
+        graphs = []
+        for layer, inp in layers:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                layer.forward(inp["x"], inp["logits"], inp["bias"])
+            graphs.append(g)
+        for i in range(warmup):
+            graphs[i % n_sets].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[i % n_sets].replay()
+        torch.cuda.synchronize()
+        graph_ms = 1e3 * (time.perf_counter() - t0) / steps
+        del graphs
     ev = []
     for i in range(steps):
         layer, inp = layers[i % n_sets]
@@ -129,6 +150,7 @@ def time_layer(cfg, n_sets, steps, warmup, dev, dominant="gate_up"):
     gemm_ms = sum(s.elapsed_time(e) for s, e in gemm_ev) / max(1, len(gemm_ev))
     steps_distinct = [distinct[i % n_sets] for i in range(steps)]
     return {"wall_s": wall, "ms_per_step": 1e3 * wall / steps, "gemm13_ms": gemm_ms,
+            "graph_ms_per_step": graph_ms,
             "per_call_us": per_call_us,
             "distinct_mean": sum(steps_distinct) / steps, "distinct_per_set": distinct,
             "layers": layers}
@@ -199,11 +221,13 @@ def main():
     dev = torch.device("cuda:0")
     cfg = W.get_config(args.workload)
     log(f"device {torch.cuda.get_device_name(0)}; workload {cfg}")
-    res = time_layer(cfg, args.sets, args.steps, args.warmup, dev)
+    res = time_layer(cfg, args.sets, args.steps, args.warmup, dev, graph=not args.no_graph)
     w13b, w2b = expert_bytes(cfg)
     D = res["distinct_mean"]
     flops = 2.0 * cfg.R * 3 * cfg.H * cfg.I
-    ms = res["ms_per_step"]
+    # headline: graph replay when captured (the decode deployment mode), else eager
+    ms_eager = res["ms_per_step"]
+    ms = res["graph_ms_per_step"] or ms_eager
     gbs = D * (w13b + w2b) / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     g13_ms = res["gemm13_ms"]
@@ -230,6 +254,9 @@ def main():
                      "avg_launch_us": round(g13_ms * 1e3, 3),
                      "bytes_per_launch": D * w13b},
         "layer_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "launch_mode": "hip graph replay" if res["graph_ms_per_step"] else "eager",
+        "eager_ms_per_step": round(ms_eager, 5),
+        "eager_value": round(D * (w13b + w2b) / (ms_eager * 1e-3) / 1e9, 3),
         "per_call_us": {k: round(v, 2) for k, v in res["per_call_us"].items()},
     }
     layers = res.pop("layers")

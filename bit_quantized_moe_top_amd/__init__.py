@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "LIB_PATH", "lib", "MOEQ_F32", "MOEQ_BF16", "EPI_NONE", "EPI_SILU_MUL", "TILE_M",
     "MAX_EXPERTS", "MAX_TOPK", "MoeqError", "moe_abi_version", "moe_status_string",
-    "moe_plan_size", "moe_route_topk", "quant_fp8_per_token", "moe_permute", "pack_int4_g128",
+    "moe_plan_size", "moe_route_topk", "quant_fp8_per_token", "moe_permute",
+    "moe_route_quant_permute", "pack_int4_g128",
     "moe_grouped_gemm_w4a8", "moe_grouped_gemm_fp8row", "moe_combine", "moe_shared_gemm_bf16",
     "plan_fields", "EXPORTED_SYMBOLS",
 ]
@@ -45,6 +46,8 @@ _SIGNATURES = {
     "moe_route_topk": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "quant_fp8_per_token": (_I, [_P, _I, _I64, _I, _I64, _P, _P, _P]),
     "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _P, _SZ, _P]),
+    "moe_route_quant_permute": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P,
+                                     _P, _SZ, _P]),
     "pack_int4_g128": (_I, [_P, _I64, _I, _P, _P, _P]),
     "moe_grouped_gemm_w4a8": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_grouped_gemm_fp8row": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
@@ -115,10 +118,11 @@ def moe_plan_size(E: int, R: int) -> int:
 def plan_fields(plan: torch.Tensor, E: int, R: int) -> dict:
     """Views of the plan's arrays (the layout documented in include/moeq.h)."""
     max_tiles = (R + TILE_M - 1) // TILE_M + min(E, R)
+    chunks = max(1, (R + 1023) // 1024)
     o = PLAN_HEADER
     f = {"header": plan[:PLAN_HEADER]}
     for name, n in (("offsets", E + 1), ("sorted_rows", R), ("row_pos", R), ("active", E),
-                    ("tile_expert", max_tiles), ("tile_row0", max_tiles)):
+                    ("tile_expert", max_tiles), ("tile_row0", max_tiles), ("scratch", chunks * E)):
         f[name] = plan[o:o + n]
         o += n
     return f
@@ -184,6 +188,37 @@ def moe_permute(topk_ids: torch.Tensor, E: int, x_q: Optional[torch.Tensor] = No
                                           _ptr(xp_q), _ptr(xp_s), _ptr(plan), plan.numel() * 4,
                                           _stream(dev)))
     return plan, xp_q, xp_s
+
+
+def moe_route_quant_permute(logits: torch.Tensor, x: torch.Tensor, k: int,
+                            bias: Optional[torch.Tensor] = None, renormalize: bool = True,
+                            out: Optional[dict] = None) -> dict:
+    """Routing, FP8 quantization of x and the permutation (with gather) in one call.
+    Returns a dict with ids, w, x_q, x_s, plan, xp_q, xp_s (reusing `out`'s tensors)."""
+    _req(logits, "logits", torch.float32, 2)
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _req(x, "x", x.dtype, 2)
+    T, E = logits.shape
+    H = x.shape[1]
+    R = T * k
+    dev = x.device
+    if bias is not None:
+        _req(bias, "bias", torch.float32, 1)
+    o = dict(out) if out is not None else {}
+    o.setdefault("ids", torch.empty(T, k, dtype=torch.int32, device=dev))
+    o.setdefault("w", torch.empty(T, k, dtype=torch.float32, device=dev))
+    o.setdefault("x_q", torch.empty(T, H, dtype=torch.uint8, device=dev))
+    o.setdefault("x_s", torch.empty(T, dtype=torch.float32, device=dev))
+    o.setdefault("plan", torch.empty((moe_plan_size(E, R) + 3) // 4, dtype=torch.int32, device=dev))
+    o.setdefault("xp_q", torch.empty(R, H, dtype=torch.uint8, device=dev))
+    o.setdefault("xp_s", torch.empty(R, dtype=torch.float32, device=dev))
+    dt = MOEQ_BF16 if x.dtype == torch.bfloat16 else MOEQ_F32
+    _check("moe_route_quant_permute", lib.moe_route_quant_permute(
+        _ptr(logits), _ptr(bias), T, E, k, 1 if renormalize else 0, _ptr(x), dt, H, _ptr(o["ids"]),
+        _ptr(o["w"]), _ptr(o["x_q"]), _ptr(o["x_s"]), _ptr(o["xp_q"]), _ptr(o["xp_s"]),
+        _ptr(o["plan"]), o["plan"].numel() * 4, _stream(dev)))
+    return o
 
 
 def pack_int4_g128(w: torch.Tensor, packed: Optional[torch.Tensor] = None,

@@ -97,6 +97,26 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, const uint8_t* x_q
                                             xp_s, plan, as_stream(stream)));
 }
 
+int moe_route_quant_permute(const float* logits, const float* bias, int T, int E, int k,
+                            int renormalize, const void* x, int x_dtype, int H, int32_t* topk_ids,
+                            float* topk_w, uint8_t* x_q, float* x_s, uint8_t* xp_q, float* xp_s,
+                            void* plan, size_t plan_bytes, void* stream) {
+  if (T < 0 || E <= 0 || k <= 0 || H <= 0 || !plan) return MOEQ_ERR_INVALID_ARG;
+  if (x_dtype != MOEQ_F32 && x_dtype != MOEQ_BF16) return MOEQ_ERR_INVALID_ARG;
+  if (k > E) return MOEQ_ERR_INVALID_ARG;
+  if (E > MOEQ_MAX_EXPERTS || k > MOEQ_MAX_TOPK) return MOEQ_ERR_UNSUPPORTED;
+  if (int64_t(T) * k > 0x3FFFFFFF || H % 16 != 0) return MOEQ_ERR_UNSUPPORTED;
+  if (T > 0 && (!logits || !x || !topk_ids || !topk_w || !x_q || !x_s || !xp_q || !xp_s))
+    return MOEQ_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(x) || !aligned16(x_q) || !aligned16(xp_q))) return MOEQ_ERR_INVALID_ARG;
+  if (plan_bytes < moe_plan_size(E, T * k)) return MOEQ_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(plan) & 3u) return MOEQ_ERR_INVALID_ARG;
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_front(logits, bias, T, E, k, renormalize, x, x_dtype, H,
+                                          topk_ids, topk_w, x_q, x_s, xp_q, xp_s, plan,
+                                          as_stream(stream)));
+}
+
 int pack_int4_g128(const float* w, int64_t rows, int K, uint8_t* packed, float* scales,
                    void* stream) {
   if (rows < 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;

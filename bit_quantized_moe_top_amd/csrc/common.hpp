@@ -40,14 +40,60 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
 }
 
 // ----------------------------------------------------- wave reductions ----
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// Cross-lane steps use DPP (a VALU operand modifier, no LDS round trip):
+// quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror combine within
+// each 16-lane row; row_bcast15 / row_bcast31 (restricted to rows 1,3 / 2,3)
+// carry rows into rows; lane 63 then holds the wave-wide result, which
+// readlane broadcasts.  Lanes a step does not write return `old`.
+constexpr int kDppQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+constexpr int kDppRowShr = 0x110;         // + n: row_shr:n
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp(int old, int src) {
+  return __builtin_amdgcn_update_dpp(old, src, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float old, float src) {
+  return __builtin_bit_cast(float, dpp<CTRL, ROW_MASK>(__builtin_bit_cast(int, old),
+                                                       __builtin_bit_cast(int, src)));
+}
+__device__ __forceinline__ float readlane(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+// wave-wide combine of op over all 64 lanes (ident: op's identity), result in
+// every lane; the combination order is fixed, so results are deterministic
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op, T ident) {
+  v = op(v, dpp<kDppQuadSwap1>(ident, v));
+  v = op(v, dpp<kDppQuadSwap2>(ident, v));
+  v = op(v, dpp<kDppRowHalfMirror>(ident, v));
+  v = op(v, dpp<kDppRowMirror>(ident, v));
+  v = op(v, dpp<kDppRowBcast15, 0xA>(ident, v));
+  v = op(v, dpp<kDppRowBcast31, 0xC>(ident, v));
+  return readlane(v, 63);
+}
+__device__ __forceinline__ float wave_max(float v) {   // for v >= 0 (magnitudes)
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); }, 0.0f);
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return wave_reduce(v, [](float a, float b) { return a + b; }, 0.0f);
+}
+
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += dpp<kDppRowShr + 1>(0, v);
+  v += dpp<kDppRowShr + 2>(0, v);
+  v += dpp<kDppRowShr + 4>(0, v);
+  v += dpp<kDppRowShr + 8>(0, v);
+  v += dpp<kDppRowBcast15, 0xA>(0, v);
+  v += dpp<kDppRowBcast31, 0xC>(0, v);
   return v;
 }
 

@@ -22,12 +22,16 @@ struct PlanView {
   int32_t* active;       // [E]
   int32_t* tile_expert;  // [max_tiles]
   int32_t* tile_row0;    // [max_tiles]
+  int32_t* scratch;      // [plan_chunks(R) * E] used while the plan is built
   int max_tiles;
 };
 
 __host__ __device__ inline int plan_max_tiles(int E, int R) {
   return (R + MOEQ_TILE_M - 1) / MOEQ_TILE_M + (E < R ? E : R);
 }
+
+// chunks of 1024 routed rows ranked by separate workgroups
+__host__ __device__ inline int plan_chunks(int R) { return (R + 1023) / 1024 > 0 ? (R + 1023) / 1024 : 1; }
 
 __host__ __device__ inline PlanView plan_view(void* plan, int E, int R) {
   PlanView v;
@@ -39,12 +43,13 @@ __host__ __device__ inline PlanView plan_view(void* plan, int E, int R) {
   v.tile_expert = v.active + E;
   v.max_tiles = plan_max_tiles(E, R);
   v.tile_row0 = v.tile_expert + v.max_tiles;
+  v.scratch = v.tile_row0 + v.max_tiles;
   return v;
 }
 
 __host__ __device__ inline size_t plan_words(int E, int R) {
   return size_t(kPlanHeader) + size_t(E + 1) + 2 * size_t(R) + size_t(E) +
-         2 * size_t(plan_max_tiles(E, R));
+         2 * size_t(plan_max_tiles(E, R)) + size_t(plan_chunks(R)) * size_t(E);
 }
 
 hipError_t launch_route_topk(const float* logits, const float* bias, int T, int E, int k,
@@ -71,6 +76,14 @@ hipError_t launch_grouped_gemm(int wfmt, const uint8_t* a_q, const float* a_s, c
 hipError_t launch_combine(const uint16_t* o, const void* plan, const float* w,
                           const uint16_t* shared, int T, int k, int H, uint16_t* y,
                           hipStream_t stream);
+
+// moe_route_topk + quant_fp8_per_token + moe_permute (with the gather) in one
+// launch for T <= kFrontSmallT tokens; separate launches otherwise.
+constexpr int kFrontSmallT = 16;
+hipError_t launch_front(const float* logits, const float* bias, int T, int E, int k,
+                        int renormalize, const void* x, int x_dtype, int H, int32_t* ids, float* w,
+                        uint8_t* x_q, float* x_s, uint8_t* xp_q, float* xp_s, void* plan,
+                        hipStream_t stream);
 
 hipError_t launch_shared_gemm_bf16(const uint16_t* a, const uint16_t* w, int M, int N, int K,
                                    int epilogue, uint16_t* out, hipStream_t stream);

@@ -2,40 +2,14 @@
 //
 // Pass 1 reads the row and reduces max|x| (wave shuffles, then 4 partials in
 // LDS); pass 2 re-reads the row (now in cache), divides by the scale with an
-// IEEE division and encodes E4M3 with round-to-nearest-even.  Each thread moves
-// 8 elements (16 B of bf16 / 32 B of fp32) per step and writes 8 codes (8 B).
-#include "common.hpp"
-#include "kernels.hpp"
+// IEEE division and encodes E4M3 with round-to-nearest-even (fp8_scale and
+// fp8_codes8 in front.hpp, shared with the fused front-end kernel).  Each
+// thread moves 8 elements per step and writes 8 codes (8 B).
+#include "front.hpp"
 
 namespace moeq {
 
 namespace {
-
-template <typename T>
-struct Load8;
-
-template <>
-struct Load8<uint16_t> {
-  static __device__ __forceinline__ void run(const uint16_t* p, float (&v)[8]) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = u2f(w[i] << 16);
-      v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
-    }
-  }
-};
-
-template <>
-struct Load8<float> {
-  static __device__ __forceinline__ void run(const float* p, float (&v)[8]) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-};
 
 template <typename T>
 __global__ void __launch_bounds__(256)
@@ -48,7 +22,7 @@ quant_fp8_kernel(const T* __restrict__ x, int K, int64_t ld_x, uint8_t* __restri
   float amax = 0.0f;
   for (int c = threadIdx.x * 8; c < K; c += 256 * 8) {
     float v[8];
-    Load8<T>::run(row + c, v);
+    load8(row + c, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   }
@@ -56,20 +30,12 @@ quant_fp8_kernel(const T* __restrict__ x, int K, int64_t ld_x, uint8_t* __restri
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
-  const float s = __fdiv_rn(amax, 448.0f);
+  const float s = fp8_scale(amax);
   if (threadIdx.x == 0) scale[m] = s;
   for (int c = threadIdx.x * 8; c < K; c += 256 * 8) {
-    uint32_t lo = 0, hi = 0;
-    if (s > 0.0f) {
-      float v[8];
-      Load8<T>::run(row + c, v);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo |= f32_to_e4m3(__fdiv_rn(v[i], s)) << (8 * i);
-        hi |= f32_to_e4m3(__fdiv_rn(v[4 + i], s)) << (8 * i);
-      }
-    }
-    *reinterpret_cast<uint2*>(qrow + c) = make_uint2(lo, hi);
+    float v[8];
+    load8(row + c, v);
+    *reinterpret_cast<uint2*>(qrow + c) = fp8_codes8(v, s);
   }
 }
 

@@ -1,7 +1,7 @@
 """One quantized MoE expert layer as a fixed sequence of libmoeq calls.
 
-    route -> quantize x -> permute -> gate/up GEMM (+SiLU) -> quantize h
-          -> down GEMM -> combine (+ shared experts)
+    route + quantize x + permute (one call) -> gate/up GEMM (+SiLU)
+          -> quantize h -> down GEMM -> combine (+ shared experts)
 
 Only orchestration lives here: buffers are torch allocations, reused across
 calls with the same token count, and every step is a C-ABI call into libmoeq.
@@ -13,7 +13,7 @@ from typing import Optional
 import torch
 
 from . import (EPI_NONE, EPI_SILU_MUL, moe_combine, moe_grouped_gemm_fp8row,
-               moe_grouped_gemm_w4a8, moe_permute, moe_plan_size, moe_route_topk,
+               moe_grouped_gemm_w4a8, moe_plan_size, moe_route_quant_permute,
                moe_shared_gemm_bf16, pack_int4_g128, quant_fp8_per_token)
 
 
@@ -98,11 +98,8 @@ class MoELayer:
             events.append((name, s, e))
             return r
 
-        step("route", moe_route_topk, logits, self.k, bias, self.renormalize, ids=b["ids"],
-             weights=b["w"])
-        step("quant_x", quant_fp8_per_token, x, q=b["x_q"], scale=b["x_s"])
-        step("permute", moe_permute, b["ids"], self.E, b["x_q"], b["x_s"], plan=b["plan"],
-             xp_q=b["xp_q"], xp_s=b["xp_s"])
+        step("route_quant_permute", moe_route_quant_permute, logits, x, self.k, bias,
+             self.renormalize, out=b)
         step("gemm_gate_up", gemm, b["xp_q"], b["xp_s"], b["plan"], self.w13, self.s13,
              epilogue=EPI_SILU_MUL, out=b["h"])
         step("quant_h", quant_fp8_per_token, b["h"], q=b["h_q"], scale=b["h_s"])

@@ -85,7 +85,9 @@ const char* moe_status_string(int status);
  *   active      [E]        experts with at least one row, increasing (n_active used)
  *   tile_expert [max_tiles] expert of each MOEQ_TILE_M-row tile (n_tiles used)
  *   tile_row0   [max_tiles] first sorted position of each tile
- * with max_tiles = ceil(R / MOEQ_TILE_M) + min(E, R).  Returns 0 for E <= 0 or R < 0.
+ *   scratch     [chunks * E] per-chunk counts used while the plan is built
+ * with max_tiles = ceil(R / MOEQ_TILE_M) + min(E, R) and chunks = max(1, ceil(R / 1024)).
+ * Returns 0 for E <= 0 or R < 0.
  */
 size_t moe_plan_size(int E, int R);
 
@@ -147,6 +149,25 @@ int quant_fp8_per_token(const void* x, int x_dtype, int64_t M, int K, int64_t ld
 int moe_permute(const int32_t* topk_ids, int T, int k, int E,
                 const uint8_t* x_q, const float* x_s, int H,
                 uint8_t* xp_q, float* xp_s, void* plan, size_t plan_bytes, void* stream);
+
+/*
+ * moe_route_quant_permute -- moe_route_topk, quant_fp8_per_token on x and
+ * moe_permute (with the gather), in that order, as one call.
+ *
+ * Every output equals the one the three separate calls produce (same routines,
+ * bit-identical).  For T <= 16 tokens (decode-sized batches) all of it runs in a
+ * single 1024-thread workgroup launch, which removes three launch latencies
+ * from the layer; larger T uses the separate kernels.
+ *
+ *   logits [T, E] fp32, bias [E] or NULL, x [T, H] fp32 or bf16 (x_dtype)
+ *   topk_ids [T, k], topk_w [T, k], x_q [T, H], x_s [T], xp_q [T*k, H], xp_s [T*k],
+ *   plan (out; plan_bytes >= moe_plan_size(E, T*k))
+ * Limits: those of the three calls; H % 16 == 0; x, x_q, xp_q 16-byte aligned.
+ */
+int moe_route_quant_permute(const float* logits, const float* bias, int T, int E, int k,
+                            int renormalize, const void* x, int x_dtype, int H, int32_t* topk_ids,
+                            float* topk_w, uint8_t* x_q, float* x_s, uint8_t* xp_q, float* xp_s,
+                            void* plan, size_t plan_bytes, void* stream);
 
 /*
  * pack_int4_g128 -- symmetric INT4 quantization in groups of 128 along K and

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     assert set(names) == set(mq.EXPORTED_SYMBOLS)
 
 
@@ -47,7 +47,8 @@ def test_version_and_status_strings():
 def test_plan_size_formula():
     for E, R in [(8, 32), (256, 24), (256, 12288), (384, 12288), (1, 0)]:
         max_tiles = (R + 63) // 64 + min(E, R)
-        words = 16 + (E + 1) + 2 * R + E + 2 * max_tiles
+        chunks = max(1, (R + 1023) // 1024)
+        words = 16 + (E + 1) + 2 * R + E + 2 * max_tiles + chunks * E
         assert mq.moe_plan_size(E, R) == 4 * words
     assert mq.moe_plan_size(0, 5) == 0 and mq.moe_plan_size(4, -1) == 0
 
@@ -73,6 +74,16 @@ def test_argument_errors_are_reported_without_a_gpu():
     assert L.moe_permute(FAKE, 16, 2, 8, FAKE, N, 64, FAKE, FAKE, FAKE, 1 << 20, N) == INVALID
     assert L.moe_permute(FAKE, 16, 2, 8, FAKE, FAKE, 24, FAKE, FAKE, FAKE, 1 << 20, N) == UNSUPPORTED
     assert L.moe_permute(FAKE, 16, 9, 8, N, N, 0, N, N, FAKE, 1 << 20, N) == UNSUPPORTED
+    # fused front end
+    big = 1 << 20
+    assert L.moe_route_quant_permute(FAKE, N, 4, 8, 2, 1, FAKE, 1, 24, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, big, N) == UNSUPPORTED                  # H % 16
+    assert L.moe_route_quant_permute(FAKE, N, 4, 8, 2, 1, FAKE, 5, 32, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, big, N) == INVALID                      # dtype
+    assert L.moe_route_quant_permute(FAKE, N, 4, 8, 2, 1, N, 1, 32, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, big, N) == INVALID                      # x null
+    assert L.moe_route_quant_permute(FAKE, N, 4, 8, 2, 1, FAKE, 1, 32, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, 64, N) == WORKSPACE
     # pack
     assert L.pack_int4_g128(FAKE, 4, 100, FAKE, FAKE, N) == UNSUPPORTED
     assert L.pack_int4_g128(N, 4, 128, FAKE, FAKE, N) == INVALID

@@ -157,6 +157,43 @@ def test_permute_plan_only_and_empty():
     assert (f["offsets"].numpy() == 0).all() and f["header"][3] == 0
 
 
+@pytest.mark.parametrize("T,E,k,H,dtype", [(4, 256, 6, 4096, torch.bfloat16), (1, 8, 2, 256, torch.float32),
+                                           (16, 1000, 8, 512, torch.bfloat16), (17, 64, 3, 256, torch.bfloat16),
+                                           (300, 256, 6, 128, torch.bfloat16), (0, 16, 2, 64, torch.float32)])
+def test_route_quant_permute_fused_matches_separate_and_oracle(T, E, k, H, dtype):
+    g = torch.Generator().manual_seed(T * 31 + E + H)
+    logits = torch.randn(T, E, generator=g)
+    if T > 1:
+        logits[1] = logits[0]                       # identical tokens -> equal ids
+    bias = torch.randn(E, generator=g) if E % 2 == 0 else None
+    x = (torch.randn(T, H, generator=g) * 3).to(dtype)
+    if T > 2:
+        x[2] = 0                                    # zero row
+    dl, dx = logits.to(_dev()), x.to(_dev())
+    db = None if bias is None else bias.to(_dev())
+    fused = mq.moe_route_quant_permute(dl, dx, k, db)
+    ids, w = mq.moe_route_topk(dl, k, db)
+    xq, xs = mq.quant_fp8_per_token(dx)
+    plan, xp_q, xp_s = mq.moe_permute(ids, E, xq, xs)
+    torch.cuda.synchronize()
+    for name, a, b in (("ids", fused["ids"], ids), ("w", fused["w"], w), ("x_q", fused["x_q"], xq),
+                       ("x_s", fused["x_s"], xs), ("xp_q", fused["xp_q"], xp_q),
+                       ("xp_s", fused["xp_s"], xp_s)):
+        assert torch.equal(a, b), name
+    R = T * k
+    fp, sp = mq.plan_fields(fused["plan"].cpu(), E, R), mq.plan_fields(plan.cpu(), E, R)
+    for name in ("header", "offsets", "sorted_rows", "row_pos"):
+        assert torch.equal(fp[name], sp[name]), name
+    na = int(fp["header"][2])                       # entries past n_active are unspecified
+    assert torch.equal(fp["active"][:na], sp["active"][:na])
+    if T:
+        rid, rw = L.route_topk(logits.numpy(), k, None if bias is None else bias.numpy())
+        np.testing.assert_array_equal(fused["ids"].cpu().numpy(), rid)
+        rq, rs = L.quant_fp8_per_token(x.to(torch.float32).numpy())
+        np.testing.assert_array_equal(fused["x_q"].cpu().numpy(), rq)
+        _check_plan(fused["plan"], rid, E, rq, rs, fused["xp_q"], fused["xp_s"])
+
+
 # ----------------------------------------------------------- grouped GEMMs ----
 def _case_ids(T, k, E, rng, hot=None):
     rows = []
