@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="weight sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 1 GiB device buffer 5 times (a plain copy kernel of known "
+                         "size, to scale the memory-traffic counters), then exit")
     ap.add_argument("--no-graph", action="store_true",
                     help="time only eager launches (default: also replay captured graphs)")
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed", "fp8row"])
@@ -156,6 +159,26 @@ def time_layer(cfg, n_sets, steps, warmup, dev, graph=False):
             "layers": layers}
 
 
+def measured_traffic(kernel_bytes: float):
+    """HBM bytes per launch of the decode gate/up GEMM from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if the kernel sources are still
+    the ones the counters were taken on (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_decode_T4_traffic.json")
+    try:
+        doc = json.load(open(path))
+        h = hashlib.sha256()
+        for f in doc["sources"]:
+            h.update(open(os.path.join(ROOT, "bit_quantized_moe_top_amd", "csrc", f), "rb").read())
+        if h.hexdigest() != doc["source_sha256"]:
+            return None
+        return {"bytes_per_launch": doc["hbm_bytes_per_launch"],
+                "vs_algorithmic": round(doc["hbm_bytes_per_launch"] / kernel_bytes, 4),
+                "source": "profiles/gemm_decode_T4_traffic.md"}
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(cfg, layers, target_s=10.0):
     """The oracle, as it stands, on the host: full layer for the first weight set."""
     import numpy as np
@@ -219,6 +242,14 @@ def main():
 
     import workloads as W
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)      # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 5}))
+        return
     cfg = W.get_config(args.workload)
     log(f"device {torch.cuda.get_device_name(0)}; workload {cfg}")
     res = time_layer(cfg, args.sets, args.steps, args.warmup, dev, graph=not args.no_graph)
@@ -250,7 +281,10 @@ def main():
                    "weight_bytes_per_step": D * (w13b + w2b)},
         "roofline": {"kernel": "moe_grouped_gemm (gate/up, SiLU epilogue)", "bound": "hbm",
                      "achieved": round(g13_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(g13_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(g13_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": (measured_traffic(D * w13b) or {}).get("bytes_per_launch")
+                     if cfg.name == "decode" else None,
+                     "traffic_detail": measured_traffic(D * w13b) if cfg.name == "decode" else None,
                      "avg_launch_us": round(g13_ms * 1e3, 3),
                      "bytes_per_launch": D * w13b},
         "layer_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
