@@ -1,53 +1,172 @@
 // moe_route_quant_permute: the layer's front end (routing, FP8 quantization of
-// x, permutation plan and gather) as one launch for small batches.
+// x, permutation plan and the copy of the routed rows into plan order) as one
+// launch for small batches.
 //
-// At decode-sized T the four separate launches are almost pure latency (a few
+// At decode-sized T the separate launches are almost pure latency (a few
 // microseconds each for a few kilobytes of work).  One 1024-thread workgroup
-// does all of it: waves route one token each, 16/T waves quantize each token's
-// row, the workgroup builds
-// the plan from the expert ids it keeps in LDS, and the waves then copy the
-// routed rows into plan order.  The arithmetic is the shared front.hpp code, so
-// the results are bit-identical to the separate calls.
+// does all of it in three phases separated by two barriers:
+//   1. the waves of each row load their 8-element chunks of x into registers;
+//      waves t < T route token t (expert ids into LDS); each wave then writes
+//      the max |x| of its chunks to LDS;
+//   2. the last wave builds the plan (R <= 64; the whole workgroup otherwise)
+//      while the others turn their chunks into E4M3 codes, kept in registers
+//      and written to x_q;
+//   3. the codes go to the k plan positions of their token.
+// The barriers order LDS only, so no wave waits for another's global stores.
+// The arithmetic is the shared front.hpp code, so the results are bit-identical
+// to the separate calls.
 #include "front.hpp"
 
 namespace moeq {
 
 namespace {
 
+constexpr int kFrontMaxRows = kFrontSmallT * MOEQ_MAX_TOPK;
+
+// 8 consecutive elements of x held in registers as loaded
 template <typename XT>
+struct XChunk;
+template <>
+struct XChunk<uint16_t> {
+  uint4 raw;
+  __device__ __forceinline__ void load(const uint16_t* p) { raw = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void values(float (&v)[8]) const {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = u2f(w[i] << 16);
+      v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <>
+struct XChunk<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void values(float (&v)[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+constexpr int kFrontChunksPerThread = 4;    // 8-element chunks of x held per lane
+
+// Waves quantizing each row: the rows share the waves equally; the last wave,
+// which builds the plan, stays out when the others still cover every chunk of
+// a row with kFrontChunksPerThread chunks per lane.  0: too large for one launch.
+__host__ __device__ inline int front_waves_per_row(int T, int H) {
+  if (T <= 0) return 1;
+  const int cpr = H >> 3;
+  const int cap = kWave * kFrontChunksPerThread;
+  if (T < kPlanWaves && (kPlanWaves - 1) / T * cap >= cpr) return (kPlanWaves - 1) / T;
+  const int wpr = kPlanWaves / T;
+  return wpr * cap >= cpr ? wpr : 0;
+}
+
+template <typename XT, int NS>
 __global__ void __launch_bounds__(kPlanThreads)
 front_small_kernel(const float* __restrict__ logits, const float* __restrict__ bias, int T, int E,
                    int k, int renormalize, const XT* __restrict__ x, int H, int32_t* ids, float* w,
                    uint8_t* x_q, float* x_s, uint8_t* xp_q, float* xp_s, int32_t* plan) {
-  extern __shared__ int smem[];           // plan_build_workgroup's E * 17 ints, then R ids
-  int* s_ids = smem + E * (1 + kPlanWaves);
+  // plan LDS: R <= 64: E 64-bit row masks + E offsets; otherwise E * 17 ints
+  extern __shared__ __align__(16) int smem[];
+  __shared__ int s_ids[kFrontMaxRows];
+  __shared__ int s_pos[kFrontMaxRows];
+  __shared__ float s_part[kPlanWaves];        // per-wave max |x|
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = T * k;
+  const int cpr = H >> 3;                     // 8-element chunks per row
+  const int wpr = front_waves_per_row(T, H);
+  const int row = wave / wpr, sub = wave - row * wpr;
+  const bool qrow = row < T;                  // this wave quantizes part of row `row`
+  const auto chunk = [&](int i) { return (i * wpr + sub) * kWave + lane; };
 
+  // ---- phase 1: chunk loads in flight, routing, per-wave max |x|
+  XChunk<XT> xc[kFrontChunksPerThread];
+#pragma unroll
+  for (int i = 0; i < kFrontChunksPerThread; ++i)
+    if (qrow && chunk(i) < cpr) xc[i].load(x + int64_t(row) * H + chunk(i) * 8);
   for (int t = wave; t < T; t += kPlanWaves) {
-    const int e = route_token_wave(logits + int64_t(t) * E, bias, E, k, renormalize,
-                                   ids + int64_t(t) * k, w + int64_t(t) * k, lane);
+    const int e = route_token_wave<NS>(logits + int64_t(t) * E, bias, E, k, renormalize,
+                                       ids + int64_t(t) * k, w + int64_t(t) * k, lane);
     if (lane < k) s_ids[t * k + lane] = e;
   }
-  __shared__ float s_part[kPlanWaves];
-  quant_rows_workgroup<XT>(x, T, H, x_q, x_s, s_part);
-  __threadfence_block();
-  __syncthreads();
-
-  plan_build_workgroup([&](int r) { return s_ids[r]; }, T, k, E, plan, smem);
-  __threadfence_block();
-  __syncthreads();
-
-  // gather: wave-strided over the placed rows, 16 bytes per lane per step
-  const PlanView pv = plan_view(plan, E, R);
-  const int n_rows = pv.offsets[E];
-  for (int p = wave; p < n_rows; p += kPlanWaves) {
-    const int t = pv.sorted_rows[p] / k;
-    const uint4* src = reinterpret_cast<const uint4*>(x_q + int64_t(t) * H);
-    uint4* dst = reinterpret_cast<uint4*>(xp_q + int64_t(p) * H);
-    for (int c = lane; c < H / 16; c += kWave) dst[c] = src[c];
-    if (lane == 0) xp_s[p] = x_s[t];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kFrontChunksPerThread; ++i) {
+    if (qrow && chunk(i) < cpr) {
+      float v[8];
+      xc[i].values(v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    }
   }
+  amax = wave_max(amax);
+  if (lane == 0) s_part[wave] = amax;
+  lds_barrier();
+
+  // ---- phase 2: plan, and E4M3 codes of this thread's chunks
+  if (R <= kWave && wave == kPlanWaves - 1)
+    plan_build_wave<NS>(s_ids, T, k, E, plan, reinterpret_cast<unsigned long long*>(smem),
+                        smem + 2 * E, s_pos, lane);
+  float scale = 0.0f;
+  uint2 codes[kFrontChunksPerThread] = {};
+  if (qrow) {
+    float m = 0.0f;
+    for (int i = 0; i < wpr; ++i) m = fmaxf(m, s_part[row * wpr + i]);
+    scale = fp8_scale(m);
+#pragma unroll
+    for (int i = 0; i < kFrontChunksPerThread; ++i) {
+      if (chunk(i) < cpr) {
+        float v[8];
+        xc[i].values(v);
+        codes[i] = fp8_codes8(v, scale);
+        *reinterpret_cast<uint2*>(x_q + int64_t(row) * H + chunk(i) * 8) = codes[i];
+      }
+    }
+    if (sub == 0 && lane == 0) x_s[row] = scale;
+  }
+  if (R > kWave) {
+    plan_build_workgroup([&](int r) { return s_ids[r]; }, T, k, E, plan, smem);
+    __threadfence_block();
+    __syncthreads();
+    const PlanView pv = plan_view(plan, E, R);
+    for (int r = tid; r < R; r += kPlanThreads) s_pos[r] = pv.row_pos[r];
+  }
+  lds_barrier();
+
+  // ---- phase 3: codes and scale to the plan positions of the row's token
+  if (qrow) {
+    for (int j = 0; j < k; ++j) {
+      const int p = s_pos[row * k + j];
+      if (p < 0) continue;
+#pragma unroll
+      for (int i = 0; i < kFrontChunksPerThread; ++i)
+        if (chunk(i) < cpr)
+          *reinterpret_cast<uint2*>(xp_q + int64_t(p) * H + chunk(i) * 8) = codes[i];
+      if (sub == 0 && lane == 0) xp_s[p] = scale;
+    }
+  }
+}
+
+template <typename XT, int NS>
+hipError_t launch_small(const float* logits, const float* bias, int T, int E, int k,
+                        int renormalize, const XT* x, int H, int32_t* ids, float* w,
+                        uint8_t* x_q, float* x_s, uint8_t* xp_q, float* xp_s, int32_t* plan,
+                        hipStream_t stream) {
+  const int R = T * k;
+  const size_t lds = size_t(E) * (R <= kWave ? 3 : 1 + kPlanWaves) * sizeof(int);
+  auto fn = front_small_kernel<XT, NS>;
+  hipError_t err;
+  if (lds > 64 * 1024 &&
+      (err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds))) != hipSuccess)
+    return err;
+  hipLaunchKernelGGL(fn, dim3(1), dim3(kPlanThreads), lds, stream, logits, bias, T, E, k,
+                     renormalize, x, H, ids, w, x_q, x_s, xp_q, xp_s, plan);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -56,34 +175,24 @@ hipError_t launch_front(const float* logits, const float* bias, int T, int E, in
                         int renormalize, const void* x, int x_dtype, int H, int32_t* ids, float* w,
                         uint8_t* x_q, float* x_s, uint8_t* xp_q, float* xp_s, void* plan,
                         hipStream_t stream) {
-  hipError_t err;
-  if (T > kFrontSmallT) {
+  if (T > kFrontSmallT || front_waves_per_row(T, H) == 0) {
+    hipError_t err;
     if ((err = launch_route_topk(logits, bias, T, E, k, renormalize, ids, w, stream)) != hipSuccess)
       return err;
     if ((err = launch_quant_fp8(x, x_dtype, T, H, H, x_q, x_s, stream)) != hipSuccess) return err;
     return launch_permute(ids, T, k, E, x_q, x_s, H, xp_q, xp_s, plan, stream);
   }
-  const size_t lds = (size_t(E) * (1 + kPlanWaves) + size_t(T) * k) * sizeof(int);
   int32_t* p = static_cast<int32_t*>(plan);
-  if (x_dtype == MOEQ_BF16) {
-    auto fn = front_small_kernel<uint16_t>;
-    if (lds > 64 * 1024 &&
-        (err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, int(lds))) != hipSuccess)
-      return err;
-    hipLaunchKernelGGL(fn, dim3(1), dim3(kPlanThreads), lds, stream, logits, bias, T, E, k,
-                       renormalize, static_cast<const uint16_t*>(x), H, ids, w, x_q, x_s, xp_q, xp_s,
-                       p);
-  } else {
-    auto fn = front_small_kernel<float>;
-    if (lds > 64 * 1024 &&
-        (err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, int(lds))) != hipSuccess)
-      return err;
-    hipLaunchKernelGGL(fn, dim3(1), dim3(kPlanThreads), lds, stream, logits, bias, T, E, k,
-                       renormalize, static_cast<const float*>(x), H, ids, w, x_q, x_s, xp_q, xp_s, p);
-  }
-  return hipGetLastError();
+  return with_route_slots(E, [&](auto ns) {
+    constexpr int NS = decltype(ns)::value;
+    if (x_dtype == MOEQ_BF16)
+      return launch_small<uint16_t, NS>(logits, bias, T, E, k, renormalize,
+                                        static_cast<const uint16_t*>(x), H, ids, w, x_q, x_s,
+                                        xp_q, xp_s, p, stream);
+    return launch_small<float, NS>(logits, bias, T, E, k, renormalize,
+                                   static_cast<const float*>(x), H, ids, w, x_q, x_s, xp_q, xp_s,
+                                   p, stream);
+  });
 }
 
 }  // namespace moeq

@@ -8,42 +8,51 @@
 
 namespace moeq {
 
+template <int N>
+struct SlotsTag { static constexpr int value = N; };
+
 // ------------------------------------------------------------------ routing
-constexpr int kRouteSlots = MOEQ_MAX_EXPERTS / kWave;   // scores held per lane
-
-__device__ __forceinline__ bool route_better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+// Scores are held in registers, NS per lane (expert e in lane e % 64, slot
+// e / 64); NS = 64-expert slots covering E, rounded up to a power of two.
+__host__ __device__ constexpr int route_slots_for(int E) {
+  return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16;
 }
 
-// wave-wide best (score, expert) pair, in every lane (DPP steps as wave_reduce)
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ void argmax_step(float& v, int& i) {
-  const float ov = dpp<CTRL, ROW_MASK>(v, v);
-  const int oi = dpp<CTRL, ROW_MASK>(i, i);
-  if (route_better(ov, oi, v, i)) { v = ov; i = oi; }
+// Order-preserving 32-bit key of a score: a larger float gives a larger key
+// (-0 is first made +0, so equal scores give equal keys).  Every float,
+// -inf included, gets a key above 0, which marks "no candidate".
+__device__ __forceinline__ uint32_t score_key(float v) {
+  const uint32_t b = f2u(v + 0.0f);
+  return b ^ ((b >> 31) ? 0xFFFFFFFFu : 0x80000000u);
 }
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  argmax_step<kDppQuadSwap1>(v, i);
-  argmax_step<kDppQuadSwap2>(v, i);
-  argmax_step<kDppRowHalfMirror>(v, i);
-  argmax_step<kDppRowMirror>(v, i);
-  argmax_step<kDppRowBcast15, 0xA>(v, i);
-  argmax_step<kDppRowBcast31, 0xC>(v, i);
-  v = readlane(v, 63);
-  i = readlane(i, 63);
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return u2f(k ^ ((k >> 31) ? 0x80000000u : 0xFFFFFFFFu));
 }
 
-// One wave routes one token.  Expert e's score lives in lane e % 64, slot e / 64.
-// k rounds of a wave-wide argmax pick the experts best first; the order (score
-// descending, expert index ascending) makes ties go to the lower index and the
-// result independent of the reduction order.  Lanes j < k write slot j.
-// Returns the expert chosen in slot `lane` (valid for lane < k).
+// The best candidate of the wave: the largest key, ties to the lowest expert
+// index.  Returns the expert index (every lane); the rare tie takes a second
+// reduction over the tied lanes' indices.
+__device__ __forceinline__ int wave_best(uint32_t key, int idx, uint32_t* best_key) {
+  const uint32_t kmax = static_cast<uint32_t>(
+      wave_reduce(int(key), [](int a, int b) { return int(max(uint32_t(a), uint32_t(b))); }, 0));
+  const uint64_t tied = __ballot(key == kmax);
+  *best_key = kmax;
+  if (__popcll(tied) == 1) return readlane(idx, __ffsll(static_cast<unsigned long long>(tied)) - 1);
+  return wave_reduce(key == kmax ? idx : 0x7FFFFFFF, [](int a, int b) { return min(a, b); },
+                     0x7FFFFFFF);
+}
+
+// One wave routes one token.  k rounds of a wave-wide argmax pick the experts
+// best first; the order (score descending, expert index ascending) makes ties go
+// to the lower index and the result independent of the reduction order.  Lanes
+// j < k write slot j.  Returns the expert chosen in slot `lane` (valid for lane < k).
+template <int NS>
 __device__ __forceinline__ int route_token_wave(const float* row, const float* bias, int E, int k,
                                                 int renormalize, int32_t* ids_row, float* w_row,
                                                 int lane) {
-  float s[kRouteSlots];
+  float s[NS];
 #pragma unroll
-  for (int j = 0; j < kRouteSlots; ++j) {
+  for (int j = 0; j < NS; ++j) {
     const int e = j * kWave + lane;
     float v = -INFINITY;
     if (e < E) {
@@ -52,7 +61,9 @@ __device__ __forceinline__ int route_token_wave(const float* row, const float* b
     }
     s[j] = v;
   }
-  uint32_t used = 0;                                    // slots already selected (bit j)
+  uint32_t key[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) key[j] = (j * kWave + lane < E) ? score_key(s[j]) : 0u;
   float sel_v[MOEQ_MAX_TOPK];
   int sel_e[MOEQ_MAX_TOPK];
 #pragma unroll
@@ -60,16 +71,20 @@ __device__ __forceinline__ int route_token_wave(const float* row, const float* b
     sel_v[r] = -INFINITY;
     sel_e[r] = 0;
     if (r >= k) continue;
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    // this lane's best remaining slot (the lower slot, i.e. expert, on ties)
+    uint32_t ck = 0;
+    int ci = 0x7FFFFFFF;
 #pragma unroll
-    for (int j = 0; j < kRouteSlots; ++j) {
-      const int e = j * kWave + lane;
-      if (e < E && !((used >> j) & 1u) && route_better(s[j], e, bv, bi)) { bv = s[j]; bi = e; }
+    for (int j = 0; j < NS; ++j)
+      if (key[j] > ck) { ck = key[j]; ci = j * kWave + lane; }
+    uint32_t bk;
+    const int bi = wave_best(ck, ci, &bk);
+    if ((bi & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+        if (j == (bi >> 6)) key[j] = 0u;              // taken
     }
-    wave_argmax(bv, bi);
-    if ((bi & 63) == lane) used |= 1u << (bi >> 6);
-    sel_v[r] = bv;
+    sel_v[r] = key_score(bk);
     sel_e[r] = bi;
   }
   const float smax = sel_v[0];
@@ -81,7 +96,7 @@ __device__ __forceinline__ int route_token_wave(const float* row, const float* b
   } else {
     float part = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kRouteSlots; ++j)
+    for (int j = 0; j < NS; ++j)
       if (j * kWave + lane < E) part += expf(s[j] - smax);
     den = wave_sum(part);
   }
@@ -95,6 +110,18 @@ __device__ __forceinline__ int route_token_wave(const float* row, const float* b
     w_row[lane] = expf(v - smax) / den;
   }
   return e;
+}
+
+// Calls fn(SlotsTag<NS>{}) with NS = route_slots_for(E).
+template <typename F>
+__host__ __forceinline__ auto with_route_slots(int E, F&& fn) {
+  switch (route_slots_for(E)) {
+    case 1: return fn(SlotsTag<1>{});
+    case 2: return fn(SlotsTag<2>{});
+    case 4: return fn(SlotsTag<4>{});
+    case 8: return fn(SlotsTag<8>{});
+    default: return fn(SlotsTag<16>{});
+  }
 }
 
 // ------------------------------------------------------- FP8 quantization
@@ -115,77 +142,49 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// scale = fp32(amax / 448) (IEEE division); 8 codes of x / scale (IEEE
-// division, E4M3 round-to-nearest-even, saturating) packed little-endian
+// scale = fp32(amax / 448) (IEEE division)
 __device__ __forceinline__ float fp8_scale(float amax) { return __fdiv_rn(amax, 448.0f); }
+
+// E4M3 codes of four values in [-448, 448], packed little-endian: the gfx950
+// conversion (round to nearest even, sign kept) equals f32_to_e4m3 there.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+
+// True where E4M3 rounding of a value within a few ulp of q may differ from
+// that of q: within 8 ulp of a rounding midpoint (the 20 fp32 mantissa bits
+// below E4M3's 3 are near 0x80000) or in E4M3's subnormal range (|q| < 2^-6).
+__device__ __forceinline__ bool e4m3_rounding_close(float q) {
+  const uint32_t a = f2u(q) & 0x7FFFFFFFu;
+  return (a != 0u && a < 0x3C800000u) || ((a & 0xFFFFFu) - 0x7FFF8u) <= 0x10u;
+}
+
+// 8 codes of x / s packed little-endian: E4M3 (round to nearest even,
+// saturating) of the IEEE fp32 quotient fl32(x / s).  The quotients are formed
+// as x * (1 / s) with the hardware reciprocal, within 3 ulp of fl32(x / s);
+// where that could round to a different code (e4m3_rounding_close) the lane
+// takes the IEEE division instead, so the codes always equal those of the
+// division.  s <= 0 gives zeros.
 __device__ __forceinline__ uint2 fp8_codes8(const float (&v)[8], float s) {
-  uint32_t lo = 0, hi = 0;
-  if (s > 0.0f) {
+  if (!(s > 0.0f)) return make_uint2(0u, 0u);
+  float q[8];
+  bool exact = !(s >= 0x1p-120f && s <= 0x1p120f);   // reciprocal normal and accurate
+  if (!exact) {
+    const float rs = __builtin_amdgcn_rcpf(s);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= f32_to_e4m3(__fdiv_rn(v[i], s)) << (8 * i);
-      hi |= f32_to_e4m3(__fdiv_rn(v[4 + i], s)) << (8 * i);
+    for (int i = 0; i < 8; ++i) {
+      q[i] = v[i] * rs;
+      exact = exact || e4m3_rounding_close(q[i]);
     }
   }
-  return make_uint2(lo, hi);
-}
-
-// One wave quantizes one row of K elements (K % 8 == 0).
-template <typename T>
-__device__ __forceinline__ void quant_row_wave(const T* row, int K, uint8_t* qrow, float* scale,
-                                               int lane) {
-  float amax = 0.0f;
-  for (int c = lane * 8; c < K; c += kWave * 8) {
-    float v[8];
-    load8(row + c, v);
+  if (exact) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    for (int i = 0; i < 8; ++i) q[i] = __fdiv_rn(v[i], s);
   }
-  amax = wave_max(amax);
-  const float s = fp8_scale(amax);
-  if (lane == 0) *scale = s;
-  for (int c = lane * 8; c < K; c += kWave * 8) {
-    float v[8];
-    load8(row + c, v);
-    *reinterpret_cast<uint2*>(qrow + c) = fp8_codes8(v, s);
-  }
-}
-
-// A 1024-thread workgroup quantizes T <= 16 rows: each row gets 16 / T waves
-// (its 8-element chunks strided over them), whose partial max|x| meet in LDS.
-template <typename T>
-__device__ __forceinline__ void quant_rows_workgroup(const T* x, int rows, int K, uint8_t* q,
-                                                     float* scale, float* s_part /* 16 floats */) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wpr = rows > 0 ? 16 / rows : 16;
-  const int row = wave / wpr, sub = wave - row * wpr;
-  const bool active = row < rows;
-  const T* xr = x + int64_t(active ? row : 0) * K;
-  const int step = wpr * kWave * 8;
-  float amax = 0.0f;
-  if (active) {
-    for (int c = (sub * kWave + lane) * 8; c < K; c += step) {
-      float v[8];
-      load8(xr + c, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    }
-  }
-  amax = wave_max(amax);
-  if (lane == 0) s_part[wave] = amax;
-  __syncthreads();
-  if (active) {
-    float m = 0.0f;
-    for (int w = 0; w < wpr; ++w) m = fmaxf(m, s_part[row * wpr + w]);
-    const float s = fp8_scale(m);
-    if (sub == 0 && lane == 0) scale[row] = s;
-    uint8_t* qr = q + int64_t(row) * K;
-    for (int c = (sub * kWave + lane) * 8; c < K; c += step) {
-      float v[8];
-      load8(xr + c, v);
-      *reinterpret_cast<uint2*>(qr + c) = fp8_codes8(v, s);
-    }
-  }
+  for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(q[i], -448.0f), 448.0f);
+  return make_uint2(e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7]));
 }
 
 // ---------------------------------------------------------- plan building
@@ -324,6 +323,90 @@ __device__ __forceinline__ void plan_build_workgroup(IdsF ids, int T, int k, int
       }
     }
     __syncthreads();
+  }
+}
+
+// Workgroup barrier that orders LDS accesses only (no wait for global stores).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Orders this wave's LDS accesses: the LDS unit serves one wave's operations in
+// issue order, so a wavefront-scope fence (a compiler barrier, no wait) makes
+// every lane's earlier LDS writes visible to the wave's later reads.
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The whole plan for R = T k <= 64 routed rows, built by one wave.  Every
+// routed row sets its bit (1 << r) in its expert's 64-bit LDS mask (atomic
+// OR, so arrival order does not matter); a row's rank within its expert is the
+// number of mask bits below it (stable order), an expert's count the mask's
+// population.  Wave scans over the experts (lane x % 64, pass x / 64) give the
+// offsets, and ballots the active list.  With at most 64 rows every active
+// expert owns exactly one tile.  The result equals plan_build_workgroup's.
+// NS: passes of 64 experts covering E.  s_mask: E 64-bit words of LDS, s_off:
+// E ints of LDS; s_pos[r] receives row_pos[r].
+template <int NS>
+__device__ __forceinline__ void plan_build_wave(const int* s_ids, int T, int k, int E,
+                                                int32_t* plan, unsigned long long* s_mask,
+                                                int* s_off, int* s_pos, int lane) {
+  const int R = T * k;
+  PlanView pv = plan_view(plan, E, R);
+  const int e = lane < R ? s_ids[lane] : -1;
+  const bool valid = lane < R && e >= 0 && e < E;
+  const int dropped = __popcll(__ballot(lane < R && !valid));
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+    if (lane + j * kWave < E) s_mask[lane + j * kWave] = 0ull;
+  lds_wave_sync();
+  if (valid) atomicOr(&s_mask[e], 1ull << lane);
+  lds_wave_sync();
+
+  int carry = 0, act_carry = 0;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int x = lane + j * kWave;
+    const int c = x < E ? __popcll(s_mask[x]) : 0;
+    const int incl = wave_inclusive_scan(c);
+    const int off = carry + incl - c;
+    carry += readlane(incl, kWave - 1);
+    const uint64_t nz = __ballot(c > 0);
+    if (x < E) {
+      pv.offsets[x] = off;
+      s_off[x] = off;
+    }
+    if (c > 0) {
+      const int a = act_carry + __popcll(nz & ((1ull << lane) - 1ull));
+      pv.active[a] = x;
+      pv.tile_expert[a] = x;
+      pv.tile_row0[a] = off;
+    }
+    act_carry += __popcll(nz);
+  }
+  if (lane == 0) {
+    pv.offsets[E] = carry;
+    plan[kPlanR] = R;
+    plan[kPlanE] = E;
+    plan[kPlanActive] = act_carry;
+    plan[kPlanTiles] = act_carry;
+    plan[kPlanT] = T;
+    plan[kPlanK] = k;
+    plan[kPlanDropped] = dropped;
+  }
+  if (lane > kPlanDropped && lane < kPlanHeader) plan[lane] = 0;
+  lds_wave_sync();
+  if (lane < R) {
+    int p = -1;
+    if (valid) {
+      p = s_off[e] + __popcll(s_mask[e] & ((1ull << lane) - 1ull));
+      pv.sorted_rows[p] = lane;
+    }
+    pv.row_pos[lane] = p;
+    s_pos[lane] = p;
   }
 }
 

@@ -60,15 +60,24 @@ constexpr int kThreads = 256;
 constexpr int kBN = 128;           // weight rows per tile-kernel workgroup
 constexpr int kRowDw = 36;         // LDS row stride in dwords (128 B + 16 B pad)
 constexpr int kXcds = 8;
-// weight groups in flight per wave (an FP8 group carries twice the bytes of an INT4 one)
+// weight groups in flight per wave (an FP8 group carries twice the bytes of an INT4
+// one); the tile kernel's ring also holds each group's activation share, so it
+// runs one group shallower to stay at three waves per SIMD
 #ifndef MOEQ_W4_DEPTH
 #define MOEQ_W4_DEPTH 4
 #endif
 #ifndef MOEQ_FP8_DEPTH
 #define MOEQ_FP8_DEPTH 2
 #endif
+#ifndef MOEQ_TILE_W4_DEPTH
+#define MOEQ_TILE_W4_DEPTH 3
+#endif
 template <int WFMT>
 struct Depth { static constexpr int value = (WFMT == kW4G128) ? MOEQ_W4_DEPTH : MOEQ_FP8_DEPTH; };
+template <int WFMT>
+struct TileDepth {
+  static constexpr int value = (WFMT == kW4G128) ? MOEQ_TILE_W4_DEPTH : MOEQ_FP8_DEPTH;
+};
 
 // INT4 nibble (code + 8) -> E4M3 byte of the code, four nibbles (one per byte,
 // values 0..15) at a time.  v_perm_b32 looks bytes up in an 8-byte table; a
@@ -400,12 +409,13 @@ gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
 // ------------------------------------------------------------- tile kernel
 template <int WFMT>
 struct TileStage {
+  uint4 a0, a1;          // this thread's 32-byte share of the group's activation slice
   BFrag<WFMT> b[2];
   float s[2];
 };
 
 template <int WFMT, int EPI, int GS>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, 3)   // >= 3 waves per SIMD
 gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
                  const int32_t* __restrict__ plan, int E, int R, const uint8_t* __restrict__ w,
                  const float* __restrict__ w_scale, int N, int K, void* __restrict__ out,
@@ -445,15 +455,13 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
 
   // A staging: thread -> (row tid / 4, 32-byte chunk tid % 4) of the 64 x 128 B slice;
   // rows past the tile read the tile's first row (MFMA rows are independent and
-  // those rows are never stored).
+  // those rows are never stored).  The slice of group g is loaded into registers
+  // in group g's ring slot, ahead of its weights in issue order, and written to
+  // LDS one group before its use: waiting for it never waits for the weight
+  // loads of later groups.
   const int st_row = tid >> 2, st_chunk = tid & 3;
   const bool st_valid = st_row < ti.rows;
   const uint8_t* a_src = a_q + int64_t(ti.row0 + (st_valid ? st_row : 0)) * K + st_chunk * 32;
-  auto load_a = [&](int g, uint4& x0, uint4& x1) {
-    const uint4* p = reinterpret_cast<const uint4*>(a_src + g * 128);
-    x0 = p[0];
-    x1 = p[1];
-  };
   auto store_a = [&](int buf, const uint4& x0, const uint4& x1) {
     const v8i o = (WFMT == kW4G128) ? shuffle_a(x0, x1) : as_v8i(x0, x1);
     uint4* dst = reinterpret_cast<uint4*>(&As[buf][st_row * kRowDw + st_chunk * 8]);
@@ -468,11 +476,14 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
     acc[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 
-  constexpr int kDepth = Depth<WFMT>::value;
+  constexpr int kDepth = TileDepth<WFMT>::value;
   TileStage<WFMT> st[kDepth];
   GroupScales<WFMT, GS> sc;
   sc.init(srow, kb);
   auto issue = [&](int slot, int g) {
+    const uint4* ap = reinterpret_cast<const uint4*>(a_src + g * 128);
+    st[slot].a0 = ap[0];
+    st[slot].a1 = ap[1];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       st[slot].b[j].load(wrow[j], g, kb);
@@ -482,8 +493,13 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
   auto consume = [&](int slot, int g, bool refill) {
     const int buf = g & 1;
     const bool more = g + 1 < G;
-    uint4 x0, x1;
-    if (more) load_a(g + 1, x0, x1);
+    if (g == 0) {
+      store_a(0, st[slot].a0, st[slot].a1);
+      __syncthreads();
+    }
+    // the next group's slice (its slot is not the one refilled below)
+    const int next = (slot + 1 == kDepth) ? 0 : slot + 1;
+    const uint4 x0 = st[next].a0, x1 = st[next].a1;
     const v8i b0 = st[slot].b[0].operand();
     const v8i b1 = st[slot].b[1].operand();
     const float s0 = sc.get(0, g, ln, st[slot].s[0]), s1 = sc.get(1, g, ln, st[slot].s[1]);
@@ -501,12 +517,6 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
     if (more) store_a(buf ^ 1, x0, x1);
     __syncthreads();
   };
-  {
-    uint4 x0, x1;
-    load_a(0, x0, x1);
-    store_a(0, x0, x1);
-  }
-  __syncthreads();
   pipeline<kDepth, GS>(G, issue, consume);
 
 #pragma unroll

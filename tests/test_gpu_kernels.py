@@ -39,6 +39,28 @@ def test_route_topk(T, E, k, renorm):
     np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-6, atol=0)
 
 
+@pytest.mark.parametrize("E,k", [(256, 6), (1000, 8), (77, 3)])
+def test_route_topk_ties_across_lanes_and_signed_zeros(E, k):
+    """Equal scores in different lanes and slots go to the lower expert index;
+    -0 and +0 are the same score; -inf scores are still selectable."""
+    T = 6
+    logits = torch.full((T, E), -1.0)
+    logits[0, [3, 67, E - 9, E - 1]] = 2.0               # same score, several slots
+    logits[1, :] = 0.0
+    logits[1, 1::2] = -0.0                              # all zeros of both signs
+    logits[2, [E - 1, E - 2, 5]] = torch.tensor([7.0, 7.0, 7.0])
+    logits[3, :] = float("-inf")
+    logits[3, E // 2] = 0.5                             # one finite score, the rest -inf
+    logits[4] = torch.randn(E, generator=torch.Generator().manual_seed(E))
+    logits[5, :] = 1e-30
+    logits[5, 0] = -1e-30
+    ids, w = mq.moe_route_topk(logits.to(_dev()), k)
+    torch.cuda.synchronize()
+    rid, rw = L.route_topk(logits.numpy(), k, None, True)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-6, atol=0)
+
+
 def test_route_empty():
     ids, w = mq.moe_route_topk(torch.zeros(0, 16, device=_dev()), 2)
     assert ids.shape == (0, 2)
@@ -157,15 +179,27 @@ def test_permute_plan_only_and_empty():
     assert (f["offsets"].numpy() == 0).all() and f["header"][3] == 0
 
 
-@pytest.mark.parametrize("T,E,k,H,dtype", [(4, 256, 6, 4096, torch.bfloat16), (1, 8, 2, 256, torch.float32),
-                                           (16, 1000, 8, 512, torch.bfloat16), (17, 64, 3, 256, torch.bfloat16),
-                                           (300, 256, 6, 128, torch.bfloat16), (0, 16, 2, 64, torch.float32)])
-def test_route_quant_permute_fused_matches_separate_and_oracle(T, E, k, H, dtype):
+# one-wave plan (R <= 64) with the plan wave outside (T = 4, 5) or inside (T = 8)
+# the quantizing waves, workgroup plan (R > 64), a row narrower than a wave
+# (H = 48), the largest fused rows (T = 16, H = 2048), the separate-kernel
+# fallbacks (T > 16, or rows too long), a single expert, a hot expert, no tokens
+@pytest.mark.parametrize("T,E,k,H,dtype,hot", [
+    (4, 256, 6, 4096, torch.bfloat16, False), (1, 8, 2, 256, torch.float32, False),
+    (5, 256, 6, 4096, torch.float32, False), (8, 256, 6, 4096, torch.bfloat16, False),
+    (16, 1000, 8, 512, torch.bfloat16, False), (8, 64, 8, 48, torch.bfloat16, False),
+    (8, 1000, 8, 1024, torch.float32, False), (16, 384, 6, 2048, torch.bfloat16, False),
+    (16, 256, 6, 4096, torch.bfloat16, False), (3, 1, 1, 80, torch.bfloat16, False),
+    (6, 256, 6, 2048, torch.bfloat16, True), (12, 256, 6, 4096, torch.bfloat16, True),
+    (17, 64, 3, 256, torch.bfloat16, False), (300, 256, 6, 128, torch.bfloat16, False),
+    (0, 16, 2, 64, torch.float32, False)])
+def test_route_quant_permute_fused_matches_separate_and_oracle(T, E, k, H, dtype, hot):
     g = torch.Generator().manual_seed(T * 31 + E + H)
     logits = torch.randn(T, E, generator=g)
     if T > 1:
         logits[1] = logits[0]                       # identical tokens -> equal ids
     bias = torch.randn(E, generator=g) if E % 2 == 0 else None
+    if hot:
+        bias[5] = 100.0                             # every token routes to expert 5 first
     x = (torch.randn(T, H, generator=g) * 3).to(dtype)
     if T > 2:
         x[2] = 0                                    # zero row
