@@ -51,6 +51,10 @@ _SIGNATURES = {
     "pack_int4_g128": (_I, [_P, _I64, _I, _P, _P, _P]),
     "moe_grouped_gemm_w4a8": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_grouped_gemm_fp8row": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
+    "moe_expert_mlp_w4a8": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P,
+                                 _P]),
+    "moe_expert_mlp_fp8row": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P,
+                                   _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_shared_gemm_bf16": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
 }
@@ -279,6 +283,63 @@ def moe_grouped_gemm_fp8row(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Te
         raise ValueError("w_row_scale shape does not match w_fp8")
     return _gemm("moe_grouped_gemm_fp8row", a_q, a_s, plan, E, w_fp8, w_row_scale, N, K,
                  epilogue, out_dtype, out)
+
+
+def _expert_mlp(fn_name: str, xp_q, xp_s, plan, E, w13, s13, w2, s2, H, I, out):
+    _req(xp_q, "xp_q", torch.uint8, 2)
+    _req(xp_s, "xp_s", torch.float32, 1)
+    _req(plan, "plan", torch.int32, 1)
+    R = xp_q.shape[0]
+    if xp_q.shape[1] != H:
+        raise ValueError("xp_q has the wrong H")
+    dev = xp_q.device
+    o = dict(out) if out is not None else {}
+    o.setdefault("h", torch.empty(R, I, dtype=torch.bfloat16, device=dev))
+    o.setdefault("h_q", torch.empty(R, I, dtype=torch.uint8, device=dev))
+    o.setdefault("h_s", torch.empty(R, dtype=torch.float32, device=dev))
+    o.setdefault("o", torch.empty(R, H, dtype=torch.bfloat16, device=dev))
+    fn = getattr(lib, fn_name)
+    _check(fn_name, fn(_ptr(xp_q), _ptr(xp_s), _ptr(plan), plan.numel() * 4, E, R, _ptr(w13),
+                       _ptr(s13), _ptr(w2), _ptr(s2), H, I, _ptr(o["h"]), _ptr(o["h_q"]),
+                       _ptr(o["h_s"]), _ptr(o["o"]), _stream(dev)))
+    return o
+
+
+def moe_expert_mlp_w4a8(xp_q: torch.Tensor, xp_s: torch.Tensor, plan: torch.Tensor,
+                        w13: torch.Tensor, w13_scales: torch.Tensor, w2: torch.Tensor,
+                        w2_scales: torch.Tensor, out: Optional[dict] = None) -> dict:
+    """gate/up GEMM + SiLU, FP8 quantization of h, down GEMM (two launches for R <= 64).
+    w13 [E, 2I, H/2], w13_scales [E, 2I, H/128], w2 [E, H, I/2], w2_scales [E, H, I/128].
+    Returns a dict with h, h_q, h_s, o (reusing `out`'s tensors)."""
+    for t, name in ((w13, "w13"), (w2, "w2")):
+        _req(t, name, torch.uint8, 3)
+    for t, name in ((w13_scales, "w13_scales"), (w2_scales, "w2_scales")):
+        _req(t, name, torch.float32, 3)
+    E, N13, H2 = w13.shape
+    H, I = 2 * H2, N13 // 2
+    if tuple(w2.shape) != (E, H, I // 2) or tuple(w13_scales.shape) != (E, N13, H // 128) or \
+            tuple(w2_scales.shape) != (E, H, I // 128):
+        raise ValueError("w13 / w2 / scale shapes do not match")
+    return _expert_mlp("moe_expert_mlp_w4a8", xp_q, xp_s, plan, E, w13, w13_scales, w2, w2_scales,
+                       H, I, out)
+
+
+def moe_expert_mlp_fp8row(xp_q: torch.Tensor, xp_s: torch.Tensor, plan: torch.Tensor,
+                          w13: torch.Tensor, w13_scales: torch.Tensor, w2: torch.Tensor,
+                          w2_scales: torch.Tensor, out: Optional[dict] = None) -> dict:
+    """moe_expert_mlp_w4a8 with E4M3 weights: w13 [E, 2I, H], w13_scales [E, 2I],
+    w2 [E, H, I], w2_scales [E, H]."""
+    for t, name in ((w13, "w13"), (w2, "w2")):
+        _req(t, name, torch.uint8, 3)
+    for t, name in ((w13_scales, "w13_scales"), (w2_scales, "w2_scales")):
+        _req(t, name, torch.float32, 2)
+    E, N13, H = w13.shape
+    I = N13 // 2
+    if tuple(w2.shape) != (E, H, I) or tuple(w13_scales.shape) != (E, N13) or \
+            tuple(w2_scales.shape) != (E, H):
+        raise ValueError("w13 / w2 / scale shapes do not match")
+    return _expert_mlp("moe_expert_mlp_fp8row", xp_q, xp_s, plan, E, w13, w13_scales, w2,
+                       w2_scales, H, I, out)
 
 
 def moe_combine(o: torch.Tensor, plan: torch.Tensor, topk_w: torch.Tensor,

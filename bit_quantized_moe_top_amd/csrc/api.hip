@@ -161,6 +161,46 @@ int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* pl
                      out_dtype, stream);
 }
 
+static int mlp_common(int wfmt, const uint8_t* xp_q, const float* xp_s, const void* plan,
+                      size_t plan_bytes, int E, int R, const uint8_t* w13, const float* s13,
+                      const uint8_t* w2, const float* s2, int H, int I, uint16_t* h, uint8_t* h_q,
+                      float* h_s, uint16_t* o, void* stream) {
+  if (R < 0 || E <= 0 || H <= 0 || I <= 0) return MOEQ_ERR_INVALID_ARG;
+  if (E > MOEQ_MAX_EXPERTS) return MOEQ_ERR_UNSUPPORTED;
+  if (H % 128 != 0 || I % 128 != 0) return MOEQ_ERR_UNSUPPORTED;
+  if (int64_t(2 * int64_t(I) / 128) * moeq::plan_max_tiles(E, R) > 0x7FFFFFF0 ||
+      int64_t(H / 128) * moeq::plan_max_tiles(E, R) > 0x7FFFFFF0)
+    return MOEQ_ERR_UNSUPPORTED;
+  if (R > 0 && (!xp_q || !xp_s || !plan || !w13 || !s13 || !w2 || !s2 || !h || !h_q || !h_s || !o))
+    return MOEQ_ERR_INVALID_ARG;
+  if (R > 0 && (!aligned16(xp_q) || !aligned16(h_q) || !aligned16(h) || !aligned16(w13) ||
+                !aligned16(s13) || !aligned16(w2) || !aligned16(s2)))
+    return MOEQ_ERR_INVALID_ARG;
+  if (R == 0) return MOEQ_OK;
+  if (reinterpret_cast<uintptr_t>(plan) & 3u) return MOEQ_ERR_INVALID_ARG;
+  if (plan_bytes < moe_plan_size(E, R)) return MOEQ_ERR_WORKSPACE;
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_expert_mlp(wfmt, xp_q, xp_s, plan, E, R, w13, s13, w2, s2, H,
+                                               I, h, h_q, h_s, o, as_stream(stream)));
+}
+
+int moe_expert_mlp_w4a8(const uint8_t* xp_q, const float* xp_s, const void* plan, size_t plan_bytes,
+                        int E, int R, const uint8_t* w13, const float* w13_scales,
+                        const uint8_t* w2, const float* w2_scales, int H, int I, uint16_t* h,
+                        uint8_t* h_q, float* h_s, uint16_t* o, void* stream) {
+  return mlp_common(moeq::kW4G128, xp_q, xp_s, plan, plan_bytes, E, R, w13, w13_scales, w2,
+                    w2_scales, H, I, h, h_q, h_s, o, stream);
+}
+
+int moe_expert_mlp_fp8row(const uint8_t* xp_q, const float* xp_s, const void* plan,
+                          size_t plan_bytes,
+                          int E, int R, const uint8_t* w13, const float* w13_scales,
+                          const uint8_t* w2, const float* w2_scales, int H, int I, uint16_t* h,
+                          uint8_t* h_q, float* h_s, uint16_t* o, void* stream) {
+  return mlp_common(moeq::kFp8Row, xp_q, xp_s, plan, plan_bytes, E, R, w13, w13_scales, w2,
+                    w2_scales, H, I, h, h_q, h_s, o, stream);
+}
+
 int moe_combine(const uint16_t* o, const void* plan, const float* topk_w, const uint16_t* shared,
                 int T, int k, int H, uint16_t* y, void* stream) {
   if (T < 0 || k <= 0 || H <= 0) return MOEQ_ERR_INVALID_ARG;

@@ -30,14 +30,7 @@ template <>
 struct XChunk<uint16_t> {
   uint4 raw;
   __device__ __forceinline__ void load(const uint16_t* p) { raw = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void values(float (&v)[8]) const {
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = u2f(w[i] << 16);
-      v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
-    }
-  }
+  __device__ __forceinline__ void values(float (&v)[8]) const { bf16x8_to_f32(raw, v); }
 };
 template <>
 struct XChunk<float> {

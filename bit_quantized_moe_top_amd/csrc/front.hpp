@@ -127,64 +127,13 @@ __host__ __forceinline__ auto with_route_slots(int E, F&& fn) {
 // ------------------------------------------------------- FP8 quantization
 // 8 consecutive elements (16 B of bf16 or 32 B of fp32) -> fp32
 __device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = u2f(w[i] << 16);
-    v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
-  }
+  bf16x8_to_f32(*reinterpret_cast<const uint4*>(p), v);
 }
 __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
   const float4 a = *reinterpret_cast<const float4*>(p);
   const float4 b = *reinterpret_cast<const float4*>(p + 4);
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
-// scale = fp32(amax / 448) (IEEE division)
-__device__ __forceinline__ float fp8_scale(float amax) { return __fdiv_rn(amax, 448.0f); }
-
-// E4M3 codes of four values in [-448, 448], packed little-endian: the gfx950
-// conversion (round to nearest even, sign kept) equals f32_to_e4m3 there.
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
-}
-
-// True where E4M3 rounding of a value within a few ulp of q may differ from
-// that of q: within 8 ulp of a rounding midpoint (the 20 fp32 mantissa bits
-// below E4M3's 3 are near 0x80000) or in E4M3's subnormal range (|q| < 2^-6).
-__device__ __forceinline__ bool e4m3_rounding_close(float q) {
-  const uint32_t a = f2u(q) & 0x7FFFFFFFu;
-  return (a != 0u && a < 0x3C800000u) || ((a & 0xFFFFFu) - 0x7FFF8u) <= 0x10u;
-}
-
-// 8 codes of x / s packed little-endian: E4M3 (round to nearest even,
-// saturating) of the IEEE fp32 quotient fl32(x / s).  The quotients are formed
-// as x * (1 / s) with the hardware reciprocal, within 3 ulp of fl32(x / s);
-// where that could round to a different code (e4m3_rounding_close) the lane
-// takes the IEEE division instead, so the codes always equal those of the
-// division.  s <= 0 gives zeros.
-__device__ __forceinline__ uint2 fp8_codes8(const float (&v)[8], float s) {
-  if (!(s > 0.0f)) return make_uint2(0u, 0u);
-  float q[8];
-  bool exact = !(s >= 0x1p-120f && s <= 0x1p120f);   // reciprocal normal and accurate
-  if (!exact) {
-    const float rs = __builtin_amdgcn_rcpf(s);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      q[i] = v[i] * rs;
-      exact = exact || e4m3_rounding_close(q[i]);
-    }
-  }
-  if (exact) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = __fdiv_rn(v[i], s);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(q[i], -448.0f), 448.0f);
-  return make_uint2(e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7]));
 }
 
 // ---------------------------------------------------------- plan building

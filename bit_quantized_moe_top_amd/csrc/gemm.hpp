@@ -1,0 +1,451 @@
+// Grouped GEMM over routed experts on the gfx950 FP8 matrix cores: the device
+// building blocks shared by the grouped GEMM kernels (gemm.hip) and the fused
+// expert MLP (mlp.hip).
+//
+//   out[p, n] = epilogue( a_s[p] * sum_g s_w[e, n, g] * sum_{k in g} a[p, k] * W[e, n, k] )
+//
+// Weight formats:
+//   kW4G128 -- INT4 codes, two per byte (low nibble first), one fp32 scale per
+//              (output row, 128-wide K group).  Each code is converted exactly to
+//              its OCP E4M3 byte with two v_perm_b32 table lookups and an xor, so
+//              the products run on v_mfma_f32_16x16x128_f8f6f4 (FP8 x FP8, fp32
+//              accumulate).  One MFMA covers exactly one 128-wide group: its fp32
+//              result is the group's partial sum, which is scaled by the group
+//              scale and added to the running fp32 accumulator.
+//   kFp8Row -- E4M3 weights with one fp32 scale per output row: the MFMA
+//              accumulates over all of K and the row scale is applied at the end.
+//
+// MFMA operand layout (16x16x128, 8 VGPRs per operand): lane (r = l % 16,
+// kb = l / 16) supplies 32 K-values of row r; the result lane l holds column
+// l % 16 of rows 4 (l / 16) + v, v = 0..3.  The MFMA sums over K, so any K
+// permutation applied identically to both operands leaves the result unchanged:
+// lane kb takes K-range [32 kb, 32 kb + 32) of the group, and for INT4 weights
+// the activation bytes of each 8-byte chunk are reordered to (0,2,4,6,1,3,5,7),
+// the order in which the nibble unpack produces the codes (low nibbles, then
+// high nibbles).
+//
+// Each wave owns two 16-column blocks of weight rows: for EPI_NONE 32
+// consecutive output columns, for EPI_SILU_MUL 16 gate rows and the matching 16
+// up rows (N/2 further), so the SiLU-gated product forms in registers.  A lane
+// streams 16 B of packed weights (32 codes) per block per group: lane (n, kb)
+// reads bytes [16 kb, 16 kb + 16) of its row's 64-byte group.  Weight loads run
+// kDepth groups ahead of their use (a register ring, unrolled so every ring
+// index is static) to keep enough bytes in flight to cover HBM latency.
+//
+// Two GEMM kernels share this arithmetic (the fused expert MLP runs the wave
+// kernel's units):
+//  * wave kernel (few rows per expert, e.g. decode): every wave is independent.
+//    Its unit is (plan tile, 32 weight rows); it reads its own activation
+//    fragment straight from global memory (tiny, cache-resident), so there is
+//    no LDS and no barrier in the K loop.  Tiles with more than 16 rows are swept
+//    once per 16-row block.
+//  * tile kernel (prefill): a 256-thread workgroup owns one plan tile (<= 64
+//    rows) x 128 weight rows.  The 64 x 128 B activation slice of each group is
+//    staged once in LDS (double-buffered, one barrier per group) and shared by
+//    the four waves, each of which runs all four 16-row blocks against its own
+//    32 weight rows.  The linear workgroup id is remapped so that each XCD
+//    (workgroups are dispatched to the 8 XCDs round-robin) receives a contiguous
+//    run of (tile, N-tile) pairs: the N-tiles of one row tile share that tile's
+//    activations in one L2.
+// Both grids are sized on the host from R alone; units past the plan's tile
+// count exit at once, so nothing is read back from the device.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moeq {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kBN = 128;           // weight rows per tile-kernel workgroup
+constexpr int kRowDw = 36;         // LDS row stride in dwords (128 B + 16 B pad)
+constexpr int kXcds = 8;
+// weight groups in flight per wave (an FP8 group carries twice the bytes of an INT4
+// one); the tile kernel's ring also holds each group's activation share, so it
+// runs one group shallower to stay at three waves per SIMD
+#ifndef MOEQ_W4_DEPTH
+#define MOEQ_W4_DEPTH 4
+#endif
+#ifndef MOEQ_FP8_DEPTH
+#define MOEQ_FP8_DEPTH 2
+#endif
+#ifndef MOEQ_TILE_W4_DEPTH
+#define MOEQ_TILE_W4_DEPTH 3
+#endif
+template <int WFMT>
+struct Depth { static constexpr int value = (WFMT == kW4G128) ? MOEQ_W4_DEPTH : MOEQ_FP8_DEPTH; };
+template <int WFMT>
+struct TileDepth {
+  static constexpr int value = (WFMT == kW4G128) ? MOEQ_TILE_W4_DEPTH : MOEQ_FP8_DEPTH;
+};
+
+// INT4 nibble (code + 8) -> E4M3 byte of the code, four nibbles (one per byte,
+// values 0..15) at a time.  v_perm_b32 looks bytes up in an 8-byte table; a
+// selector byte of 8..11 yields the replicated sign bit of table byte 1/3/5/7,
+// 12 yields 0x00 and 13..15 yield 0xFF.  With the raw nibble as selector into
+// table T and (nibble & 7) into table U, T[n] ^ U[n] is the answer for n < 8 and
+// special(n) ^ U[n - 8] for n >= 8; the tables below satisfy both.
+constexpr uint32_t kLutT0 = 0x8E8C09D0u, kLutT1 = 0x09737180u;
+constexpr uint32_t kLutU0 = 0x4440C700u, kLutU1 = 0xB1B3B548u;
+
+__device__ __forceinline__ uint32_t nib4_to_e4m3(uint32_t n4, uint32_t n4_low3) {
+  return __builtin_amdgcn_perm(kLutT1, kLutT0, n4) ^ __builtin_amdgcn_perm(kLutU1, kLutU0, n4_low3);
+}
+
+// 16 packed bytes (32 codes) -> the 32 E4M3 bytes of one MFMA operand, in the
+// order (codes 0,2,4,6)(1,3,5,7)(8,10,12,14)(9,11,13,15)...
+__device__ __forceinline__ v8i unpack_w4(const uint4& p) {
+  const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+  v8i r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t sh = w[i] >> 4;
+    r[2 * i] = int(nib4_to_e4m3(w[i] & 0x0F0F0F0Fu, w[i] & 0x07070707u));
+    r[2 * i + 1] = int(nib4_to_e4m3(sh & 0x0F0F0F0Fu, sh & 0x07070707u));
+  }
+  return r;
+}
+
+// activation bytes of one lane (32 consecutive K) -> operand order matching unpack_w4
+__device__ __forceinline__ v8i shuffle_a(const uint4& x0, const uint4& x1) {
+  const uint32_t d[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  v8i r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[2 * i] = int(__builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x06040200u));
+    r[2 * i + 1] = int(__builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x07050301u));
+  }
+  return r;
+}
+
+__device__ __forceinline__ v8i as_v8i(const uint4& x0, const uint4& x1) {
+  v8i r;
+  r[0] = int(x0.x); r[1] = int(x0.y); r[2] = int(x0.z); r[3] = int(x0.w);
+  r[4] = int(x1.x); r[5] = int(x1.y); r[6] = int(x1.z); r[7] = int(x1.w);
+  return r;
+}
+
+// One group scale.  A relaxed atomic load: the compiler may neither merge the
+// scale loads of different groups into wide loads hoisted ahead of the K sweep
+// (which costs registers and spills in the unrolled sweep) nor move them.
+__device__ __forceinline__ float load_scale(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// weight fragment of one lane for one 16-row block and one group
+template <int WFMT>
+struct BFrag;
+
+template <>
+struct BFrag<kW4G128> {
+  uint4 raw;
+  __device__ __forceinline__ void load(const uint8_t* row, int g, int kb) {
+    raw = *reinterpret_cast<const uint4*>(row + g * 64 + kb * 16);
+  }
+  __device__ __forceinline__ v8i operand() const { return unpack_w4(raw); }
+};
+
+template <>
+struct BFrag<kFp8Row> {
+  uint4 raw0, raw1;
+  __device__ __forceinline__ void load(const uint8_t* row, int g, int kb) {
+    const uint4* p = reinterpret_cast<const uint4*>(row + g * 128 + kb * 32);
+    raw0 = p[0];
+    raw1 = p[1];
+  }
+  __device__ __forceinline__ v8i operand() const { return as_v8i(raw0, raw1); }
+};
+
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
+  // cbsz = blgp = 0: both operands FP8 E4M3; no block scales.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+struct TileInfo {
+  int e, row0, rows;
+};
+
+__device__ __forceinline__ TileInfo tile_info(const int32_t* plan, int E, int R, int tile) {
+  const PlanView pv = plan_view(const_cast<int32_t*>(plan), E, R);
+  TileInfo t;
+  t.e = pv.tile_expert[tile];
+  t.row0 = pv.tile_row0[tile];
+  t.rows = min(MOEQ_TILE_M, pv.offsets[t.e + 1] - t.row0);
+  return t;
+}
+
+// weight-row bases (16-row block j of this wave) and their scale rows
+template <int WFMT, int NB = 2>
+__device__ __forceinline__ void weight_rows(const uint8_t* w, const float* w_scale, int e, int N,
+                                            int K, const int (&col)[NB], int ln,
+                                            const uint8_t* (&wrow)[NB], const float* (&srow)[NB]) {
+  const int64_t row_bytes = (WFMT == kW4G128) ? (K >> 1) : K;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int64_t n_glob = int64_t(e) * N + col[j] + ln;
+    wrow[j] = w + n_glob * row_bytes;
+    srow[j] = (WFMT == kW4G128) ? (w_scale + n_glob * (K >> 7)) : (w_scale + n_glob);
+  }
+}
+
+// epilogue for one 16-row block: lane holds rows 4 kb + v, column col[j] + ln;
+// row_scale(p) is the activation scale of sorted row p
+// the weight-row scales applied at the end (row-scaled FP8 only)
+template <int WFMT, int NB = 2>
+__device__ __forceinline__ void row_scales(const float* const (&srow)[NB], float (&rs)[NB]) {
+#pragma unroll
+  for (int j = 0; j < NB; ++j) rs[j] = (WFMT == kFp8Row) ? srow[j][0] : 1.0f;
+}
+
+// SiLU-gated product of result row v (gate block 0, up block 1) as bf16
+__device__ __forceinline__ uint16_t silu_mul_bf16(const v4f (&acc)[2], int v, float sa,
+                                                  const float (&rs)[2]) {
+  const float v0 = sa * acc[0][v] * rs[0];
+  const float v1 = sa * acc[1][v] * rs[1];
+  return f32_to_bf16(silu_f32(v0) * v1);
+}
+
+// (EPI_SILU_MUL needs NB == 2: block 0 gate rows, block 1 the matching up rows)
+template <int WFMT, int EPI, int NB = 2, typename RowScaleF>
+__device__ __forceinline__ void store_block(const v4f (&acc)[NB], int rb, int row0, int rows,
+                                            RowScaleF&& row_scale, const float* const (&srow)[NB],
+                                            const int (&col)[NB], int ln, int kb, int N, void* out,
+                                            int out_f32) {
+  float rs[NB];
+  row_scales<WFMT, NB>(srow, rs);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int r_in = 16 * rb + 4 * kb + v;
+    if (r_in >= rows) continue;
+    const int p = row0 + r_in;
+    const float sa = row_scale(p);
+    if constexpr (EPI == MOEQ_EPI_SILU_MUL && NB == 2) {
+      uint16_t* o = static_cast<uint16_t*>(out) + int64_t(p) * (N >> 1);
+      o[col[0] + ln] = silu_mul_bf16(acc, v, sa, rs);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const float vj = sa * acc[j][v] * rs[j];
+        if (out_f32)
+          static_cast<float*>(out)[int64_t(p) * N + col[j] + ln] = vj;
+        else
+          static_cast<uint16_t*>(out)[int64_t(p) * N + col[j] + ln] = f32_to_bf16(vj);
+      }
+    }
+  }
+}
+
+// An empty volatile asm that reads and writes the accumulator: it is ordered
+// with the surrounding memory operations and scheduling barriers, so the
+// arithmetic producing the accumulator cannot drift past it.
+__device__ __forceinline__ void pin(v4f& a) {
+  asm volatile("" : "+v"(a));
+}
+
+template <int WFMT>
+__device__ __forceinline__ void accumulate(v4f& acc, const v8i& a, const v8i& b, float s) {
+  if (WFMT == kW4G128) {
+    const v4f part = mfma_fp8(a, b, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = fmaf(s, part[v], acc[v]);
+  } else {
+    acc = mfma_fp8(a, b, acc);
+  }
+}
+
+// Runs consume(slot, g, refill) for g = 0 .. G-1 over a ring of kDepth slots
+// that issue(slot, g) fills kDepth groups ahead (the first kDepth issues are
+// left to the caller when kPrologue is false).  With GS > 0 (G == GS known at
+// compile time) the whole sweep is unrolled: no value is carried around a loop
+// back-edge, so every load lands directly in its slot's registers and stays in
+// flight until its use.  GS == 0 handles any G with a runtime loop.
+template <int kDepth, int GS, bool kPrologue = true, typename IssueF, typename ConsumeF>
+__device__ __forceinline__ void pipeline(int G, IssueF&& issue, ConsumeF&& consume) {
+  if constexpr (GS > 0) {
+    if constexpr (kPrologue) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d)
+        if (d < GS) issue(d, d);
+    }
+#pragma unroll
+    for (int g = 0; g < GS; ++g) consume(g % kDepth, g, g + kDepth < GS);
+  } else {
+    if constexpr (kPrologue) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d)
+        if (d < G) issue(d, d);
+    }
+    int g0 = 0;
+    for (; g0 + 2 * kDepth <= G; g0 += kDepth) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) consume(d, g0 + d, true);
+    }
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+      if (g0 + d < G) consume(d, g0 + d, g0 + d + kDepth < G);
+    g0 += kDepth;
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+      if (g0 + d < G) consume(d, g0 + d, false);
+  }
+}
+
+// Group scales of this lane's two weight rows (col[0] + ln and col[1] + ln).
+// With G = GS known at compile time the G scales of a row are spread over its
+// four lanes (ln, kb): lane kb holds groups [kb G/4, (kb+1) G/4), fetched with
+// 16-byte loads once per sweep, and the scale of group g comes from lane
+// (ln, g / (G/4)) by a cross-lane read.  This keeps the per-group scale reads
+// (16 rows x 4 bytes, 16 cache lines per instruction) out of the vector memory
+// pipeline, which they would otherwise congest as much as the weights do.
+// Otherwise (any G) one load per row and group.
+template <int WFMT, int GS, int NB = 2>
+struct GroupScales {
+  static constexpr bool kPreload = (WFMT == kW4G128) && GS > 0 && GS % 16 == 0;
+  static constexpr int kPerLane = kPreload ? GS / 4 : 1;
+  float v[NB][kPerLane];
+  const float* row[NB];
+
+  __device__ __forceinline__ void init(const float* const (&srow)[NB], int kb) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) row[j] = srow[j];
+    if constexpr (kPreload) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int i = 0; i < kPerLane; i += 4) {
+          const float4 f = *reinterpret_cast<const float4*>(srow[j] + kb * kPerLane + i);
+          v[j][i] = f.x; v[j][i + 1] = f.y; v[j][i + 2] = f.z; v[j][i + 3] = f.w;
+        }
+    }
+  }
+  // scale of group g for block j; `held` is the value a ring stage loaded (non-preload path)
+  __device__ __forceinline__ float get(int j, int g, int ln, float held) const {
+    if constexpr (kPreload) {
+      return __shfl(v[j][g % kPerLane], ln + 16 * (g / kPerLane), 64);
+    } else {
+      return held;
+    }
+  }
+  __device__ __forceinline__ float load(int j, int g) const {
+    if constexpr (kPreload || WFMT != kW4G128) return 1.0f;
+    else return load_scale(row[j] + g);
+  }
+};
+
+// ------------------------------------------------------------- wave kernel
+template <int WFMT, int NB>
+struct WaveStage {
+  uint4 a0, a1;          // 32 activation bytes of this lane's row
+  BFrag<WFMT> b[NB];     // weight fragments of the NB 16-row blocks
+  float s[NB];           // their group scales (INT4 only)
+};
+
+// Output columns of a wave unit u: EPI_SILU_MUL takes gate rows 16u.. and the
+// matching up rows N/2 + 16u..; otherwise 16 NB consecutive rows 16 NB u..
+template <int EPI, int NB = 2>
+__device__ __forceinline__ void unit_columns(int N, int u, int (&col)[NB]) {
+  if constexpr (EPI == MOEQ_EPI_SILU_MUL && NB == 2) {
+    col[0] = 16 * u;
+    col[1] = (N >> 1) + 16 * u;
+  } else {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) col[j] = 16 * (NB * u + j);
+  }
+}
+
+// Where a wave sweep reads its activation rows: global memory (row r of the
+// tile at a_q + (row0 + r) K) or LDS (row r at a_q + r * a_stride, a_q an LDS
+// address).
+enum ASource { kAGlobal = 0, kALds = 1 };
+
+// One K sweep of a wave unit over the 16-row block rb of a tile (rows row0 ..
+// row0 + rows - 1): acc[j] receives the fp32 sums (group scales applied,
+// activation scale not) of the lane's rows 16 rb + 4 kb + v against weight
+// column block j.  Only lanes of real rows load activations (the others keep
+// zeros): MFMA rows are independent and rows past the tile are never stored.
+// With kSplit the first kDepth groups' weights are issued, then before_a()
+// runs (e.g. producing the activations), then their activations; otherwise
+// each group's activations and weights are issued together.
+template <int WFMT, int NB, int GS, bool kSplit, int ASRC = kAGlobal, typename HookF>
+__device__ __forceinline__ void wave_sweep(v4f (&acc)[NB], const uint8_t* a_q, int K, int row0,
+                                           int rows, int rb, const uint8_t* const (&wrow)[NB],
+                                           const float* const (&srow)[NB], int ln, int kb,
+                                           HookF&& before_a, int a_stride = 0) {
+  const int G = K >> 7;
+  const bool a_ok = 16 * rb + ln < rows;
+  const int a_row = a_ok ? 16 * rb + ln : 0;
+  const uint8_t* a_src = (ASRC == kALds) ? a_q + a_row * a_stride + kb * 32
+                                         : a_q + int64_t(row0 + a_row) * K + kb * 32;
+  constexpr int kDepth = Depth<WFMT>::value;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  WaveStage<WFMT, NB> st[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    st[d].a0 = make_uint4(0, 0, 0, 0);
+    st[d].a1 = st[d].a0;
+  }
+  GroupScales<WFMT, GS, NB> sc;
+  sc.init(srow, kb);
+
+  auto issue_a = [&](int slot, int g) {
+    if (a_ok) {
+      const uint4* ap = reinterpret_cast<const uint4*>(a_src + g * 128);
+      st[slot].a0 = ap[0];
+      st[slot].a1 = ap[1];
+    }
+  };
+  auto issue_b = [&](int slot, int g) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      st[slot].b[j].load(wrow[j], g, kb);
+      st[slot].s[j] = sc.load(j, g);
+    }
+  };
+  auto issue = [&](int slot, int g) {
+    issue_a(slot, g);
+    issue_b(slot, g);
+  };
+  auto consume = [&](int slot, int g, bool refill) {
+    const WaveStage<WFMT, NB>& s = st[slot];
+    const v8i aop = (WFMT == kW4G128) ? shuffle_a(s.a0, s.a1) : as_v8i(s.a0, s.a1);
+    v8i b[NB];
+    float sg[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      b[j] = s.b[j].operand();
+      sg[j] = sc.get(j, g, ln, s.s[j]);
+    }
+    // refill this ring slot only after the last read of its old contents
+    __builtin_amdgcn_sched_barrier(0);
+    if (refill) issue(slot, g + kDepth);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) accumulate<WFMT>(acc[j], aop, b[j], sg[j]);
+    // Pin this group's arithmetic before the next group's: without it the
+    // instruction selector defers the scale FMAs to the end of the unrolled
+    // sweep and keeps every group's MFMA result live.
+#pragma unroll
+    for (int j = 0; j < NB; ++j) pin(acc[j]);
+  };
+  if constexpr (kSplit) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+      if (d < G) issue_b(d, d);
+    before_a();
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+      if (d < G) issue_a(d, d);
+    pipeline<kDepth, GS, false>(G, issue, consume);
+  } else {
+    pipeline<kDepth, GS, true>(G, issue, consume);
+  }
+}
+
+}  // namespace
+
+}  // namespace moeq

@@ -14,6 +14,10 @@ constexpr int kPlanHeader = 16;
 enum PlanWord { kPlanR = 0, kPlanE = 1, kPlanActive = 2, kPlanTiles = 3, kPlanT = 4, kPlanK = 5,
                 kPlanDropped = 6 };
 
+// Largest R for which the expert MLP's down GEMM quantizes h itself (every tile
+// then fits one 64-row MFMA tile).
+constexpr int kMlpMaxRows = MOEQ_TILE_M;
+
 struct PlanView {
   int32_t* base;
   int32_t* offsets;      // [E+1]
@@ -84,6 +88,14 @@ hipError_t launch_front(const float* logits, const float* bias, int T, int E, in
                         int renormalize, const void* x, int x_dtype, int H, int32_t* ids, float* w,
                         uint8_t* x_q, float* x_s, uint8_t* xp_q, float* xp_s, void* plan,
                         hipStream_t stream);
+
+// gate/up GEMM + SiLU, FP8 quantization of h and down GEMM: two launches for
+// R <= kMlpMaxRows (the down GEMM quantizes h), three otherwise.
+hipError_t launch_expert_mlp(int wfmt, const uint8_t* xp_q, const float* xp_s, const void* plan,
+                             int E,
+                             int R, const uint8_t* w13, const float* s13, const uint8_t* w2,
+                             const float* s2, int H, int I, uint16_t* h, uint8_t* h_q, float* h_s,
+                             uint16_t* o, hipStream_t stream);
 
 hipError_t launch_shared_gemm_bf16(const uint16_t* a, const uint16_t* w, int M, int N, int K,
                                    int epilogue, uint16_t* out, hipStream_t stream);

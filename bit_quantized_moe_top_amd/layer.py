@@ -1,7 +1,9 @@
 """One quantized MoE expert layer as a fixed sequence of libmoeq calls.
 
-    route + quantize x + permute (one call) -> gate/up GEMM (+SiLU)
-          -> quantize h -> down GEMM -> combine (+ shared experts)
+    route + quantize x + permute (one call)
+      -> expert MLP: gate/up GEMM (+SiLU) -> quantize h -> down GEMM (one call;
+         a single launch for decode-sized batches)
+      -> combine (+ shared experts)
 
 Only orchestration lives here: buffers are torch allocations, reused across
 calls with the same token count, and every step is a C-ABI call into libmoeq.
@@ -12,9 +14,10 @@ from typing import Optional
 
 import torch
 
-from . import (EPI_NONE, EPI_SILU_MUL, moe_combine, moe_grouped_gemm_fp8row,
-               moe_grouped_gemm_w4a8, moe_plan_size, moe_route_quant_permute,
-               moe_shared_gemm_bf16, pack_int4_g128, quant_fp8_per_token)
+from . import (EPI_NONE, EPI_SILU_MUL, moe_combine, moe_expert_mlp_fp8row, moe_expert_mlp_w4a8,
+               moe_grouped_gemm_fp8row, moe_grouped_gemm_w4a8, moe_plan_size,
+               moe_route_quant_permute, moe_shared_gemm_bf16, pack_int4_g128,
+               quant_fp8_per_token)
 
 
 class MoELayer:
@@ -81,12 +84,16 @@ class MoELayer:
 
     # ---------------------------------------------------------------- forward
     def forward(self, x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor] = None,
-                return_all: bool = False, events: Optional[list] = None):
+                return_all: bool = False, events: Optional[list] = None,
+                split_mlp: bool = False):
         """y = layer(x).  With `events` (a list), each call is bracketed by a pair of
-        timing events on the current stream, appended as (name, start, end)."""
+        timing events on the current stream, appended as (name, start, end).
+        split_mlp runs the expert MLP as its three separate calls (same results)."""
         T = x.shape[0]
         b = self.buffers(T)
-        gemm = moe_grouped_gemm_w4a8 if self.weight_format == "w4a8" else moe_grouped_gemm_fp8row
+        w4 = self.weight_format == "w4a8"
+        gemm = moe_grouped_gemm_w4a8 if w4 else moe_grouped_gemm_fp8row
+        mlp = moe_expert_mlp_w4a8 if w4 else moe_expert_mlp_fp8row
 
         def step(name, fn, *args, **kw):
             if events is None:
@@ -100,11 +107,15 @@ class MoELayer:
 
         step("route_quant_permute", moe_route_quant_permute, logits, x, self.k, bias,
              self.renormalize, out=b)
-        step("gemm_gate_up", gemm, b["xp_q"], b["xp_s"], b["plan"], self.w13, self.s13,
-             epilogue=EPI_SILU_MUL, out=b["h"])
-        step("quant_h", quant_fp8_per_token, b["h"], q=b["h_q"], scale=b["h_s"])
-        step("gemm_down", gemm, b["h_q"], b["h_s"], b["plan"], self.w2, self.s2,
-             epilogue=EPI_NONE, out=b["o"])
+        if split_mlp:
+            step("gemm_gate_up", gemm, b["xp_q"], b["xp_s"], b["plan"], self.w13, self.s13,
+                 epilogue=EPI_SILU_MUL, out=b["h"])
+            step("quant_h", quant_fp8_per_token, b["h"], q=b["h_q"], scale=b["h_s"])
+            step("gemm_down", gemm, b["h_q"], b["h_s"], b["plan"], self.w2, self.s2,
+                 epilogue=EPI_NONE, out=b["o"])
+        else:
+            step("expert_mlp", mlp, b["xp_q"], b["xp_s"], b["plan"], self.w13, self.s13, self.w2,
+                 self.s2, out=b)
         shared = None
         if self.ws13 is not None:
             xb = x if x.dtype == torch.bfloat16 else x.to(torch.bfloat16)

@@ -78,7 +78,7 @@ const char* moe_status_string(int status);
  * Plan layout (int32 words), written by moe_permute and read by the GEMMs and
  * the combine; callers may read it but must not modify it:
  *   [0] R   [1] E   [2] n_active   [3] n_tiles   [4] T   [5] k
- *   [6] number of ids outside [0, E) that were dropped   [7..15] reserved
+ *   [6] number of ids outside [0, E) that were dropped   [7..15] reserved (0)
  *   offsets     [E+1]      offsets[e] = first sorted position of expert e
  *   sorted_rows [R]        sorted position p -> routed row r = t*k + j
  *   row_pos     [R]        routed row r -> sorted position p (-1 if dropped)
@@ -230,6 +230,43 @@ int moe_grouped_gemm_w4a8(const uint8_t* a_q, const float* a_s, const void* plan
 int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
                             const uint8_t* w_fp8, const float* w_row_scale, int N, int K,
                             int epilogue, void* out, int out_dtype, void* stream);
+
+/*
+ * moe_expert_mlp_w4a8 -- the routed experts' MLP: gate/up GEMM with the
+ * SiLU-gated product, FP8 quantization of h, down GEMM.
+ *
+ * Exactly the three calls
+ *   moe_grouped_gemm_w4a8(xp_q, xp_s, w13, N = 2I, K = H, SILU_MUL) -> h
+ *   quant_fp8_per_token(h)                                          -> h_q, h_s
+ *   moe_grouped_gemm_w4a8(h_q, h_s, w2, N = H, K = I, NONE)          -> o (bf16)
+ * with bit-identical results.  For R <= MOEQ_TILE_M (decode-sized batches) the
+ * down GEMM quantizes h itself -- each of its workgroups quantizes its tile's
+ * rows into LDS while its first weight loads are in flight -- so the call
+ * makes two launches instead of three; larger R makes the three.
+ *
+ *   xp_q [R, H] E4M3, xp_s [R] fp32 -- rows in plan order (moe_permute)
+ *   plan, plan_bytes -- from moe_permute / moe_route_quant_permute with E, R (read only)
+ *   w13 [E, 2I, H/2] packed INT4 (gate rows then up rows), w13_scales [E, 2I, H/128]
+ *   w2  [E, H, I/2] packed INT4, w2_scales [E, H, I/128]
+ *   h [R, I] bf16, h_q [R, I] E4M3, h_s [R] fp32, o [R, H] bf16 (outputs)
+ * Limits: H % 128 == 0, I % 128 == 0, 1 <= E <= MOEQ_MAX_EXPERTS; xp_q, h_q,
+ * the weights and their scales 16-byte aligned.
+ */
+int moe_expert_mlp_w4a8(const uint8_t* xp_q, const float* xp_s, const void* plan, size_t plan_bytes,
+                        int E, int R, const uint8_t* w13, const float* w13_scales,
+                        const uint8_t* w2, const float* w2_scales, int H, int I, uint16_t* h,
+                        uint8_t* h_q, float* h_s, uint16_t* o, void* stream);
+
+/*
+ * moe_expert_mlp_fp8row -- moe_expert_mlp_w4a8 with row-scaled FP8 expert
+ * weights (the moe_grouped_gemm_fp8row arithmetic):
+ *   w13 [E, 2I, H] E4M3, w13_scales [E, 2I] fp32; w2 [E, H, I] E4M3, w2_scales [E, H] fp32.
+ */
+int moe_expert_mlp_fp8row(const uint8_t* xp_q, const float* xp_s, const void* plan,
+                          size_t plan_bytes,
+                          int E, int R, const uint8_t* w13, const float* w13_scales,
+                          const uint8_t* w2, const float* w2_scales, int H, int I, uint16_t* h,
+                          uint8_t* h_q, float* h_s, uint16_t* o, void* stream);
 
 /*
  * moe_combine -- weighted sum of each token's expert outputs.

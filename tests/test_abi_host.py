@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     assert set(names) == set(mq.EXPORTED_SYMBOLS)
 
 
@@ -95,6 +95,17 @@ def test_argument_errors_are_reported_without_a_gpu():
         assert fn(FAKE, FAKE, FAKE, 8, 32, FAKE, FAKE, 256, 256, 5, FAKE, 1, N) == INVALID
         assert fn(N, FAKE, FAKE, 8, 32, FAKE, FAKE, 256, 256, 0, FAKE, 1, N) == INVALID
         assert fn(N, N, N, 8, 0, N, N, 256, 256, 0, N, 1, N) == OK
+    # fused expert MLP
+    for fn in (L.moe_expert_mlp_w4a8, L.moe_expert_mlp_fp8row):
+        ok = (FAKE, FAKE, FAKE, big, 8, 24, FAKE, FAKE, FAKE, FAKE, 4096, 2048, FAKE, FAKE, FAKE,
+              FAKE, N)
+        assert fn(*ok[:10], 4000, *ok[11:]) == UNSUPPORTED                  # H % 128
+        assert fn(*ok[:11], 2000, *ok[12:]) == UNSUPPORTED                  # I % 128
+        assert fn(*ok[:4], 2000, *ok[5:]) == UNSUPPORTED                    # E > 1024
+        assert fn(*ok[:12], N, *ok[13:]) == INVALID                         # h null
+        assert fn(*ok[:3], 64, *ok[4:]) == WORKSPACE                        # plan too small
+        assert fn(ctypes.c_void_p(4100), *ok[1:]) == INVALID                # xp_q misaligned
+        assert fn(N, N, N, 0, 8, 0, N, N, N, N, 4096, 2048, N, N, N, N, N) == OK   # R = 0
     # combine / shared
     assert L.moe_combine(FAKE, FAKE, FAKE, N, 4, 2, 12, FAKE, N) == UNSUPPORTED
     assert L.moe_combine(FAKE, N, FAKE, N, 4, 2, 16, FAKE, N) == INVALID
@@ -107,6 +118,8 @@ def test_valid_call_without_gpu_reports_device_error():
     L = mq.lib
     assert L.moe_route_topk(FAKE, None, 4, 8, 2, 1, FAKE, FAKE, None) == DEVICE
     assert L.moe_combine(FAKE, FAKE, FAKE, None, 4, 2, 16, FAKE, None) == DEVICE
+    assert L.moe_expert_mlp_w4a8(FAKE, FAKE, FAKE, 1 << 20, 8, 24, FAKE, FAKE, FAKE, FAKE, 256,
+                                 128, FAKE, FAKE, FAKE, FAKE, None) == DEVICE
 
 
 def test_python_binding_raises_on_bad_input():
