@@ -46,25 +46,46 @@ gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
 }
 
 // ------------------------------------------------------------- tile kernel
-template <int WFMT>
-struct TileStage {
-  uint4 a0, a1;          // this thread's 32-byte share of the group's activation slice
-  BFrag<WFMT> b[2];
-  float s[2];
+// CB column blocks (16 weight rows each) per wave: a workgroup covers 64 CB
+// weight rows.  CB = 4 halves the activation staging and the LDS reads per
+// MFMA against CB = 2, at two waves per SIMD instead of three; the launcher
+// takes it for INT4 weights with a fully unrolled K sweep (the looped form does
+// not fit the register file) when N is a multiple of 256.
+template <int WFMT, int GS, int CB_>
+struct TileShape {
+  static constexpr int CB = CB_;
+  static_assert(CB == 2 || (CB == 4 && WFMT == kW4G128 && GS > 0 && GS % 16 == 0), "tile shape");
+  // (the looped sweep, GS == 0, keeps a shallower ring to stay within registers)
+  static constexpr int kDepth = (CB == 4 || GS == 0) ? 2 : TileDepth<WFMT>::value;
+  static constexpr int kWavesPerSimd = (CB == 4) ? 2 : 3;
+  // group scales staged in LDS ([g][wave][ln][j], 4 CB bytes per lane and
+  // group) instead of registers
+  static constexpr bool kLdsScales = (CB == 4);
 };
 
-template <int WFMT, int EPI, int GS>
-__global__ void __launch_bounds__(kThreads, 3)   // >= 3 waves per SIMD
+template <int WFMT, int CB>
+struct TileStage {
+  uint4 a0, a1;          // this lane's two 16-byte pieces of the group's activation slice
+  BFrag<WFMT> b[CB];
+  float s[CB];
+};
+
+template <int WFMT, int EPI, int GS, int CB_>
+__global__ void __launch_bounds__(kThreads, (CB_ == 4) ? 2 : 3)   // TileShape::kWavesPerSimd
 gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
                  const int32_t* __restrict__ plan, int E, int R, const uint8_t* __restrict__ w,
                  const float* __restrict__ w_scale, int N, int K, void* __restrict__ out,
                  int out_f32) {
+  using Shape = TileShape<WFMT, GS, CB_>;
+  constexpr int CB = Shape::CB;
+  constexpr int BN = 64 * CB;                           // weight rows per workgroup
   __shared__ uint32_t As[2][MOEQ_TILE_M * kRowDw];
+  __shared__ float Ss[Shape::kLdsScales ? GS * 4 * 16 * CB : 1];
 
   // Consecutive block ids go to XCDs round-robin; within each run of
   // 8 * n_ntiles ids, XCD x takes the n_ntiles N-tiles of one row tile, so every
   // XCD gets an equal share of the (device-side, unknown here) real tiles.
-  const int n_ntiles = N / kBN;
+  const int n_ntiles = N / BN;
   const int total = n_ntiles * plan_max_tiles(E, R);
   const int run = kXcds * n_ntiles;
   const int bid = blockIdx.x;
@@ -80,53 +101,75 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
   const int ln = lane & 15, kb = lane >> 4;
   const int G = K >> 7;
 
-  int col[2];
-  if (EPI == MOEQ_EPI_SILU_MUL) {
-    col[0] = nt * 64 + 16 * wave;
-    col[1] = (N >> 1) + nt * 64 + 16 * wave;
-  } else {
-    col[0] = nt * kBN + 16 * wave;
-    col[1] = nt * kBN + 16 * (wave + 4);
+  // EPI_SILU_MUL: the workgroup takes BN/2 gate rows and the matching up rows;
+  // wave w its 8 CB consecutive gate rows (blocks j < CB/2) and their up rows.
+  // Otherwise wave w takes blocks w, w + 4, ... of the workgroup's BN rows.
+  int col[CB];
+#pragma unroll
+  for (int j = 0; j < CB; ++j) {
+    if (EPI == MOEQ_EPI_SILU_MUL)
+      col[j] = (j < CB / 2 ? 0 : (N >> 1)) + nt * (BN / 2) + wave * (8 * CB) + 16 * (j % (CB / 2));
+    else
+      col[j] = nt * BN + 16 * (wave + 4 * j);
   }
-  const uint8_t* wrow[2];
-  const float* srow[2];
-  weight_rows<WFMT>(w, w_scale, ti.e, N, K, col, ln, wrow, srow);
+  const uint8_t* wrow[CB];
+  const float* srow[CB];
+  weight_rows<WFMT, CB>(w, w_scale, ti.e, N, K, col, ln, wrow, srow);
 
-  // A staging: thread -> (row tid / 4, 32-byte chunk tid % 4) of the 64 x 128 B slice;
-  // rows past the tile read the tile's first row (MFMA rows are independent and
-  // those rows are never stored).  The slice of group g is loaded into registers
-  // in group g's ring slot, ahead of its weights in issue order, and written to
-  // LDS one group before its use: waiting for it never waits for the weight
-  // loads of later groups.
-  const int st_row = tid >> 2, st_chunk = tid & 3;
-  const bool st_valid = st_row < ti.rows;
-  const uint8_t* a_src = a_q + int64_t(ti.row0 + (st_valid ? st_row : 0)) * K + st_chunk * 32;
+  // A staging: wave w stages rows 16 w .. 16 w + 15 of the 64 x 128 B slice;
+  // load j of lane l takes segment l % 8 (16 bytes) of row 16 w + 8 j + l / 8,
+  // so each load reads 8 whole 128-byte lines.  Waves past the tile's last
+  // 16-row block stage nothing; rows past the tile inside it read the tile's
+  // first row (MFMA rows are independent and those rows are never stored).
+  // The slice of group g is loaded into registers in group g's ring slot,
+  // ahead of its weights in issue order, and written to LDS one group before
+  // its use: waiting for it never waits for the weight loads of later groups.
+  const bool st_on = wave < nrb;                        // wave-uniform
+  const int st_seg = lane & 7;
+  const int st_r0 = 16 * wave + (lane >> 3), st_r1 = st_r0 + 8;
+  const uint8_t* a_src0 = a_q + int64_t(ti.row0 + (st_r0 < ti.rows ? st_r0 : 0)) * K + st_seg * 16;
+  const uint8_t* a_src1 = a_q + int64_t(ti.row0 + (st_r1 < ti.rows ? st_r1 : 0)) * K + st_seg * 16;
   auto store_a = [&](int buf, const uint4& x0, const uint4& x1) {
-    const v8i o = (WFMT == kW4G128) ? shuffle_a(x0, x1) : as_v8i(x0, x1);
-    uint4* dst = reinterpret_cast<uint4*>(&As[buf][st_row * kRowDw + st_chunk * 8]);
-    dst[0] = make_uint4(uint32_t(o[0]), uint32_t(o[1]), uint32_t(o[2]), uint32_t(o[3]));
-    dst[1] = make_uint4(uint32_t(o[4]), uint32_t(o[5]), uint32_t(o[6]), uint32_t(o[7]));
+    if (!st_on) return;
+    *reinterpret_cast<uint4*>(&As[buf][st_r0 * kRowDw + st_seg * 4]) =
+        (WFMT == kW4G128) ? shuffle_a16(x0) : x0;
+    *reinterpret_cast<uint4*>(&As[buf][st_r1 * kRowDw + st_seg * 4]) =
+        (WFMT == kW4G128) ? shuffle_a16(x1) : x1;
   };
 
-  v4f acc[4][2];
+  v4f acc[4][CB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc[i][0] = v4f{0.f, 0.f, 0.f, 0.f};
-    acc[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int kDepth = TileDepth<WFMT>::value;
-  TileStage<WFMT> st[kDepth];
-  GroupScales<WFMT, GS> sc;
+  constexpr int kDepth = Shape::kDepth;
+  TileStage<WFMT, CB> st[kDepth];
+  GroupScales<WFMT, Shape::kLdsScales ? 0 : GS, CB> sc;
   sc.init(srow, kb);
-  auto issue = [&](int slot, int g) {
-    const uint4* ap = reinterpret_cast<const uint4*>(a_src + g * 128);
-    st[slot].a0 = ap[0];
-    st[slot].a1 = ap[1];
+  if constexpr (Shape::kLdsScales) {
+    // lane (ln, kb) holds groups [kb G/4, (kb+1) G/4) of its rows; made visible
+    // by the barrier before the first group
+    constexpr int kPer = GS / 4;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < CB; ++j)
+#pragma unroll
+      for (int i = 0; i < kPer; i += 4) {
+        const float4 f = *reinterpret_cast<const float4*>(srow[j] + kb * kPer + i);
+        const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) Ss[(((kb * kPer + i + t) * 4 + wave) * 16 + ln) * CB + j] = fv[t];
+      }
+  }
+  auto issue = [&](int slot, int g) {
+    if (st_on) {
+      st[slot].a0 = *reinterpret_cast<const uint4*>(a_src0 + g * 128);
+      st[slot].a1 = *reinterpret_cast<const uint4*>(a_src1 + g * 128);
+    }
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
       st[slot].b[j].load(wrow[j], g, kb);
-      st[slot].s[j] = sc.load(j, g);
+      if constexpr (!Shape::kLdsScales) st[slot].s[j] = sc.load(j, g);
     }
   };
   auto consume = [&](int slot, int g, bool refill) {
@@ -139,9 +182,17 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
     // the next group's slice (its slot is not the one refilled below)
     const int next = (slot + 1 == kDepth) ? 0 : slot + 1;
     const uint4 x0 = st[next].a0, x1 = st[next].a1;
-    const v8i b0 = st[slot].b[0].operand();
-    const v8i b1 = st[slot].b[1].operand();
-    const float s0 = sc.get(0, g, ln, st[slot].s[0]), s1 = sc.get(1, g, ln, st[slot].s[1]);
+    v8i bop[CB];
+    float sg[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) bop[j] = st[slot].b[j].operand();
+    if constexpr (Shape::kLdsScales) {
+      const float4 f = *reinterpret_cast<const float4*>(&Ss[((g * 4 + wave) * 16 + ln) * CB]);
+      sg[0] = f.x; sg[1] = f.y; sg[2] = f.z; sg[3] = f.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < CB; ++j) sg[j] = sc.get(j, g, ln, st[slot].s[j]);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (refill) issue(slot, g + kDepth);
 #pragma unroll
@@ -149,8 +200,8 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
       if (i < nrb) {
         const uint4* ap = reinterpret_cast<const uint4*>(&As[buf][(16 * i + ln) * kRowDw + kb * 8]);
         const v8i aop = as_v8i(ap[0], ap[1]);
-        accumulate<WFMT>(acc[i][0], aop, b0, s0);
-        accumulate<WFMT>(acc[i][1], aop, b1, s1);
+#pragma unroll
+        for (int j = 0; j < CB; ++j) accumulate<WFMT>(acc[i][j], aop, bop[j], sg[j]);
       }
     }
     if (more) store_a(buf ^ 1, x0, x1);
@@ -161,9 +212,11 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i < nrb) {
-      const v4f blk[2] = {acc[i][0], acc[i][1]};
-      store_block<WFMT, EPI>(blk, i, ti.row0, ti.rows, [a_s](int p) { return a_s[p]; }, srow,
-                             col, ln, kb, N, out, out_f32);
+      v4f blk[CB];
+#pragma unroll
+      for (int j = 0; j < CB; ++j) blk[j] = acc[i][j];
+      store_block<WFMT, EPI, CB>(blk, i, ti.row0, ti.rows, [a_s](int p) { return a_s[p]; }, srow,
+                                 col, ln, kb, N, out, out_f32);
     }
   }
 }
@@ -182,11 +235,21 @@ hipError_t launch_kernels(const uint8_t* a_q, const float* a_s, const void* plan
                        dim3(kThreads), 0, stream, a_q, a_s, p, E, R, w, w_scale, N, K, out,
                        out_f32);
   } else {
-    const int64_t run = int64_t(kXcds) * (N / kBN);
-    const int64_t total = int64_t(N / kBN) * plan_max_tiles(E, R);
-    const int64_t grid = (total + run - 1) / run * run;
-    hipLaunchKernelGGL((gemm_tile_kernel<WFMT, EPI, GS>), dim3(unsigned(grid)), dim3(kThreads), 0,
-                       stream, a_q, a_s, p, E, R, w, w_scale, N, K, out, out_f32);
+    auto tile = [&](auto cb) {
+      constexpr int CB = decltype(cb)::value;
+      const int64_t run = int64_t(kXcds) * (N / (64 * CB));
+      const int64_t total = int64_t(N / (64 * CB)) * plan_max_tiles(E, R);
+      const int64_t grid = (total + run - 1) / run * run;
+      hipLaunchKernelGGL((gemm_tile_kernel<WFMT, EPI, GS, CB>), dim3(unsigned(grid)),
+                         dim3(kThreads), 0, stream, a_q, a_s, p, E, R, w, w_scale, N, K, out,
+                         out_f32);
+    };
+    if constexpr (WFMT == kW4G128 && GS > 0) {
+      if (N % 256 == 0) tile(std::integral_constant<int, 4>());
+      else tile(std::integral_constant<int, 2>());
+    } else {
+      tile(std::integral_constant<int, 2>());
+    }
   }
   return hipGetLastError();
 }

@@ -40,10 +40,10 @@
 //    no LDS and no barrier in the K loop.  Tiles with more than 16 rows are swept
 //    once per 16-row block.
 //  * tile kernel (prefill): a 256-thread workgroup owns one plan tile (<= 64
-//    rows) x 128 weight rows.  The 64 x 128 B activation slice of each group is
-//    staged once in LDS (double-buffered, one barrier per group) and shared by
-//    the four waves, each of which runs all four 16-row blocks against its own
-//    32 weight rows.  The linear workgroup id is remapped so that each XCD
+//    rows) x 128 or 256 weight rows.  The 64 x 128 B activation slice of each
+//    group is staged once in LDS (double-buffered, one barrier per group) and
+//    shared by the four waves, each of which runs all four 16-row blocks
+//    against its own 32 or 64 weight rows.  The linear workgroup id is remapped so that each XCD
 //    (workgroups are dispatched to the 8 XCDs round-robin) receives a contiguous
 //    run of (tile, N-tile) pairs: the N-tiles of one row tile share that tile's
 //    activations in one L2.
@@ -62,7 +62,6 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kBN = 128;           // weight rows per tile-kernel workgroup
 constexpr int kRowDw = 36;         // LDS row stride in dwords (128 B + 16 B pad)
 constexpr int kXcds = 8;
 // weight groups in flight per wave (an FP8 group carries twice the bytes of an INT4
@@ -121,6 +120,14 @@ __device__ __forceinline__ v8i shuffle_a(const uint4& x0, const uint4& x1) {
     r[2 * i + 1] = int(__builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x07050301u));
   }
   return r;
+}
+
+// the same reorder for one 16-byte piece (two independent 8-byte units)
+__device__ __forceinline__ uint4 shuffle_a16(const uint4& x) {
+  return make_uint4(__builtin_amdgcn_perm(x.y, x.x, 0x06040200u),
+                    __builtin_amdgcn_perm(x.y, x.x, 0x07050301u),
+                    __builtin_amdgcn_perm(x.w, x.z, 0x06040200u),
+                    __builtin_amdgcn_perm(x.w, x.z, 0x07050301u));
 }
 
 __device__ __forceinline__ v8i as_v8i(const uint4& x0, const uint4& x1) {
@@ -210,7 +217,7 @@ __device__ __forceinline__ uint16_t silu_mul_bf16(const v4f (&acc)[2], int v, fl
   return f32_to_bf16(silu_f32(v0) * v1);
 }
 
-// (EPI_SILU_MUL needs NB == 2: block 0 gate rows, block 1 the matching up rows)
+// (EPI_SILU_MUL: blocks j < NB/2 gate rows, block j + NB/2 the matching up rows)
 template <int WFMT, int EPI, int NB = 2, typename RowScaleF>
 __device__ __forceinline__ void store_block(const v4f (&acc)[NB], int rb, int row0, int rows,
                                             RowScaleF&& row_scale, const float* const (&srow)[NB],
@@ -227,6 +234,15 @@ __device__ __forceinline__ void store_block(const v4f (&acc)[NB], int rb, int ro
     if constexpr (EPI == MOEQ_EPI_SILU_MUL && NB == 2) {
       uint16_t* o = static_cast<uint16_t*>(out) + int64_t(p) * (N >> 1);
       o[col[0] + ln] = silu_mul_bf16(acc, v, sa, rs);
+    } else if constexpr (EPI == MOEQ_EPI_SILU_MUL) {
+      // blocks j < NB/2 hold gate rows, block j + NB/2 the matching up rows
+      uint16_t* o = static_cast<uint16_t*>(out) + int64_t(p) * (N >> 1);
+#pragma unroll
+      for (int j = 0; j < NB / 2; ++j) {
+        const float v0 = sa * acc[j][v] * rs[j];
+        const float v1 = sa * acc[j + NB / 2][v] * rs[j + NB / 2];
+        o[col[j] + ln] = f32_to_bf16(silu_f32(v0) * v1);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
