@@ -123,9 +123,11 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 // True where E4M3 rounding of a value within a few ulp of q may differ from
 // that of q: within 8 ulp of a rounding midpoint (the 20 fp32 mantissa bits
 // below E4M3's 3 are near 0x80000) or in E4M3's subnormal range (|q| < 2^-6).
+// (Bitwise operators, not && / ||: the test is evaluated for every value and
+// must not turn into branches.)
 __device__ __forceinline__ bool e4m3_rounding_close(float q) {
   const uint32_t a = f2u(q) & 0x7FFFFFFFu;
-  return (a != 0u && a < 0x3C800000u) || ((a & 0xFFFFFu) - 0x7FFF8u) <= 0x10u;
+  return ((a - 1u) < 0x3C7FFFFFu) | (((a & 0xFFFFFu) - 0x7FFF8u) <= 0x10u);
 }
 
 // 8 codes of x / s packed little-endian: E4M3 (round to nearest even,
@@ -143,7 +145,7 @@ __device__ __forceinline__ uint2 fp8_codes8(const float (&v)[8], float s) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       q[i] = v[i] * rs;
-      exact = exact || e4m3_rounding_close(q[i]);
+      exact = exact | e4m3_rounding_close(q[i]);
     }
   }
   if (exact) {

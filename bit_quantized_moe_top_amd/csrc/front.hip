@@ -23,27 +23,6 @@ namespace {
 
 constexpr int kFrontMaxRows = kFrontSmallT * MOEQ_MAX_TOPK;
 
-// 8 consecutive elements of x held in registers as loaded
-template <typename XT>
-struct XChunk;
-template <>
-struct XChunk<uint16_t> {
-  uint4 raw;
-  __device__ __forceinline__ void load(const uint16_t* p) { raw = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void values(float (&v)[8]) const { bf16x8_to_f32(raw, v); }
-};
-template <>
-struct XChunk<float> {
-  float4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const float4*>(p);
-    b = *reinterpret_cast<const float4*>(p + 4);
-  }
-  __device__ __forceinline__ void values(float (&v)[8]) const {
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-};
 constexpr int kFrontChunksPerThread = 4;    // 8-element chunks of x held per lane
 
 // Waves quantizing each row: the rows share the waves equally; the last wave,
@@ -169,9 +148,13 @@ hipError_t launch_front(const float* logits, const float* bias, int T, int E, in
                         uint8_t* x_q, float* x_s, uint8_t* xp_q, float* xp_s, void* plan,
                         hipStream_t stream) {
   if (T > kFrontSmallT || front_waves_per_row(T, H) == 0) {
+    // routing, then the plan, then x quantized once per token straight into
+    // x_q and its k plan positions (rows of <= 4096 elements)
     hipError_t err;
     if ((err = launch_route_topk(logits, bias, T, E, k, renormalize, ids, w, stream)) != hipSuccess)
       return err;
+    if (row_quant_cpl(H) != 0)
+      return launch_permute_quant(ids, T, k, E, x, x_dtype, H, x_q, x_s, xp_q, xp_s, plan, stream);
     if ((err = launch_quant_fp8(x, x_dtype, T, H, H, x_q, x_s, stream)) != hipSuccess) return err;
     return launch_permute(ids, T, k, E, x_q, x_s, H, xp_q, xp_s, plan, stream);
   }

@@ -136,6 +136,85 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// 8 consecutive elements of x held in registers as loaded (bf16 or fp32)
+template <typename XT>
+struct XChunk;
+template <>
+struct XChunk<uint16_t> {
+  uint4 raw;
+  __device__ __forceinline__ void load(const uint16_t* p) { raw = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void values(float (&v)[8]) const { bf16x8_to_f32(raw, v); }
+};
+template <>
+struct XChunk<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void values(float (&v)[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+// A row of x quantized by one wave with the row held in registers: lane l
+// takes the 8-element chunks l, l + 64, ... (CPL of them; K <= 512 CPL).
+// The codes stay in `codes` for the caller to store wherever they go.
+template <typename XT, int CPL>
+struct RowQuant {
+  XChunk<XT> xc[CPL];
+  uint2 codes[CPL];
+  float scale;
+  __device__ __forceinline__ void run(const XT* row, int K, int lane) {
+    const int chunks = K >> 3;
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+      if (lane + kWave * i < chunks) xc[i].load(row + (lane + kWave * i) * 8);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      if (lane + kWave * i < chunks) {
+        float v[8];
+        xc[i].values(v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      }
+    }
+    scale = fp8_scale(wave_max(amax));
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      if (lane + kWave * i < chunks) {
+        float v[8];
+        xc[i].values(v);
+        codes[i] = fp8_codes8(v, scale);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* q_row, int K, int lane) const {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+      if (lane + kWave * i < (K >> 3))
+        *reinterpret_cast<uint2*>(q_row + (lane + kWave * i) * 8) = codes[i];
+  }
+};
+
+// chunks per lane for a row of K elements held by one wave (0: K too large)
+__host__ __device__ inline int row_quant_cpl(int K) {
+  const int c = (K + 8 * kWave - 1) / (8 * kWave);
+  return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : c <= 8 ? 8 : 0;
+}
+template <typename F>
+__host__ inline hipError_t with_row_quant_cpl(int K, F&& fn) {
+  switch (row_quant_cpl(K)) {
+    case 1: return fn(SlotsTag<1>{});
+    case 2: return fn(SlotsTag<2>{});
+    case 4: return fn(SlotsTag<4>{});
+    case 8: return fn(SlotsTag<8>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // ---------------------------------------------------------- plan building
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / kWave;

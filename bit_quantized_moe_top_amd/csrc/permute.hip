@@ -147,6 +147,36 @@ place_gather_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
   if (threadIdx.x == 0) xp_s[pos] = x_s[t];
 }
 
+// Quantization of x fused with the scatter (moe_route_quant_permute at larger
+// T): one wave per token quantizes its row in registers (RowQuant), writes the
+// codes and scale to x_q / x_s and to the k plan positions of the token's
+// rows.  kPlace: the positions are placed here (chunk base + rank, after
+// chunk_rank_kernel and plan_scan_kernel); otherwise the plan is complete and
+// row_pos is read.
+template <typename XT, int CPL, bool kPlace>
+__global__ void __launch_bounds__(256)
+quant_scatter_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                     int32_t* __restrict__ plan, const XT* __restrict__ x, int H,
+                     uint8_t* __restrict__ x_q, float* __restrict__ x_s,
+                     uint8_t* __restrict__ xp_q, float* __restrict__ xp_s) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;                                   // wave-uniform
+  PlanView pv = plan_view(plan, E, T * k);
+  int pos = -1;
+  if (lane < k) pos = kPlace ? place_row(ids, t * k + lane, E, pv) : pv.row_pos[t * k + lane];
+  RowQuant<XT, CPL> rq;
+  rq.run(x + int64_t(t) * H, H, lane);
+  rq.store(x_q + int64_t(t) * H, H, lane);
+  if (lane == 0) x_s[t] = rq.scale;
+  for (int j = 0; j < k; ++j) {
+    const int p = readlane(pos, j);
+    if (p < 0) continue;
+    rq.store(xp_q + int64_t(p) * H, H, lane);
+    if (lane == 0) xp_s[p] = rq.scale;
+  }
+}
+
 hipError_t set_lds(const void* fn, size_t bytes) {
   if (bytes <= 64 * 1024) return hipSuccess;
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
@@ -185,6 +215,53 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, const uint8_t
     hipLaunchKernelGGL(place_gather_kernel, dim3(R), dim3(256), 0, stream, ids, T, k, E, p, x_q, x_s,
                        H, xp_q, xp_s);
   return hipGetLastError();
+}
+
+hipError_t launch_permute_quant(const int32_t* ids, int T, int k, int E, const void* x,
+                                int x_dtype, int H, uint8_t* x_q, float* x_s, uint8_t* xp_q,
+                                float* xp_s, void* plan, hipStream_t stream) {
+  if (row_quant_cpl(H) == 0) return hipErrorInvalidValue;
+  const int R = T * k;
+  int32_t* p = static_cast<int32_t*>(plan);
+  hipError_t err;
+  const bool place = R > kPlanChunk;
+  if (!place) {
+    const size_t lds = size_t(E) * (1 + kPlanWaves) * sizeof(int);
+    if ((err = set_lds(reinterpret_cast<const void*>(&plan_kernel), lds)) != hipSuccess) return err;
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), lds, stream, ids, T, k, E, p);
+  } else {
+    const size_t lds_rank = size_t(E) * kPlanWaves * sizeof(int);
+    if ((err = set_lds(reinterpret_cast<const void*>(&chunk_rank_kernel), lds_rank)) != hipSuccess)
+      return err;
+    hipLaunchKernelGGL(chunk_rank_kernel, dim3(plan_chunks(R)), dim3(kPlanThreads), lds_rank,
+                       stream, ids, T, k, E, p);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kPlanThreads), size_t(E) * sizeof(int),
+                       stream, T, k, E, p);
+  }
+  if ((err = hipGetLastError()) != hipSuccess || T == 0) return err;
+  const dim3 grid(unsigned((T + 3) / 4));
+  return with_row_quant_cpl(H, [&](auto cpl) {
+    constexpr int CPL = decltype(cpl)::value;
+    if (x_dtype == MOEQ_BF16) {
+      const uint16_t* xb = static_cast<const uint16_t*>(x);
+      if (place)
+        hipLaunchKernelGGL((quant_scatter_kernel<uint16_t, CPL, true>), grid, dim3(256), 0, stream,
+                           ids, T, k, E, p, xb, H, x_q, x_s, xp_q, xp_s);
+      else
+        hipLaunchKernelGGL((quant_scatter_kernel<uint16_t, CPL, false>), grid, dim3(256), 0, stream,
+                           ids, T, k, E, p, xb, H, x_q, x_s, xp_q, xp_s);
+    } else {
+      const float* xf = static_cast<const float*>(x);
+      if (place)
+        hipLaunchKernelGGL((quant_scatter_kernel<float, CPL, true>), grid, dim3(256), 0, stream,
+                           ids, T, k, E, p, xf, H, x_q, x_s, xp_q, xp_s);
+      else
+        hipLaunchKernelGGL((quant_scatter_kernel<float, CPL, false>), grid, dim3(256), 0, stream,
+                           ids, T, k, E, p, xf, H, x_q, x_s, xp_q, xp_s);
+    }
+    return hipGetLastError();
+  });
 }
 
 }  // namespace moeq
