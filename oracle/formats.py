@@ -5,6 +5,10 @@
   card ("Inkling 2 Small FP8 for AMD MI300X", "Precision and files") uses the
   FNUZ flavour with max 240 on MI300X; the flavour native to gfx950 is OCP, so
   the divisor used throughout is 448 (reading recorded in the design notes).
+* E4M3FNUZ (the MI300X flavour of the row-FP8 card): 1 sign, 4 exponent
+  (bias 8), 3 mantissa bits; no infinities and no negative zero; 0x80 is the
+  only NaN; largest finite magnitude 240 (0x7F).  Read only, to convert such
+  checkpoints to OCP E4M3.
 * bfloat16: the top 16 bits of an IEEE binary32.
 * INT4: signed codes in [-8, 7] stored as nibble = code + 8, eight consecutive
   codes per little-endian 32-bit word with the first code in the least
@@ -74,6 +78,22 @@ def e4m3_encode(v, block: int = 1 << 19) -> np.ndarray:
     for i in range(0, flat.size, block):
         out[i:i + block] = _e4m3_encode_block(flat[i:i + block])
     return out.reshape(v.shape)
+
+
+def e4m3fnuz_decode(codes) -> np.ndarray:
+    """Value of each E4M3FNUZ byte, as float64 (NaN for 0x80).
+
+    normal (exponent field e >= 1): (-1)^s * 2^(e-8) * (1 + m/8)
+    subnormal (e == 0):             (-1)^s * 2^(-7) * (m/8)
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -7), np.ldexp(1.0 + m / 8.0, e - 8))
+    val = np.where(s == 1, -mag, mag)
+    val = np.where(c == 0x80, np.nan, val)
+    return val.astype(np.float64)
 
 
 def fp32(v) -> np.ndarray:

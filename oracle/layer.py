@@ -22,6 +22,8 @@ Sources (page title, section):
   * "Inkling 2 Small FP8 for AMD MI300X", "Precision and files": expert weights
     FP8 with one fp32 scale per output channel, scale = max|row| / fmax, and
     dynamic per-token FP8 activations; scale tensor [n_experts, out_channels].
+    That card stores E4M3FNUZ with fmax = 240 (MI300X); requant_fnuz_rows
+    converts such rows to the OCP E4M3 / 448 rows used here.
 
 Readings where the pages are silent (each listed in the design notes):
   routing is softmax over the k selected logits (softmax-then-top-k with
@@ -36,7 +38,7 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import (E4M3_MAX, GROUP, bf16_round, e4m3_decode, e4m3_encode,
-                      fp32, pack_int4, unpack_int4)
+                      e4m3fnuz_decode, fp32, pack_int4, unpack_int4)
 
 # ----------------------------------------------------------------- a1: routing
 
@@ -152,6 +154,25 @@ def quant_fp8_per_row_weights(w):
     Identical arithmetic to the per-token activation quantization applied to
     the rows of W [rows, K]: s_row = fl32(max|row| / 448), wq = E4M3(fl32(W / s)).
     """
+    return quant_fp8_per_token(w)
+
+
+
+def requant_fnuz_rows(w_fnuz, s_fnuz):
+    """Row-scaled E4M3FNUZ weights -> row-scaled OCP E4M3 weights.
+
+    The MI300X card's rows hold E4M3FNUZ codes b with one fp32 scale s per
+    output channel (s = max|row| / 240).  Each element's value is formed once in
+    fp32, w = fl32(s * fnuz(b)), and the rows of w are quantized exactly as
+    quant_fp8_per_row_weights: s' = fl32(max|w| / 448), codes = E4M3(fl32(w / s')).
+    The FNUZ NaN code 0x80 is read as 0 (weights hold no NaN).
+    Returns codes uint8 [rows, K] and scales float32 [rows].
+    """
+    b = np.asarray(w_fnuz, dtype=np.uint8)
+    s = np.asarray(s_fnuz, dtype=np.float32)
+    v = e4m3fnuz_decode(b)
+    v = np.where(np.isnan(v), 0.0, v).astype(np.float32)      # exact: 4 significant bits
+    w = (s[:, None] * v).astype(np.float32)                   # one fp32 rounding
     return quant_fp8_per_token(w)
 
 # -------------------------------------------------------------- a3: permute

@@ -37,6 +37,32 @@ def test_e4m3_decode_matches_torch_for_all_codes():
     assert same.all()
 
 
+def test_e4m3fnuz_decode_fixed_points():
+    # E4M3FNUZ: bias 8, max 240 at S.1111.111, min normal 2^-7, min subnormal
+    # 2^-10, 0x80 (the negative-zero pattern) is the only NaN.
+    cases = {0x00: 0.0, 0x01: 2.0 ** -10, 0x07: 7 * 2.0 ** -10, 0x08: 2.0 ** -7,
+             0x40: 1.0, 0x41: 1.125, 0x48: 2.0, 0x7F: 240.0, 0xFF: -240.0, 0xC0: -1.0,
+             0x7E: 224.0}
+    for c, v in cases.items():
+        assert F.e4m3fnuz_decode([c])[0] == v, hex(c)
+    assert np.isnan(F.e4m3fnuz_decode([0x80])[0])
+
+
+def test_e4m3fnuz_decode_matches_torch_for_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = F.e4m3fnuz_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fnuz).to(torch.float64).numpy()
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+
+
+def test_e4m3fnuz_is_half_of_ocp_on_shared_finite_codes():
+    # the two flavours differ only in the exponent bias (8 vs 7) and the special
+    # codes: a byte that is finite in both decodes to half the OCP value
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)], dtype=np.uint8)
+    assert np.array_equal(F.e4m3fnuz_decode(codes) * 2.0, F.e4m3_decode(codes))
+
+
 def test_e4m3_roundtrip_every_finite_code():
     codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
     assert len(codes) == 254

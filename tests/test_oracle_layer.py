@@ -257,6 +257,49 @@ def test_fp8row_equals_dequantize_then_matmul_and_row_max():
 
 
 # ----------------------------------------------------------- SwiGLU, combine ----
+def test_requant_fnuz_hand_example():
+    # row [0x7F, 0x01, 0x80, 0xC8] with s = 0.5: FNUZ values 240, 2^-10, NaN
+    # (read as 0), -2 -> w = [120, 2^-11, 0, -1]; s' = 120/448; w/s' = 448,
+    # 0.0018 (nearest E4M3: 2^-9 = 0x01), 0, -3.733 (nearest: -3.75 = 0xC7)
+    q, s = L.requant_fnuz_rows(np.array([[0x7F, 0x01, 0x80, 0xC8]], dtype=np.uint8),
+                               np.array([0.5], dtype=np.float32))
+    assert q.tolist() == [[0x7E, 0x01, 0x00, 0xC7]]
+    assert s[0] == np.float32(np.float32(120.0) / np.float32(448.0))
+
+
+def test_requant_fnuz_matches_library_composition():
+    # the same steps with library routines: torch's FNUZ decode, numpy float32
+    # products and quotients, torch's OCP cast (RNE; magnitudes stay <= 448)
+    rng = np.random.default_rng(11)
+    b = rng.integers(0, 256, size=(24, 256), dtype=np.uint8)
+    b[b == 0x80] = 0x00
+    b[:, 7] = 0x7F                                         # every row has a max element
+    s = (rng.random(24) * 1e-2 + 1e-4).astype(np.float32)
+    q, s2 = L.requant_fnuz_rows(b, s)
+    v = torch.from_numpy(b).view(torch.float8_e4m3fnuz).to(torch.float32).numpy()
+    w = s[:, None] * v
+    s_ref = (np.abs(w).max(axis=1) / np.float32(448.0)).astype(np.float32)
+    ratio = (w / s_ref[:, None]).astype(np.float32)
+    q_ref = torch.from_numpy(ratio).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(s2, s_ref)
+    assert np.array_equal(q, q_ref)
+    assert np.all(q[:, 7] == 0x7E)                         # the row max encodes to 448
+
+
+def test_requant_fnuz_error_bound():
+    # each requantized element is within half an E4M3 step of the FNUZ value
+    rng = np.random.default_rng(12)
+    b = rng.integers(0, 256, size=(16, 512), dtype=np.uint8)
+    b[b == 0x80] = 0x00
+    s = np.full(16, 3e-3, dtype=np.float32)
+    q, s2 = L.requant_fnuz_rows(b, s)
+    w = s[:, None].astype(np.float64) * F.e4m3fnuz_decode(b)
+    back = F.e4m3_decode(q) * s2[:, None].astype(np.float64)
+    # E4M3 relative step 2^-3 for normals; absolute 2^-9 s' below 2^-6 s'
+    bound = np.maximum(np.abs(w) * 2.0 ** -4, 2.0 ** -10 * s2[:, None]) * (1 + 1e-6)
+    assert np.all(np.abs(back - w) <= bound)
+
+
 def test_silu_closed_forms():
     z = np.linspace(-30, 30, 1001)
     np.testing.assert_allclose(L.silu(z), z * scipy.special.expit(z), rtol=1e-14, atol=1e-300)
