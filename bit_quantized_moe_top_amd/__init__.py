@@ -20,7 +20,7 @@ __all__ = [
     "LIB_PATH", "lib", "MOEQ_F32", "MOEQ_BF16", "EPI_NONE", "EPI_SILU_MUL", "TILE_M",
     "MAX_EXPERTS", "MAX_TOPK", "MoeqError", "moe_abi_version", "moe_status_string",
     "moe_plan_size", "moe_route_topk", "quant_fp8_per_token", "moe_permute",
-    "moe_route_quant_permute", "pack_int4_g128",
+    "moe_route_quant_permute", "pack_int4_g128", "moe_requant_fp8_fnuz",
     "moe_grouped_gemm_w4a8", "moe_grouped_gemm_fp8row", "moe_combine", "moe_shared_gemm_bf16",
     "plan_fields", "EXPORTED_SYMBOLS",
 ]
@@ -49,6 +49,7 @@ _SIGNATURES = {
     "moe_route_quant_permute": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P,
                                      _P, _SZ, _P]),
     "pack_int4_g128": (_I, [_P, _I64, _I, _P, _P, _P]),
+    "moe_requant_fp8_fnuz": (_I, [_P, _P, _I64, _I, _P, _P, _P]),
     "moe_grouped_gemm_w4a8": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_grouped_gemm_fp8row": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_expert_mlp_w4a8": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P,
@@ -238,6 +239,26 @@ def pack_int4_g128(w: torch.Tensor, packed: Optional[torch.Tensor] = None,
     _check("pack_int4_g128", lib.pack_int4_g128(_ptr(w), rows, K, _ptr(packed), _ptr(scales),
                                                 _stream(w.device)))
     return packed, scales
+
+
+def moe_requant_fp8_fnuz(w_fnuz: torch.Tensor, s_fnuz: torch.Tensor,
+                         w_ocp: Optional[torch.Tensor] = None,
+                         s_ocp: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Row-scaled E4M3FNUZ weights w_fnuz uint8 [..., K] with scales s_fnuz fp32
+    [...] -> row-scaled OCP E4M3 weights uint8 [..., K] and scales fp32 [...]."""
+    _req(w_fnuz, "w_fnuz", torch.uint8)
+    _req(s_fnuz, "s_fnuz", torch.float32)
+    K = w_fnuz.shape[-1]
+    rows = w_fnuz.numel() // K if K else 0
+    if tuple(s_fnuz.shape) != tuple(w_fnuz.shape[:-1]):
+        raise ValueError("s_fnuz must have shape w_fnuz.shape[:-1]")
+    if w_ocp is None:
+        w_ocp = torch.empty_like(w_fnuz)
+    if s_ocp is None:
+        s_ocp = torch.empty_like(s_fnuz)
+    _check("moe_requant_fp8_fnuz", lib.moe_requant_fp8_fnuz(
+        _ptr(w_fnuz), _ptr(s_fnuz), rows, K, _ptr(w_ocp), _ptr(s_ocp), _stream(w_fnuz.device)))
+    return w_ocp, s_ocp
 
 
 def _gemm(fn_name: str, a_q, a_s, plan, E, w, w_scale, N, K, epilogue, out_dtype, out):

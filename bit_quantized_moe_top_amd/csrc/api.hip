@@ -77,6 +77,20 @@ int quant_fp8_per_token(const void* x, int x_dtype, int64_t M, int K, int64_t ld
   return launch_status(moeq::launch_quant_fp8(x, x_dtype, M, K, ld_x, q, scale, as_stream(stream)));
 }
 
+int moe_requant_fp8_fnuz(const uint8_t* w_fnuz, const float* s_fnuz, int64_t rows, int K,
+                         uint8_t* w_ocp, float* s_ocp, void* stream) {
+  if (rows < 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;
+  if (rows > 0 && (!w_fnuz || !s_fnuz || !w_ocp || !s_ocp)) return MOEQ_ERR_INVALID_ARG;
+  if (K % 8 != 0) return MOEQ_ERR_UNSUPPORTED;
+  if (rows > 0 && ((reinterpret_cast<uintptr_t>(w_fnuz) & 7u) ||
+                   (reinterpret_cast<uintptr_t>(w_ocp) & 7u)))
+    return MOEQ_ERR_INVALID_ARG;
+  if (rows == 0) return MOEQ_OK;
+  if (int rc = check_device()) return rc;
+  return launch_status(
+      moeq::launch_requant_fnuz(w_fnuz, s_fnuz, rows, K, w_ocp, s_ocp, as_stream(stream)));
+}
+
 int moe_permute(const int32_t* topk_ids, int T, int k, int E, const uint8_t* x_q, const float* x_s,
                 int H, uint8_t* xp_q, float* xp_s, void* plan, size_t plan_bytes, void* stream) {
   if (T < 0 || k <= 0 || E <= 0 || !plan) return MOEQ_ERR_INVALID_ARG;

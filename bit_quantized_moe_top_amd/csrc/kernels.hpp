@@ -70,6 +70,8 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, const uint8_t
 hipError_t launch_permute_quant(const int32_t* ids, int T, int k, int E, const void* x,
                                 int x_dtype, int H, uint8_t* x_q, float* x_s, uint8_t* xp_q,
                                 float* xp_s, void* plan, hipStream_t stream);
+hipError_t launch_requant_fnuz(const uint8_t* w_fnuz, const float* s_fnuz, int64_t rows, int K,
+                               uint8_t* w_ocp, float* s_ocp, hipStream_t stream);
 hipError_t launch_pack_int4(const float* w, int64_t rows, int K, uint8_t* packed, float* scales,
                             hipStream_t stream);
 

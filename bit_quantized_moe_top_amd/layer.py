@@ -16,7 +16,7 @@ import torch
 
 from . import (EPI_NONE, EPI_SILU_MUL, moe_combine, moe_expert_mlp_fp8row, moe_expert_mlp_w4a8,
                moe_grouped_gemm_fp8row, moe_grouped_gemm_w4a8, moe_plan_size,
-               moe_route_quant_permute, moe_shared_gemm_bf16, pack_int4_g128,
+               moe_requant_fp8_fnuz, moe_route_quant_permute, moe_shared_gemm_bf16, pack_int4_g128,
                quant_fp8_per_token)
 
 
@@ -51,6 +51,15 @@ class MoELayer:
         else:
             self.w13, self.s13 = quant_fp8_per_token(w13_f32)
             self.w2, self.s2 = quant_fp8_per_token(w2_f32)
+
+    def set_weights_fnuz(self, w13_fnuz, s13_fnuz, w2_fnuz, s2_fnuz):
+        """Row-scaled E4M3FNUZ expert weights (the MI300X checkpoint layout: scales
+        [E, out_channels], max|row| / 240), converted on the device to the
+        row-scaled OCP E4M3 weights this layer runs on."""
+        if self.weight_format != "fp8row":
+            raise ValueError("E4M3FNUZ weights are row-scaled FP8 experts (weight_format='fp8row')")
+        self.w13, self.s13 = moe_requant_fp8_fnuz(w13_fnuz, s13_fnuz)
+        self.w2, self.s2 = moe_requant_fp8_fnuz(w2_fnuz, s2_fnuz)
 
     def set_shared(self, ws13: Optional[torch.Tensor], ws2: Optional[torch.Tensor]):
         self.ws13, self.ws2 = ws13, ws2

@@ -11,8 +11,8 @@
  *   down      moe_grouped_gemm_w4a8 (epilogue NONE)      -> o (bf16)
  *   combine   moe_combine           y_t = sum_j w_tj * o_tj (+ shared_t)
  * with the row-scaled FP8 expert variant (moe_grouped_gemm_fp8row), the offline
- * weight packer (pack_int4_g128) and the dense bf16 shared-expert GEMM
- * (moe_shared_gemm_bf16).
+ * weight preparation (pack_int4_g128; moe_requant_fp8_fnuz for E4M3FNUZ
+ * checkpoints) and the dense bf16 shared-expert GEMM (moe_shared_gemm_bf16).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -188,6 +188,29 @@ int moe_route_quant_permute(const float* logits, const float* bias, int T, int E
  */
 int pack_int4_g128(const float* w, int64_t rows, int K, uint8_t* packed, float* scales,
                    void* stream);
+
+/*
+ * moe_requant_fp8_fnuz -- row-scaled E4M3FNUZ expert weights to row-scaled OCP
+ * E4M3 (offline weight preparation).
+ *
+ * The row-FP8 MI300X card ("Inkling 2 Small FP8 for AMD MI300X", "Precision and
+ * files") stores expert weights as E4M3FNUZ bytes (exponent bias 8, max 240,
+ * 0x80 the only NaN) with one fp32 scale per output channel, scale =
+ * max|row| / 240, tensors [n_experts, out_channels].  gfx950's FP8 is OCP E4M3,
+ * so each row is converted once:
+ *   w[r, k]  = fp32(s_fnuz[r] * fnuz(w_fnuz[r, k]))          (one rounding)
+ *   s_ocp[r] = fp32(max_k |w[r, k]| / 448)
+ *   w_ocp[r, k] = E4M3_RNE_saturating(fp32(w[r, k] / s_ocp[r]))   (IEEE division)
+ * i.e. quant_fp8_per_token applied to the dequantized rows.  Reading: the
+ * FNUZ NaN code 0x80 is read as 0 (checkpoints hold no NaN weights).
+ *
+ *   w_fnuz [rows, K] E4M3FNUZ bytes    s_fnuz [rows] fp32 (>= 0)
+ *   w_ocp  [rows, K] E4M3 (out)        s_ocp  [rows] fp32 (out)
+ * rows = experts * output channels.  Limits: rows >= 0, K % 8 == 0, w_fnuz and
+ * w_ocp 8-byte aligned.
+ */
+int moe_requant_fp8_fnuz(const uint8_t* w_fnuz, const float* s_fnuz, int64_t rows, int K,
+                         uint8_t* w_ocp, float* s_ocp, void* stream);
 
 /*
  * moe_grouped_gemm_w4a8 -- grouped GEMM over the routed experts with INT4 g128

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     assert set(names) == set(mq.EXPORTED_SYMBOLS)
 
 
@@ -68,6 +68,12 @@ def test_argument_errors_are_reported_without_a_gpu():
     assert L.quant_fp8_per_token(FAKE, 1, 4, 16, 8, FAKE, FAKE, N) == INVALID       # ld < K
     assert L.quant_fp8_per_token(ctypes.c_void_p(4100), 1, 4, 16, 16, FAKE, FAKE, N) == INVALID
     assert L.quant_fp8_per_token(N, 1, 0, 16, 16, N, N, N) == OK
+    # FNUZ -> OCP requantization
+    assert L.moe_requant_fp8_fnuz(FAKE, FAKE, 4, 12, FAKE, FAKE, N) == UNSUPPORTED    # K % 8
+    assert L.moe_requant_fp8_fnuz(N, FAKE, 4, 16, FAKE, FAKE, N) == INVALID           # null
+    assert L.moe_requant_fp8_fnuz(FAKE, FAKE, -1, 16, FAKE, FAKE, N) == INVALID       # rows < 0
+    assert L.moe_requant_fp8_fnuz(ctypes.c_void_p(4100), FAKE, 4, 16, FAKE, FAKE, N) == INVALID
+    assert L.moe_requant_fp8_fnuz(N, N, 0, 16, N, N, N) == OK                          # empty
     # permute
     small = mq.moe_plan_size(8, 32) - 4
     assert L.moe_permute(FAKE, 16, 2, 8, N, N, 0, N, N, FAKE, small, N) == WORKSPACE

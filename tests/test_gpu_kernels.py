@@ -69,7 +69,8 @@ def test_route_empty():
 # ------------------------------------------------------------ FP8 quantization ----
 @pytest.mark.parametrize("M,K,dtype", [(33, 4096, torch.bfloat16), (16, 256, torch.float32),
                                        (7, 2056, torch.bfloat16), (3, 8, torch.float32),
-                                       (130, 2048, torch.bfloat16)])
+                                       (130, 2048, torch.bfloat16), (5, 8200, torch.bfloat16),
+                                       (2, 4104, torch.float32)])
 def test_quant_fp8_per_token(M, K, dtype):
     g = torch.Generator().manual_seed(M * 7 + K)
     x = torch.randn(M, K, generator=g) * torch.logspace(-4, 3, M)[:, None]
@@ -108,6 +109,25 @@ def test_e4m3_encoder_boundary_sweep():
     torch.cuda.synchronize()
     assert (s.cpu().numpy() == 1.0).all()
     np.testing.assert_array_equal(q.cpu().numpy()[:, 1:], F.e4m3_encode(x[:, 1:]))
+
+
+# ------------------------------------------------- E4M3FNUZ -> OCP requantization ----
+@pytest.mark.parametrize("rows,K", [(37, 4096), (50, 2048), (9, 24), (5, 8192), (3, 520),
+                                    (4096, 4096)])
+def test_requant_fp8_fnuz(rows, K):
+    rng = np.random.default_rng(rows * 13 + K)
+    b = rng.integers(0, 256, size=(rows, K), dtype=np.uint8)   # includes 0x80 (read as 0)
+    b[:, rng.integers(0, K)] = 0x7F                            # a +240 in every row
+    s = (rng.random(rows) * 2e-3).astype(np.float32)
+    if rows > 3:
+        b[1] = 0x00                                            # zero row
+        s[2] = 0.0                                             # zero scale
+        b[3] = b[3] | 0x80                                     # all-negative row
+    w, sc = mq.moe_requant_fp8_fnuz(torch.from_numpy(b).to(_dev()), torch.from_numpy(s).to(_dev()))
+    torch.cuda.synchronize()
+    rq, rs = L.requant_fnuz_rows(b, s)
+    np.testing.assert_array_equal(sc.cpu().numpy(), rs)
+    np.testing.assert_array_equal(w.cpu().numpy(), rq)
 
 
 # -------------------------------------------------------------- INT4 packing ----
