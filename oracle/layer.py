@@ -106,12 +106,14 @@ def dequant_fp8_rows(q, s) -> np.ndarray:
 # ------------------------------------------------------ a9: INT4 g128 packing
 
 
-def _quantize_int4_block(w32):
+def _quantize_int4_block(w32, scale_dtype):
     rows, K = w32.shape
     G = K // GROUP
     wg = w32.reshape(rows, G, GROUP)
     a = np.abs(wg).max(axis=2)
     s = (a / np.float32(7.0)).astype(np.float32)
+    if scale_dtype == "bf16":
+        s = bf16_round(s).astype(np.float32)              # the stored scale, RNE to bfloat16
     c = np.zeros(wg.shape, dtype=np.int8)
     nz = s > 0
     ratio = (wg[nz] / s[nz][:, None]).astype(np.float32)
@@ -119,15 +121,21 @@ def _quantize_int4_block(w32):
     return c.reshape(rows, K), s
 
 
-def quantize_int4_g128(w, block_rows: int = 512):
+def quantize_int4_g128(w, block_rows: int = 512, scale_dtype: str = "fp32"):
     """Symmetric INT4 quantization in groups of 128 along the last (input) axis.
 
     For each row n and group g: a = max|W[n, g]|; s = fl32(a / 7);
     c = clamp(rint(fl32(W / s)), -8, 7) with rint = round half to even;
     a zero group gets s = 0 and codes 0.
-    Returns codes int8 [rows, K] and scales float32 [rows, K/128].
+    scale_dtype "bf16": the scale is stored as bfloat16, s = bf16(fl32(a / 7))
+    (RNE), and the codes are taken against that stored scale -- the 16-bit
+    scales that the W4A8 card's payload accounting implies (section 5).
+    Returns codes int8 [rows, K] and scales float32 [rows, K/128] (bf16 values
+    for "bf16").
     (Rows are processed in blocks only to bound temporary memory.)
     """
+    if scale_dtype not in ("fp32", "bf16"):
+        raise ValueError(scale_dtype)
     w32 = np.asarray(w, dtype=np.float32)
     rows, K = w32.shape
     if K % GROUP:
@@ -136,13 +144,13 @@ def quantize_int4_g128(w, block_rows: int = 512):
     scales = np.empty((rows, K // GROUP), dtype=np.float32)
     for r0 in range(0, rows, block_rows):
         codes[r0:r0 + block_rows], scales[r0:r0 + block_rows] = _quantize_int4_block(
-            w32[r0:r0 + block_rows])
+            w32[r0:r0 + block_rows], scale_dtype)
     return codes, scales
 
 
-def pack_int4_g128(w):
+def pack_int4_g128(w, scale_dtype: str = "fp32"):
     """quantize_int4_g128 followed by the storage packing: bytes [rows, K/2], scales."""
-    codes, s = quantize_int4_g128(w)
+    codes, s = quantize_int4_g128(w, scale_dtype=scale_dtype)
     return pack_int4(codes), s
 
 # ------------------------------------------------ a8 weights: row-scaled FP8

@@ -134,6 +134,26 @@ def test_int4_quant_brute_force():
                 assert codes[r, 128 * g + i] == want      # Python round() is half-to-even
 
 
+def test_int4_quant_bf16_scales_brute_force():
+    # the stored scale is torch's bfloat16 cast of fl32(a / 7); codes against it
+    rng = np.random.default_rng(18)
+    w = (rng.standard_normal((5, 256)) * 0.02).astype(np.float32)
+    w[1, :128] = 0.0                                  # a zero group
+    w[3, 5] = 0.02 * 7 * 1.003                        # scale rounded down: |w/s| > 7 -> clamp
+    codes, s = L.quantize_int4_g128(w, scale_dtype="bf16")
+    for r in range(5):
+        for g in range(2):
+            grp = [float(v) for v in w[r, 128 * g:128 * (g + 1)]]
+            a = max(abs(v) for v in grp)
+            sc = float(torch.tensor(float(np.float32(a) / np.float32(7.0)),
+                                    dtype=torch.float32).to(torch.bfloat16).float())
+            assert s[r, g] == sc
+            for i, v in enumerate(grp):
+                want = 0 if sc == 0 else max(-8, min(7, round(float(np.float32(v) / np.float32(sc)))))
+                assert codes[r, 128 * g + i] == want
+    assert np.abs(codes).max() <= 7                   # max/bf16(max/7) stays below 7.5
+
+
 def test_int4_quant_invariants_and_scale_shape_from_card():
     d = _golden_shapes()
     rows, cols = int(d["proj_rows"]), int(d["proj_cols"])
