@@ -55,9 +55,10 @@ def log(msg):
 
 def expert_bytes(cfg) -> tuple:
     """Algorithmic bytes of one expert's weights: (w13, w2) incl. scales."""
-    if cfg.weight_format == "w4a8":
-        w13 = 2 * cfg.I * cfg.H // 2 + 2 * cfg.I * (cfg.H // 128) * 4
-        w2 = cfg.H * cfg.I // 2 + cfg.H * (cfg.I // 128) * 4
+    if cfg.weight_format in ("w4a8", "w4a8_bf16s"):
+        sb = 2 if cfg.weight_format == "w4a8_bf16s" else 4      # bytes per group scale
+        w13 = 2 * cfg.I * cfg.H // 2 + 2 * cfg.I * (cfg.H // 128) * sb
+        w2 = cfg.H * cfg.I // 2 + cfg.H * (cfg.I // 128) * sb
     else:
         w13 = 2 * cfg.I * cfg.H + 2 * cfg.I * 4
         w2 = cfg.H * cfg.I + cfg.H * 4
@@ -79,8 +80,10 @@ def build_sets(cfg, n_sets, dev):
         kd13, kd2 = (c.H, c.I) if fp8 else (c.H // 2, c.I // 2)
         w13 = torch.empty(c.E, 2 * c.I, kd13, dtype=torch.uint8, device=dev)
         w2 = torch.empty(c.E, c.H, kd2, dtype=torch.uint8, device=dev)
-        s13 = torch.empty((c.E, 2 * c.I) if fp8 else (c.E, 2 * c.I, c.H // 128), device=dev)
-        s2 = torch.empty((c.E, c.H) if fp8 else (c.E, c.H, c.I // 128), device=dev)
+        sdt = torch.bfloat16 if c.weight_format == "w4a8_bf16s" else torch.float32
+        s13 = torch.empty((c.E, 2 * c.I) if fp8 else (c.E, 2 * c.I, c.H // 128), dtype=sdt,
+                          device=dev)
+        s2 = torch.empty((c.E, c.H) if fp8 else (c.E, c.H, c.I // 128), dtype=sdt, device=dev)
         quant = mq.quant_fp8_per_token if fp8 else mq.pack_int4_g128
         for which, wq, ws in (("w13", w13, s13), ("w2", w2, s2)):
             for e0, wf in W.iter_expert_weights(c, which, dev, chunk=32):

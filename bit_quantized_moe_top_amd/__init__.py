@@ -21,7 +21,8 @@ __all__ = [
     "MAX_EXPERTS", "MAX_TOPK", "MoeqError", "moe_abi_version", "moe_status_string",
     "moe_plan_size", "moe_route_topk", "quant_fp8_per_token", "moe_permute",
     "moe_route_quant_permute", "pack_int4_g128", "moe_requant_fp8_fnuz",
-    "moe_grouped_gemm_w4a8", "moe_grouped_gemm_fp8row", "moe_combine", "moe_shared_gemm_bf16",
+    "moe_grouped_gemm_w4a8", "moe_grouped_gemm_w4a8_bf16s", "moe_expert_mlp_w4a8",
+    "moe_expert_mlp_w4a8_bf16s", "moe_expert_mlp_fp8row", "pack_int4_g128_bf16s", "moe_grouped_gemm_fp8row", "moe_combine", "moe_shared_gemm_bf16",
     "plan_fields", "EXPORTED_SYMBOLS",
 ]
 
@@ -49,11 +50,15 @@ _SIGNATURES = {
     "moe_route_quant_permute": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P,
                                      _P, _SZ, _P]),
     "pack_int4_g128": (_I, [_P, _I64, _I, _P, _P, _P]),
+    "pack_int4_g128_bf16s": (_I, [_P, _I64, _I, _P, _P, _P]),
     "moe_requant_fp8_fnuz": (_I, [_P, _P, _I64, _I, _P, _P, _P]),
     "moe_grouped_gemm_w4a8": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_grouped_gemm_fp8row": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
+    "moe_grouped_gemm_w4a8_bf16s": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_expert_mlp_w4a8": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P,
                                  _P]),
+    "moe_expert_mlp_w4a8_bf16s": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P,
+                                       _P, _P]),
     "moe_expert_mlp_fp8row": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P,
                                    _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
@@ -227,18 +232,32 @@ def moe_route_quant_permute(logits: torch.Tensor, x: torch.Tensor, k: int,
 
 
 def pack_int4_g128(w: torch.Tensor, packed: Optional[torch.Tensor] = None,
-                   scales: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """w [..., K] fp32 -> packed uint8 [..., K/2], scales fp32 [..., K/128]."""
+                   scales: Optional[torch.Tensor] = None,
+                   scale_dtype=torch.float32) -> Tuple[torch.Tensor, torch.Tensor]:
+    """w [..., K] fp32 -> packed uint8 [..., K/2], scales [..., K/128] of scale_dtype
+    (fp32: pack_int4_g128; bfloat16: pack_int4_g128_bf16s)."""
     _req(w, "w", torch.float32)
+    if scales is not None:
+        scale_dtype = scales.dtype
+    if scale_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("scale_dtype must be float32 or bfloat16")
     K = w.shape[-1]
     rows = w.numel() // K if K else 0
     if packed is None:
         packed = torch.empty(*w.shape[:-1], K // 2, dtype=torch.uint8, device=w.device)
     if scales is None:
-        scales = torch.empty(*w.shape[:-1], K // 128, dtype=torch.float32, device=w.device)
-    _check("pack_int4_g128", lib.pack_int4_g128(_ptr(w), rows, K, _ptr(packed), _ptr(scales),
-                                                _stream(w.device)))
+        scales = torch.empty(*w.shape[:-1], K // 128, dtype=scale_dtype, device=w.device)
+    _req(scales, "scales", scale_dtype)
+    name = "pack_int4_g128" if scale_dtype == torch.float32 else "pack_int4_g128_bf16s"
+    _check(name, getattr(lib, name)(_ptr(w), rows, K, _ptr(packed), _ptr(scales),
+                                    _stream(w.device)))
     return packed, scales
+
+
+def pack_int4_g128_bf16s(w: torch.Tensor, packed: Optional[torch.Tensor] = None,
+                         scales: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """pack_int4_g128 with bfloat16 scales."""
+    return pack_int4_g128(w, packed, scales, scale_dtype=torch.bfloat16)
 
 
 def moe_requant_fp8_fnuz(w_fnuz: torch.Tensor, s_fnuz: torch.Tensor,
@@ -282,14 +301,23 @@ def moe_grouped_gemm_w4a8(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Tens
                           w_packed: torch.Tensor, w_scales: torch.Tensor,
                           epilogue: int = EPI_NONE, out_dtype=torch.bfloat16,
                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """w_packed [E, N, K/2] uint8, w_scales [E, N, K/128] fp32."""
+    """w_packed [E, N, K/2] uint8, w_scales [E, N, K/128] fp32 (or bfloat16: then
+    moe_grouped_gemm_w4a8_bf16s)."""
     _req(w_packed, "w_packed", torch.uint8, 3)
-    _req(w_scales, "w_scales", torch.float32, 3)
+    bf16 = w_scales.dtype == torch.bfloat16
+    _req(w_scales, "w_scales", torch.bfloat16 if bf16 else torch.float32, 3)
     E, N, K2 = w_packed.shape
     if tuple(w_scales.shape) != (E, N, 2 * K2 // 128):
         raise ValueError("w_scales shape does not match w_packed")
-    return _gemm("moe_grouped_gemm_w4a8", a_q, a_s, plan, E, w_packed, w_scales, N, 2 * K2,
-                 epilogue, out_dtype, out)
+    name = "moe_grouped_gemm_w4a8_bf16s" if bf16 else "moe_grouped_gemm_w4a8"
+    return _gemm(name, a_q, a_s, plan, E, w_packed, w_scales, N, 2 * K2, epilogue, out_dtype, out)
+
+
+def moe_grouped_gemm_w4a8_bf16s(a_q, a_s, plan, w_packed, w_scales, epilogue: int = EPI_NONE,
+                                out_dtype=torch.bfloat16, out=None) -> torch.Tensor:
+    """moe_grouped_gemm_w4a8 with bfloat16 group scales w_scales [E, N, K/128]."""
+    _req(w_scales, "w_scales", torch.bfloat16, 3)
+    return moe_grouped_gemm_w4a8(a_q, a_s, plan, w_packed, w_scales, epilogue, out_dtype, out)
 
 
 def moe_grouped_gemm_fp8row(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Tensor,
@@ -331,18 +359,26 @@ def moe_expert_mlp_w4a8(xp_q: torch.Tensor, xp_s: torch.Tensor, plan: torch.Tens
                         w2_scales: torch.Tensor, out: Optional[dict] = None) -> dict:
     """gate/up GEMM + SiLU, FP8 quantization of h, down GEMM (two launches for R <= 64).
     w13 [E, 2I, H/2], w13_scales [E, 2I, H/128], w2 [E, H, I/2], w2_scales [E, H, I/128].
+    Scales fp32, or both bfloat16 (then moe_expert_mlp_w4a8_bf16s).
     Returns a dict with h, h_q, h_s, o (reusing `out`'s tensors)."""
     for t, name in ((w13, "w13"), (w2, "w2")):
         _req(t, name, torch.uint8, 3)
+    sdt = torch.bfloat16 if w13_scales.dtype == torch.bfloat16 else torch.float32
     for t, name in ((w13_scales, "w13_scales"), (w2_scales, "w2_scales")):
-        _req(t, name, torch.float32, 3)
+        _req(t, name, sdt, 3)
     E, N13, H2 = w13.shape
     H, I = 2 * H2, N13 // 2
     if tuple(w2.shape) != (E, H, I // 2) or tuple(w13_scales.shape) != (E, N13, H // 128) or \
             tuple(w2_scales.shape) != (E, H, I // 128):
         raise ValueError("w13 / w2 / scale shapes do not match")
-    return _expert_mlp("moe_expert_mlp_w4a8", xp_q, xp_s, plan, E, w13, w13_scales, w2, w2_scales,
-                       H, I, out)
+    name = "moe_expert_mlp_w4a8_bf16s" if sdt == torch.bfloat16 else "moe_expert_mlp_w4a8"
+    return _expert_mlp(name, xp_q, xp_s, plan, E, w13, w13_scales, w2, w2_scales, H, I, out)
+
+
+def moe_expert_mlp_w4a8_bf16s(xp_q, xp_s, plan, w13, w13_scales, w2, w2_scales, out=None) -> dict:
+    """moe_expert_mlp_w4a8 with bfloat16 group scales."""
+    _req(w13_scales, "w13_scales", torch.bfloat16, 3)
+    return moe_expert_mlp_w4a8(xp_q, xp_s, plan, w13, w13_scales, w2, w2_scales, out)
 
 
 def moe_expert_mlp_fp8row(xp_q: torch.Tensor, xp_s: torch.Tensor, plan: torch.Tensor,

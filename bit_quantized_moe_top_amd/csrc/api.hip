@@ -131,8 +131,8 @@ int moe_route_quant_permute(const float* logits, const float* bias, int T, int E
                                           as_stream(stream)));
 }
 
-int pack_int4_g128(const float* w, int64_t rows, int K, uint8_t* packed, float* scales,
-                   void* stream) {
+static int pack_common(const float* w, int64_t rows, int K, uint8_t* packed, void* scales,
+                       int bf16_scales, void* stream) {
   if (rows < 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;
   if (K % 128 != 0) return MOEQ_ERR_UNSUPPORTED;
   if (rows > 0 && (!w || !packed || !scales)) return MOEQ_ERR_INVALID_ARG;
@@ -140,11 +140,22 @@ int pack_int4_g128(const float* w, int64_t rows, int K, uint8_t* packed, float* 
     return MOEQ_ERR_INVALID_ARG;
   if (rows == 0) return MOEQ_OK;
   if (int rc = check_device()) return rc;
-  return launch_status(moeq::launch_pack_int4(w, rows, K, packed, scales, as_stream(stream)));
+  return launch_status(
+      moeq::launch_pack_int4(w, rows, K, packed, scales, bf16_scales, as_stream(stream)));
+}
+
+int pack_int4_g128(const float* w, int64_t rows, int K, uint8_t* packed, float* scales,
+                   void* stream) {
+  return pack_common(w, rows, K, packed, scales, 0, stream);
+}
+
+int pack_int4_g128_bf16s(const float* w, int64_t rows, int K, uint8_t* packed, uint16_t* scales,
+                         void* stream) {
+  return pack_common(w, rows, K, packed, scales, 1, stream);
 }
 
 static int gemm_common(int wfmt, const uint8_t* a_q, const float* a_s, const void* plan, int E,
-                       int R, const uint8_t* w, const float* w_scale, int N, int K, int epilogue,
+                       int R, const uint8_t* w, const void* w_scale, int N, int K, int epilogue,
                        void* out, int out_dtype, void* stream) {
   if (R < 0 || E <= 0 || N <= 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;
   if (epilogue != MOEQ_EPI_NONE && epilogue != MOEQ_EPI_SILU_MUL) return MOEQ_ERR_INVALID_ARG;
@@ -168,6 +179,13 @@ int moe_grouped_gemm_w4a8(const uint8_t* a_q, const float* a_s, const void* plan
                      out_dtype, stream);
 }
 
+int moe_grouped_gemm_w4a8_bf16s(const uint8_t* a_q, const float* a_s, const void* plan, int E,
+                                int R, const uint8_t* w_packed, const uint16_t* w_scales, int N,
+                                int K, int epilogue, void* out, int out_dtype, void* stream) {
+  return gemm_common(moeq::kW4G128Bf16, a_q, a_s, plan, E, R, w_packed, w_scales, N, K, epilogue,
+                     out, out_dtype, stream);
+}
+
 int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
                             const uint8_t* w_fp8, const float* w_row_scale, int N, int K,
                             int epilogue, void* out, int out_dtype, void* stream) {
@@ -176,8 +194,8 @@ int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* pl
 }
 
 static int mlp_common(int wfmt, const uint8_t* xp_q, const float* xp_s, const void* plan,
-                      size_t plan_bytes, int E, int R, const uint8_t* w13, const float* s13,
-                      const uint8_t* w2, const float* s2, int H, int I, uint16_t* h, uint8_t* h_q,
+                      size_t plan_bytes, int E, int R, const uint8_t* w13, const void* s13,
+                      const uint8_t* w2, const void* s2, int H, int I, uint16_t* h, uint8_t* h_q,
                       float* h_s, uint16_t* o, void* stream) {
   if (R < 0 || E <= 0 || H <= 0 || I <= 0) return MOEQ_ERR_INVALID_ARG;
   if (E > MOEQ_MAX_EXPERTS) return MOEQ_ERR_UNSUPPORTED;
@@ -203,6 +221,15 @@ int moe_expert_mlp_w4a8(const uint8_t* xp_q, const float* xp_s, const void* plan
                         const uint8_t* w2, const float* w2_scales, int H, int I, uint16_t* h,
                         uint8_t* h_q, float* h_s, uint16_t* o, void* stream) {
   return mlp_common(moeq::kW4G128, xp_q, xp_s, plan, plan_bytes, E, R, w13, w13_scales, w2,
+                    w2_scales, H, I, h, h_q, h_s, o, stream);
+}
+
+int moe_expert_mlp_w4a8_bf16s(const uint8_t* xp_q, const float* xp_s, const void* plan,
+                              size_t plan_bytes, int E, int R, const uint8_t* w13,
+                              const uint16_t* w13_scales, const uint8_t* w2,
+                              const uint16_t* w2_scales, int H, int I, uint16_t* h, uint8_t* h_q,
+                              float* h_s, uint16_t* o, void* stream) {
+  return mlp_common(moeq::kW4G128Bf16, xp_q, xp_s, plan, plan_bytes, E, R, w13, w13_scales, w2,
                     w2_scales, H, I, h, h_q, h_s, o, stream);
 }
 

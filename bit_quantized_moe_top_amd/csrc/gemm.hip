@@ -18,7 +18,8 @@ namespace {
 template <int WFMT, int EPI, int GS, int NB>
 __global__ void __launch_bounds__(kThreads, 3)   // >= 3 waves per SIMD
 gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int E, int R,
-                 const uint8_t* w, const float* w_scale, int N, int K, void* out, int out_f32) {
+                 const uint8_t* w, const ScaleT<WFMT>* w_scale, int N, int K, void* out,
+                 int out_f32) {
   const int lane = threadIdx.x & 63;
   const int ln = lane & 15, kb = lane >> 4;
   const int units_per_tile = N / (16 * NB);
@@ -33,7 +34,7 @@ gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
   int col[NB];
   unit_columns<EPI, NB>(N, u, col);
   const uint8_t* wrow[NB];
-  const float* srow[NB];
+  const ScaleT<WFMT>* srow[NB];
   weight_rows<WFMT, NB>(w, w_scale, ti.e, N, K, col, ln, wrow, srow);
 
   const int nrb = (ti.rows + 15) >> 4;
@@ -54,7 +55,7 @@ gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
 template <int WFMT, int GS, int CB_>
 struct TileShape {
   static constexpr int CB = CB_;
-  static_assert(CB == 2 || (CB == 4 && WFMT == kW4G128 && GS > 0 && GS % 16 == 0), "tile shape");
+  static_assert(CB == 2 || (CB == 4 && kIsW4<WFMT> && GS > 0 && GS % 16 == 0), "tile shape");
   // (the looped sweep, GS == 0, keeps a shallower ring to stay within registers)
   static constexpr int kDepth = (CB == 4 || GS == 0) ? 2 : TileDepth<WFMT>::value;
   static constexpr int kWavesPerSimd = (CB == 4) ? 2 : 3;
@@ -74,7 +75,7 @@ template <int WFMT, int EPI, int GS, int CB_>
 __global__ void __launch_bounds__(kThreads, (CB_ == 4) ? 2 : 3)   // TileShape::kWavesPerSimd
 gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
                  const int32_t* __restrict__ plan, int E, int R, const uint8_t* __restrict__ w,
-                 const float* __restrict__ w_scale, int N, int K, void* __restrict__ out,
+                 const ScaleT<WFMT>* __restrict__ w_scale, int N, int K, void* __restrict__ out,
                  int out_f32) {
   using Shape = TileShape<WFMT, GS, CB_>;
   constexpr int CB = Shape::CB;
@@ -113,7 +114,7 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
       col[j] = nt * BN + 16 * (wave + 4 * j);
   }
   const uint8_t* wrow[CB];
-  const float* srow[CB];
+  const ScaleT<WFMT>* srow[CB];
   weight_rows<WFMT, CB>(w, w_scale, ti.e, N, K, col, ln, wrow, srow);
 
   // A staging: wave w stages rows 16 w .. 16 w + 15 of the 64 x 128 B slice;
@@ -132,9 +133,9 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
   auto store_a = [&](int buf, const uint4& x0, const uint4& x1) {
     if (!st_on) return;
     *reinterpret_cast<uint4*>(&As[buf][st_r0 * kRowDw + st_seg * 4]) =
-        (WFMT == kW4G128) ? shuffle_a16(x0) : x0;
+        kIsW4<WFMT> ? shuffle_a16(x0) : x0;
     *reinterpret_cast<uint4*>(&As[buf][st_r1 * kRowDw + st_seg * 4]) =
-        (WFMT == kW4G128) ? shuffle_a16(x1) : x1;
+        kIsW4<WFMT> ? shuffle_a16(x1) : x1;
   };
 
   v4f acc[4][CB];
@@ -155,8 +156,8 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
     for (int j = 0; j < CB; ++j)
 #pragma unroll
       for (int i = 0; i < kPer; i += 4) {
-        const float4 f = *reinterpret_cast<const float4*>(srow[j] + kb * kPer + i);
-        const float fv[4] = {f.x, f.y, f.z, f.w};
+        float fv[4];
+        load_scales<4>(srow[j] + kb * kPer + i, fv);
 #pragma unroll
         for (int t = 0; t < 4; ++t) Ss[(((kb * kPer + i + t) * 4 + wave) * 16 + ln) * CB + j] = fv[t];
       }
@@ -223,7 +224,7 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
 
 template <int WFMT, int EPI, int GS>
 hipError_t launch_kernels(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
-                          const uint8_t* w, const float* w_scale, int N, int K, void* out,
+                          const uint8_t* w, const ScaleT<WFMT>* w_scale, int N, int K, void* out,
                           int out_f32, hipStream_t stream) {
   const int32_t* p = static_cast<const int32_t*>(plan);
   if (R <= 64) {
@@ -244,7 +245,7 @@ hipError_t launch_kernels(const uint8_t* a_q, const float* a_s, const void* plan
                          dim3(kThreads), 0, stream, a_q, a_s, p, E, R, w, w_scale, N, K, out,
                          out_f32);
     };
-    if constexpr (WFMT == kW4G128 && GS > 0) {
+    if constexpr (kIsW4<WFMT> && GS > 0) {
       if (N % 256 == 0) tile(std::integral_constant<int, 4>());
       else tile(std::integral_constant<int, 2>());
     } else {
@@ -258,7 +259,7 @@ hipError_t launch_kernels(const uint8_t* a_q, const float* a_s, const void* plan
 // fully unrolled K sweeps; any other multiple of 128 uses the looped sweep.
 template <int WFMT, int EPI>
 hipError_t launch_shape(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
-                        const uint8_t* w, const float* w_scale, int N, int K, void* out,
+                        const uint8_t* w, const ScaleT<WFMT>* w_scale, int N, int K, void* out,
                         int out_f32, hipStream_t stream) {
   switch (K >> 7) {
     case 32:
@@ -275,7 +276,8 @@ hipError_t launch_shape(const uint8_t* a_q, const float* a_s, const void* plan, 
 
 template <int WFMT>
 hipError_t launch_fmt(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
-                      const uint8_t* w, const float* w_scale, int N, int K, int epilogue, void* out,
+                      const uint8_t* w, const ScaleT<WFMT>* w_scale, int N, int K, int epilogue,
+                      void* out,
                       int out_f32, hipStream_t stream) {
   if (epilogue == MOEQ_EPI_SILU_MUL)
     return launch_shape<WFMT, MOEQ_EPI_SILU_MUL>(a_q, a_s, plan, E, R, w, w_scale, N, K, out,
@@ -287,15 +289,22 @@ hipError_t launch_fmt(const uint8_t* a_q, const float* a_s, const void* plan, in
 }  // namespace
 
 hipError_t launch_grouped_gemm(int wfmt, const uint8_t* a_q, const float* a_s, const void* plan,
-                               int E, int R, const uint8_t* w, const float* w_scale, int N, int K,
+                               int E, int R, const uint8_t* w, const void* w_scale, int N, int K,
                                int epilogue, void* out, int out_dtype, hipStream_t stream) {
   if (R == 0) return hipSuccess;
   const int out_f32 = out_dtype == MOEQ_F32 ? 1 : 0;
-  if (wfmt == kW4G128)
-    return launch_fmt<kW4G128>(a_q, a_s, plan, E, R, w, w_scale, N, K, epilogue, out, out_f32,
-                               stream);
-  return launch_fmt<kFp8Row>(a_q, a_s, plan, E, R, w, w_scale, N, K, epilogue, out, out_f32,
-                             stream);
+  switch (wfmt) {
+    case kW4G128:
+      return launch_fmt<kW4G128>(a_q, a_s, plan, E, R, w, static_cast<const float*>(w_scale), N, K,
+                                 epilogue, out, out_f32, stream);
+    case kW4G128Bf16:
+      return launch_fmt<kW4G128Bf16>(a_q, a_s, plan, E, R, w,
+                                     static_cast<const uint16_t*>(w_scale), N, K, epilogue, out,
+                                     out_f32, stream);
+    default:
+      return launch_fmt<kFp8Row>(a_q, a_s, plan, E, R, w, static_cast<const float*>(w_scale), N, K,
+                                 epilogue, out, out_f32, stream);
+  }
 }
 
 }  // namespace moeq

@@ -6,7 +6,8 @@
 //
 // Weight formats:
 //   kW4G128 -- INT4 codes, two per byte (low nibble first), one fp32 scale per
-//              (output row, 128-wide K group).  Each code is converted exactly to
+//              (output row, 128-wide K group); kW4G128Bf16 the same with
+//              bfloat16 scales (converted to fp32 as they are read).  Each code is converted exactly to
 //              its OCP E4M3 byte with two v_perm_b32 table lookups and an xor, so
 //              the products run on v_mfma_f32_16x16x128_f8f6f4 (FP8 x FP8, fp32
 //              accumulate).  One MFMA covers exactly one 128-wide group: its fp32
@@ -76,11 +77,46 @@ constexpr int kXcds = 8;
 #ifndef MOEQ_TILE_W4_DEPTH
 #define MOEQ_TILE_W4_DEPTH 3
 #endif
+// INT4 weights (either scale type)
 template <int WFMT>
-struct Depth { static constexpr int value = (WFMT == kW4G128) ? MOEQ_W4_DEPTH : MOEQ_FP8_DEPTH; };
+constexpr bool kIsW4 = (WFMT == kW4G128 || WFMT == kW4G128Bf16);
+
+// element type of the weight scales
+template <int WFMT>
+struct ScaleOf { using type = float; };
+template <>
+struct ScaleOf<kW4G128Bf16> { using type = uint16_t; };
+template <int WFMT>
+using ScaleT = typename ScaleOf<WFMT>::type;
+
+__device__ __forceinline__ float scale_value(float s) { return s; }
+__device__ __forceinline__ float scale_value(uint16_t s) { return bf16_to_f32(s); }
+
+// n consecutive scales (n % 4 == 0) starting at p, as fp32: 16-byte (fp32) or
+// 8-byte (bf16) vector loads
+template <int n>
+__device__ __forceinline__ void load_scales(const float* p, float* out) {
+#pragma unroll
+  for (int i = 0; i < n; i += 4) {
+    const float4 f = *reinterpret_cast<const float4*>(p + i);
+    out[i] = f.x; out[i + 1] = f.y; out[i + 2] = f.z; out[i + 3] = f.w;
+  }
+}
+template <int n>
+__device__ __forceinline__ void load_scales(const uint16_t* p, float* out) {
+#pragma unroll
+  for (int i = 0; i < n; i += 4) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+    out[i] = u2f(u.x << 16); out[i + 1] = u2f(u.x & 0xFFFF0000u);
+    out[i + 2] = u2f(u.y << 16); out[i + 3] = u2f(u.y & 0xFFFF0000u);
+  }
+}
+
+template <int WFMT>
+struct Depth { static constexpr int value = kIsW4<WFMT> ? MOEQ_W4_DEPTH : MOEQ_FP8_DEPTH; };
 template <int WFMT>
 struct TileDepth {
-  static constexpr int value = (WFMT == kW4G128) ? MOEQ_TILE_W4_DEPTH : MOEQ_FP8_DEPTH;
+  static constexpr int value = kIsW4<WFMT> ? MOEQ_TILE_W4_DEPTH : MOEQ_FP8_DEPTH;
 };
 
 // INT4 nibble (code + 8) -> E4M3 byte of the code, four nibbles (one per byte,
@@ -143,6 +179,9 @@ __device__ __forceinline__ v8i as_v8i(const uint4& x0, const uint4& x1) {
 __device__ __forceinline__ float load_scale(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ float load_scale(const uint16_t* p) {
+  return bf16_to_f32(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
 
 // weight fragment of one lane for one 16-row block and one group
 template <int WFMT>
@@ -156,6 +195,9 @@ struct BFrag<kW4G128> {
   }
   __device__ __forceinline__ v8i operand() const { return unpack_w4(raw); }
 };
+
+template <>
+struct BFrag<kW4G128Bf16> : BFrag<kW4G128> {};
 
 template <>
 struct BFrag<kFp8Row> {
@@ -188,15 +230,16 @@ __device__ __forceinline__ TileInfo tile_info(const int32_t* plan, int E, int R,
 
 // weight-row bases (16-row block j of this wave) and their scale rows
 template <int WFMT, int NB = 2>
-__device__ __forceinline__ void weight_rows(const uint8_t* w, const float* w_scale, int e, int N,
-                                            int K, const int (&col)[NB], int ln,
-                                            const uint8_t* (&wrow)[NB], const float* (&srow)[NB]) {
-  const int64_t row_bytes = (WFMT == kW4G128) ? (K >> 1) : K;
+__device__ __forceinline__ void weight_rows(const uint8_t* w, const ScaleT<WFMT>* w_scale, int e,
+                                            int N, int K, const int (&col)[NB], int ln,
+                                            const uint8_t* (&wrow)[NB],
+                                            const ScaleT<WFMT>* (&srow)[NB]) {
+  const int64_t row_bytes = kIsW4<WFMT> ? (K >> 1) : K;
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int64_t n_glob = int64_t(e) * N + col[j] + ln;
     wrow[j] = w + n_glob * row_bytes;
-    srow[j] = (WFMT == kW4G128) ? (w_scale + n_glob * (K >> 7)) : (w_scale + n_glob);
+    srow[j] = kIsW4<WFMT> ? (w_scale + n_glob * (K >> 7)) : (w_scale + n_glob);
   }
 }
 
@@ -204,9 +247,9 @@ __device__ __forceinline__ void weight_rows(const uint8_t* w, const float* w_sca
 // row_scale(p) is the activation scale of sorted row p
 // the weight-row scales applied at the end (row-scaled FP8 only)
 template <int WFMT, int NB = 2>
-__device__ __forceinline__ void row_scales(const float* const (&srow)[NB], float (&rs)[NB]) {
+__device__ __forceinline__ void row_scales(const ScaleT<WFMT>* const (&srow)[NB], float (&rs)[NB]) {
 #pragma unroll
-  for (int j = 0; j < NB; ++j) rs[j] = (WFMT == kFp8Row) ? srow[j][0] : 1.0f;
+  for (int j = 0; j < NB; ++j) rs[j] = (WFMT == kFp8Row) ? scale_value(srow[j][0]) : 1.0f;
 }
 
 // SiLU-gated product of result row v (gate block 0, up block 1) as bf16
@@ -220,7 +263,8 @@ __device__ __forceinline__ uint16_t silu_mul_bf16(const v4f (&acc)[2], int v, fl
 // (EPI_SILU_MUL: blocks j < NB/2 gate rows, block j + NB/2 the matching up rows)
 template <int WFMT, int EPI, int NB = 2, typename RowScaleF>
 __device__ __forceinline__ void store_block(const v4f (&acc)[NB], int rb, int row0, int rows,
-                                            RowScaleF&& row_scale, const float* const (&srow)[NB],
+                                            RowScaleF&& row_scale,
+                                            const ScaleT<WFMT>* const (&srow)[NB],
                                             const int (&col)[NB], int ln, int kb, int N, void* out,
                                             int out_f32) {
   float rs[NB];
@@ -265,7 +309,7 @@ __device__ __forceinline__ void pin(v4f& a) {
 
 template <int WFMT>
 __device__ __forceinline__ void accumulate(v4f& acc, const v8i& a, const v8i& b, float s) {
-  if (WFMT == kW4G128) {
+  if (kIsW4<WFMT>) {
     const v4f part = mfma_fp8(a, b, v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[v] = fmaf(s, part[v], acc[v]);
@@ -321,22 +365,17 @@ __device__ __forceinline__ void pipeline(int G, IssueF&& issue, ConsumeF&& consu
 // Otherwise (any G) one load per row and group.
 template <int WFMT, int GS, int NB = 2>
 struct GroupScales {
-  static constexpr bool kPreload = (WFMT == kW4G128) && GS > 0 && GS % 16 == 0;
+  static constexpr bool kPreload = kIsW4<WFMT> && GS > 0 && GS % 16 == 0;
   static constexpr int kPerLane = kPreload ? GS / 4 : 1;
   float v[NB][kPerLane];
-  const float* row[NB];
+  const ScaleT<WFMT>* row[NB];
 
-  __device__ __forceinline__ void init(const float* const (&srow)[NB], int kb) {
+  __device__ __forceinline__ void init(const ScaleT<WFMT>* const (&srow)[NB], int kb) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) row[j] = srow[j];
     if constexpr (kPreload) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int i = 0; i < kPerLane; i += 4) {
-          const float4 f = *reinterpret_cast<const float4*>(srow[j] + kb * kPerLane + i);
-          v[j][i] = f.x; v[j][i + 1] = f.y; v[j][i + 2] = f.z; v[j][i + 3] = f.w;
-        }
+      for (int j = 0; j < NB; ++j) load_scales<kPerLane>(srow[j] + kb * kPerLane, v[j]);
     }
   }
   // scale of group g for block j; `held` is the value a ring stage loaded (non-preload path)
@@ -348,7 +387,7 @@ struct GroupScales {
     }
   }
   __device__ __forceinline__ float load(int j, int g) const {
-    if constexpr (kPreload || WFMT != kW4G128) return 1.0f;
+    if constexpr (kPreload || !kIsW4<WFMT>) return 1.0f;
     else return load_scale(row[j] + g);
   }
 };
@@ -390,7 +429,7 @@ enum ASource { kAGlobal = 0, kALds = 1 };
 template <int WFMT, int NB, int GS, bool kSplit, int ASRC = kAGlobal, typename HookF>
 __device__ __forceinline__ void wave_sweep(v4f (&acc)[NB], const uint8_t* a_q, int K, int row0,
                                            int rows, int rb, const uint8_t* const (&wrow)[NB],
-                                           const float* const (&srow)[NB], int ln, int kb,
+                                           const ScaleT<WFMT>* const (&srow)[NB], int ln, int kb,
                                            HookF&& before_a, int a_stride = 0) {
   const int G = K >> 7;
   const bool a_ok = 16 * rb + ln < rows;
@@ -429,7 +468,7 @@ __device__ __forceinline__ void wave_sweep(v4f (&acc)[NB], const uint8_t* a_q, i
   };
   auto consume = [&](int slot, int g, bool refill) {
     const WaveStage<WFMT, NB>& s = st[slot];
-    const v8i aop = (WFMT == kW4G128) ? shuffle_a(s.a0, s.a1) : as_v8i(s.a0, s.a1);
+    const v8i aop = kIsW4<WFMT> ? shuffle_a(s.a0, s.a1) : as_v8i(s.a0, s.a1);
     v8i b[NB];
     float sg[NB];
 #pragma unroll

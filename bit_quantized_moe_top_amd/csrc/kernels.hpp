@@ -72,14 +72,16 @@ hipError_t launch_permute_quant(const int32_t* ids, int T, int k, int E, const v
                                 float* xp_s, void* plan, hipStream_t stream);
 hipError_t launch_requant_fnuz(const uint8_t* w_fnuz, const float* s_fnuz, int64_t rows, int K,
                                uint8_t* w_ocp, float* s_ocp, hipStream_t stream);
-hipError_t launch_pack_int4(const float* w, int64_t rows, int K, uint8_t* packed, float* scales,
-                            hipStream_t stream);
+// INT4 g128 packing; bf16_scales: scales stored as bfloat16 (uint16), else fp32
+hipError_t launch_pack_int4(const float* w, int64_t rows, int K, uint8_t* packed, void* scales,
+                            int bf16_scales, hipStream_t stream);
 
-// weight formats of the grouped GEMM
-enum WeightFormat { kW4G128 = 0, kFp8Row = 1 };
+// weight formats of the grouped GEMM: INT4 g128 with fp32 or bf16 group scales,
+// row-scaled E4M3 (fp32 row scales); w_scale points to scales of that type
+enum WeightFormat { kW4G128 = 0, kFp8Row = 1, kW4G128Bf16 = 2 };
 
 hipError_t launch_grouped_gemm(int wfmt, const uint8_t* a_q, const float* a_s, const void* plan,
-                               int E, int R, const uint8_t* w, const float* w_scale, int N, int K,
+                               int E, int R, const uint8_t* w, const void* w_scale, int N, int K,
                                int epilogue, void* out, int out_dtype, hipStream_t stream);
 
 // E is read from the plan header on the device.
@@ -99,8 +101,8 @@ hipError_t launch_front(const float* logits, const float* bias, int T, int E, in
 // R <= kMlpMaxRows (the down GEMM quantizes h), three otherwise.
 hipError_t launch_expert_mlp(int wfmt, const uint8_t* xp_q, const float* xp_s, const void* plan,
                              int E,
-                             int R, const uint8_t* w13, const float* s13, const uint8_t* w2,
-                             const float* s2, int H, int I, uint16_t* h, uint8_t* h_q, float* h_s,
+                             int R, const uint8_t* w13, const void* s13, const uint8_t* w2,
+                             const void* s2, int H, int I, uint16_t* h, uint8_t* h_q, float* h_s,
                              uint16_t* o, hipStream_t stream);
 
 hipError_t launch_shared_gemm_bf16(const uint16_t* a, const uint16_t* w, int M, int N, int K,

@@ -33,7 +33,7 @@ __host__ __device__ inline int lds_stride(int I) { return I + kLdsPad; }
 template <int WFMT, int GS>
 __global__ void __launch_bounds__(kThreads, 3)   // >= 3 waves per SIMD
 down_quant_kernel(const uint16_t* h, const int32_t* plan, int E, int R, const uint8_t* w2,
-                  const float* s2, int H, int I, uint8_t* h_q, float* h_s, uint16_t* o) {
+                  const ScaleT<WFMT>* s2, int H, int I, uint8_t* h_q, float* h_s, uint16_t* o) {
   extern __shared__ __align__(16) uint8_t s_codes[];   // [rows][lds_stride(I)] E4M3
   __shared__ float s_scale[kMlpMaxRows];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -76,7 +76,7 @@ down_quant_kernel(const uint16_t* h, const int32_t* plan, int E, int R, const ui
   int col[2];
   unit_columns<MOEQ_EPI_NONE>(H, u, col);
   const uint8_t* wrow[2];
-  const float* srow[2];
+  const ScaleT<WFMT>* srow[2];
   weight_rows<WFMT>(w2, s2, ti.e, H, I, col, ln, wrow, srow);
   const int nrb = (ti.rows + 15) >> 4;
   for (int rb = 0; rb < nrb; ++rb) {
@@ -95,7 +95,8 @@ down_quant_kernel(const uint16_t* h, const int32_t* plan, int E, int R, const ui
 
 template <int WFMT, int GS>
 hipError_t launch_down_quant(const uint16_t* h, const void* plan, int E, int R, const uint8_t* w2,
-                             const float* s2, int H, int I, uint8_t* h_q, float* h_s, uint16_t* o,
+                             const ScaleT<WFMT>* s2, int H, int I, uint8_t* h_q, float* h_s,
+                             uint16_t* o,
                              size_t lds, hipStream_t stream) {
   auto fn = down_quant_kernel<WFMT, GS>;
   hipError_t err;
@@ -111,7 +112,8 @@ hipError_t launch_down_quant(const uint16_t* h, const void* plan, int E, int R, 
 
 template <int WFMT>
 hipError_t launch_down_quant_shape(const uint16_t* h, const void* plan, int E, int R,
-                                   const uint8_t* w2, const float* s2, int H, int I, uint8_t* h_q,
+                                   const uint8_t* w2, const ScaleT<WFMT>* s2, int H, int I,
+                                   uint8_t* h_q,
                                    float* h_s, uint16_t* o, size_t lds, hipStream_t stream) {
   if (I == 2048)
     return launch_down_quant<WFMT, 16>(h, plan, E, R, w2, s2, H, I, h_q, h_s, o, lds, stream);
@@ -121,9 +123,8 @@ hipError_t launch_down_quant_shape(const uint16_t* h, const void* plan, int E, i
 }  // namespace
 
 hipError_t launch_expert_mlp(int wfmt, const uint8_t* xp_q, const float* xp_s, const void* plan,
-                             int E,
-                             int R, const uint8_t* w13, const float* s13, const uint8_t* w2,
-                             const float* s2, int H, int I, uint16_t* h, uint8_t* h_q, float* h_s,
+                             int E, int R, const uint8_t* w13, const void* s13, const uint8_t* w2,
+                             const void* s2, int H, int I, uint16_t* h, uint8_t* h_q, float* h_s,
                              uint16_t* o, hipStream_t stream) {
   if (R == 0) return hipSuccess;
   hipError_t err = launch_grouped_gemm(wfmt, xp_q, xp_s, plan, E, R, w13, s13, 2 * I, H,
@@ -131,12 +132,20 @@ hipError_t launch_expert_mlp(int wfmt, const uint8_t* xp_q, const float* xp_s, c
   if (err != hipSuccess) return err;
   const int max_rows = R < kMlpMaxRows ? R : kMlpMaxRows;     // rows of one tile
   const size_t lds = size_t(max_rows) * lds_stride(I);
-  if (R <= kMlpMaxRows && lds <= kLdsPerWorkgroup)
-    return wfmt == kW4G128
-               ? launch_down_quant_shape<kW4G128>(h, plan, E, R, w2, s2, H, I, h_q, h_s, o, lds,
-                                                  stream)
-               : launch_down_quant_shape<kFp8Row>(h, plan, E, R, w2, s2, H, I, h_q, h_s, o, lds,
-                                                  stream);
+  if (R <= kMlpMaxRows && lds <= kLdsPerWorkgroup) {
+    switch (wfmt) {
+      case kW4G128:
+        return launch_down_quant_shape<kW4G128>(h, plan, E, R, w2, static_cast<const float*>(s2),
+                                                H, I, h_q, h_s, o, lds, stream);
+      case kW4G128Bf16:
+        return launch_down_quant_shape<kW4G128Bf16>(h, plan, E, R, w2,
+                                                    static_cast<const uint16_t*>(s2), H, I, h_q,
+                                                    h_s, o, lds, stream);
+      default:
+        return launch_down_quant_shape<kFp8Row>(h, plan, E, R, w2, static_cast<const float*>(s2),
+                                                H, I, h_q, h_s, o, lds, stream);
+    }
+  }
   if ((err = launch_quant_fp8(h, MOEQ_BF16, R, I, I, h_q, h_s, stream)) != hipSuccess) return err;
   return launch_grouped_gemm(wfmt, h_q, h_s, plan, E, R, w2, s2, H, I, MOEQ_EPI_NONE, o, MOEQ_BF16,
                              stream);

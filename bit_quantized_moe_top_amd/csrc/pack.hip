@@ -2,7 +2,9 @@
 // loads 8 consecutive fp32 weights (32 B), the group's max |w| is reduced over
 // the 16 lanes, s = max/7 (IEEE division), codes = clamp(rne(w / s), -8, 7), and
 // each lane stores its 8 codes as one little-endian 32-bit word of nibbles
-// (code + 8, first code in the least significant nibble).
+// (code + 8, first code in the least significant nibble).  With bfloat16
+// scales the stored scale is bf16(max/7) (RNE) and the codes are taken
+// against that stored value.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -10,9 +12,10 @@ namespace moeq {
 
 namespace {
 
+template <typename ST>
 __global__ void __launch_bounds__(256)
 pack_int4_kernel(const float* __restrict__ w, int64_t n_groups, int groups_per_row,
-                 uint32_t* __restrict__ packed, float* __restrict__ scales) {
+                 uint32_t* __restrict__ packed, ST* __restrict__ scales) {
   const int64_t gid = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   const bool valid = gid < n_groups;
@@ -30,7 +33,14 @@ pack_int4_kernel(const float* __restrict__ w, int64_t n_groups, int groups_per_r
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
   if (!valid) return;
-  const float s = __fdiv_rn(amax, 7.0f);
+  float s = __fdiv_rn(amax, 7.0f);
+  ST stored;
+  if constexpr (sizeof(ST) == 2) {
+    stored = f32_to_bf16(s);
+    s = bf16_to_f32(stored);
+  } else {
+    stored = s;
+  }
   uint32_t word = 0x88888888u;           // all-zero codes
   if (s > 0.0f) {
     word = 0;
@@ -42,26 +52,34 @@ pack_int4_kernel(const float* __restrict__ w, int64_t n_groups, int groups_per_r
     }
   }
   packed[gid * 16 + sub] = word;
-  if (sub == 0) scales[gid] = s;
+  if (sub == 0) scales[gid] = stored;
   (void)groups_per_row;
 }
 
 }  // namespace
 
-hipError_t launch_pack_int4(const float* w, int64_t rows, int K, uint8_t* packed, float* scales,
-                            hipStream_t stream) {
+template <typename ST>
+hipError_t launch_pack(const float* w, int64_t rows, int K, uint8_t* packed, ST* scales,
+                       hipStream_t stream) {
   const int64_t n_groups = rows * (K / 128);
   if (n_groups == 0) return hipSuccess;
   const int64_t kMaxGrid = 0x7FFFFFFF;
   for (int64_t g0 = 0; g0 < n_groups; g0 += kMaxGrid * 16) {
     const int64_t ng = (n_groups - g0 < kMaxGrid * 16) ? (n_groups - g0) : kMaxGrid * 16;
-    hipLaunchKernelGGL(pack_int4_kernel, dim3(unsigned((ng + 15) / 16)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(pack_int4_kernel<ST>, dim3(unsigned((ng + 15) / 16)), dim3(256), 0, stream,
                        w + g0 * 128, ng, K / 128, reinterpret_cast<uint32_t*>(packed + g0 * 64),
                        scales + g0);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+hipError_t launch_pack_int4(const float* w, int64_t rows, int K, uint8_t* packed, void* scales,
+                            int bf16_scales, hipStream_t stream) {
+  if (bf16_scales)
+    return launch_pack(w, rows, K, packed, static_cast<uint16_t*>(scales), stream);
+  return launch_pack(w, rows, K, packed, static_cast<float*>(scales), stream);
 }
 
 }  // namespace moeq

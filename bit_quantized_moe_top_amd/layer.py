@@ -23,12 +23,14 @@ from . import (EPI_NONE, EPI_SILU_MUL, moe_combine, moe_expert_mlp_fp8row, moe_e
 class MoELayer:
     """Routed experts (W4A8 INT4-g128 or row-scaled FP8) plus optional bf16 shared experts.
 
+    weight_format: "w4a8" (INT4 g128, fp32 group scales), "w4a8_bf16s" (INT4
+    g128, bfloat16 group scales) or "fp8row" (E4M3, one fp32 scale per row).
     Weights: w13 [E, 2I, H] (gate rows then up rows), w2 [E, H, I].
     """
 
     def __init__(self, H: int, I: int, E: int, k: int, weight_format: str = "w4a8",
                  renormalize: bool = True, device="cuda"):
-        if weight_format not in ("w4a8", "fp8row"):
+        if weight_format not in ("w4a8", "w4a8_bf16s", "fp8row"):
             raise ValueError(weight_format)
         self.H, self.I, self.E, self.k = H, I, E, k
         self.weight_format = weight_format
@@ -45,9 +47,10 @@ class MoELayer:
 
     def quantize_weights(self, w13_f32: torch.Tensor, w2_f32: torch.Tensor):
         """Quantize fp32 weights on the device with the library's own kernels."""
-        if self.weight_format == "w4a8":
-            self.w13, self.s13 = pack_int4_g128(w13_f32)
-            self.w2, self.s2 = pack_int4_g128(w2_f32)
+        if self.weight_format in ("w4a8", "w4a8_bf16s"):
+            sdt = torch.bfloat16 if self.weight_format == "w4a8_bf16s" else torch.float32
+            self.w13, self.s13 = pack_int4_g128(w13_f32, scale_dtype=sdt)
+            self.w2, self.s2 = pack_int4_g128(w2_f32, scale_dtype=sdt)
         else:
             self.w13, self.s13 = quant_fp8_per_token(w13_f32)
             self.w2, self.s2 = quant_fp8_per_token(w2_f32)
@@ -100,7 +103,7 @@ class MoELayer:
         split_mlp runs the expert MLP as its three separate calls (same results)."""
         T = x.shape[0]
         b = self.buffers(T)
-        w4 = self.weight_format == "w4a8"
+        w4 = self.weight_format != "fp8row"      # INT4 (scale dtype picks the entry point)
         gemm = moe_grouped_gemm_w4a8 if w4 else moe_grouped_gemm_fp8row
         mlp = moe_expert_mlp_w4a8 if w4 else moe_expert_mlp_fp8row
 

@@ -190,6 +190,21 @@ int pack_int4_g128(const float* w, int64_t rows, int K, uint8_t* packed, float* 
                    void* stream);
 
 /*
+ * pack_int4_g128_bf16s -- pack_int4_g128 with bfloat16 group scales.
+ *
+ * The W4A8 card's payload accounting ("wstewart3/Inkling-Small-W4A8-G128",
+ * section 5: the I8 / BF16 / F32 byte totals) implies 16-bit scales in the
+ * exported checkpoint.  Reading implemented: the stored scale is the bfloat16
+ * rounding (RNE) of fp32(max|group| / 7), and the codes are taken against the
+ * stored value:  s = bf16(fp32(a / 7));  c = clamp(rne(fp32(w / s)), -8, 7).
+ *
+ *   w [rows, K] fp32, packed [rows, K/2] bytes (out), scales [rows, K/128] bf16 (out)
+ * Limits: as pack_int4_g128.
+ */
+int pack_int4_g128_bf16s(const float* w, int64_t rows, int K, uint8_t* packed, uint16_t* scales,
+                         void* stream);
+
+/*
  * moe_requant_fp8_fnuz -- row-scaled E4M3FNUZ expert weights to row-scaled OCP
  * E4M3 (offline weight preparation).
  *
@@ -239,6 +254,17 @@ int moe_grouped_gemm_w4a8(const uint8_t* a_q, const float* a_s, const void* plan
                           int epilogue, void* out, int out_dtype, void* stream);
 
 /*
+ * moe_grouped_gemm_w4a8_bf16s -- moe_grouped_gemm_w4a8 with bfloat16 group
+ * scales w_scales [E, N, K/128] (as written by pack_int4_g128_bf16s; the
+ * 16-bit scales the W4A8 card's payload accounting implies, section 5).  Each
+ * scale is widened exactly to fp32 and applied as in moe_grouped_gemm_w4a8.
+ * Limits and errors: as moe_grouped_gemm_w4a8.
+ */
+int moe_grouped_gemm_w4a8_bf16s(const uint8_t* a_q, const float* a_s, const void* plan, int E,
+                                int R, const uint8_t* w_packed, const uint16_t* w_scales, int N,
+                                int K, int epilogue, void* out, int out_dtype, void* stream);
+
+/*
  * moe_grouped_gemm_fp8row -- grouped GEMM with row-scaled FP8 expert weights.
  *
  * Expert weights E4M3 with one fp32 scale per output channel, scale tensor
@@ -285,6 +311,18 @@ int moe_expert_mlp_w4a8(const uint8_t* xp_q, const float* xp_s, const void* plan
  * weights (the moe_grouped_gemm_fp8row arithmetic):
  *   w13 [E, 2I, H] E4M3, w13_scales [E, 2I] fp32; w2 [E, H, I] E4M3, w2_scales [E, H] fp32.
  */
+/*
+ * moe_expert_mlp_w4a8_bf16s -- moe_expert_mlp_w4a8 with bfloat16 group scales
+ * (w13_scales [E, 2I, H/128], w2_scales [E, H, I/128]): exactly the three calls
+ * with moe_grouped_gemm_w4a8_bf16s, bit-identical.  Limits: as
+ * moe_expert_mlp_w4a8.
+ */
+int moe_expert_mlp_w4a8_bf16s(const uint8_t* xp_q, const float* xp_s, const void* plan,
+                              size_t plan_bytes, int E, int R, const uint8_t* w13,
+                              const uint16_t* w13_scales, const uint8_t* w2,
+                              const uint16_t* w2_scales, int H, int I, uint16_t* h, uint8_t* h_q,
+                              float* h_s, uint16_t* o, void* stream);
+
 int moe_expert_mlp_fp8row(const uint8_t* xp_q, const float* xp_s, const void* plan,
                           size_t plan_bytes,
                           int E, int R, const uint8_t* w13, const float* w13_scales,

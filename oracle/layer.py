@@ -323,13 +323,14 @@ def shared_mlp(x, ws13, ws2):
 
 def moe_layer(x, logits, k: int, w13=None, w2=None, bias=None, renormalize=True,
               packed13=None, scales13=None, packed2=None, scales2=None,
-              fp8row=False, ws13=None, ws2=None):
+              fp8row=False, ws13=None, ws2=None, scale_dtype="fp32"):
     """Route -> quantize x -> permute -> gate/up GEMM + SiLU -> quantize h ->
     down GEMM -> combine (+ shared experts).  Returns every intermediate.
 
     Weights are given either full precision (w13 [E, 2I, H], w2 [E, H, I]) and
     quantized here, or already quantized (packed13/scales13, packed2/scales2).
-    With fp8row=True the full-precision weights are quantized row-wise to FP8.
+    With fp8row=True the full-precision weights are quantized row-wise to FP8;
+    scale_dtype "bf16" stores the INT4 group scales as bfloat16.
     """
     x = np.asarray(x)
     T, H = x.shape
@@ -355,8 +356,8 @@ def moe_layer(x, logits, k: int, w13=None, w2=None, bias=None, renormalize=True,
         if packed13 is None:
             c13, c2, sc13, sc2 = {}, {}, {}, {}
             for e in plan["active"]:
-                c13[e], sc13[e] = quantize_int4_g128(w13[e])
-                c2[e], sc2[e] = quantize_int4_g128(w2[e])
+                c13[e], sc13[e] = quantize_int4_g128(w13[e], scale_dtype=scale_dtype)
+                c2[e], sc2[e] = quantize_int4_g128(w2[e], scale_dtype=scale_dtype)
             codes13, codes2 = (lambda e: c13[e]), (lambda e: c2[e])
             sf13, sf2 = (lambda e: sc13[e]), (lambda e: sc2[e])
         else:

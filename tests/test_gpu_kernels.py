@@ -131,17 +131,19 @@ def test_requant_fp8_fnuz(rows, K):
 
 
 # -------------------------------------------------------------- INT4 packing ----
+@pytest.mark.parametrize("scale_dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("shape", [(3, 256, 384), (1, 16, 128), (5, 128, 4096)])
-def test_pack_int4_g128(shape):
+def test_pack_int4_g128(shape, scale_dtype):
     g = torch.Generator().manual_seed(sum(shape))
     w = torch.randn(*shape, generator=g) * 0.02
     w[0, 1, 128 if shape[2] > 128 else 0:][:128] = 0.0       # a zero group
     w[0, 2, :128] = torch.linspace(-7, 7, 128) * 1e-3          # exact ties at +-0.5 steps
-    packed, scales = mq.pack_int4_g128(w.to(_dev()))
+    packed, scales = mq.pack_int4_g128(
+        w.to(_dev()), scale_dtype=torch.bfloat16 if scale_dtype == "bf16" else torch.float32)
     torch.cuda.synchronize()
     rows = shape[0] * shape[1]
-    rp, rs = L.pack_int4_g128(w.reshape(rows, shape[2]).numpy())
-    np.testing.assert_array_equal(scales.cpu().numpy().reshape(rows, -1), rs)
+    rp, rs = L.pack_int4_g128(w.reshape(rows, shape[2]).numpy(), scale_dtype=scale_dtype)
+    np.testing.assert_array_equal(scales.cpu().float().numpy().reshape(rows, -1), rs)
     np.testing.assert_array_equal(packed.cpu().numpy().reshape(rows, -1), rp)
 
 
@@ -297,9 +299,11 @@ def test_w4a8_integer_exact(T, k, E, N, K, hot):
             assert_close(to_np(out), L.silu_mul(ref), rel=4e-3, max_abs_frac=1e-2, what="silu")
 
 
-@pytest.mark.parametrize("fmt", ["w4a8", "fp8row"])
+@pytest.mark.parametrize("fmt", ["w4a8", "fp8row", "w4a8_bf16s"])
 @pytest.mark.parametrize("T,k,E,N,K,hot", [(40, 2, 8, 256, 256, None), (4, 6, 16, 256, 512, None),
-                                           (100, 3, 5, 256, 384, 2), (50, 6, 64, 128, 256, None)])
+                                           (100, 3, 5, 256, 384, 2), (50, 6, 64, 128, 256, None),
+                                           (70, 2, 4, 384, 4096, 1), (100, 3, 6, 512, 2048, 2),
+                                           (4, 6, 24, 512, 4096, None)])
 def test_grouped_gemm_random(fmt, T, k, E, N, K, hot):
     rng = np.random.default_rng(E + N + K + T)
     ids = _case_ids(T, k, E, rng, hot)
@@ -308,10 +312,14 @@ def test_grouped_gemm_random(fmt, T, k, E, N, K, hot):
     x = (rng.standard_normal((R, K)) * rng.uniform(0.1, 10, (R, 1))).astype(np.float32)
     a_q, a_s = L.quant_fp8_per_token(x)
     w = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
-    if fmt == "w4a8":
-        cs = [L.quantize_int4_g128(w[e]) for e in range(E)]
+    ws_t = lambda a: torch.from_numpy(a).to(_dev())  # noqa
+    if fmt in ("w4a8", "w4a8_bf16s"):
+        sdt = "bf16" if fmt == "w4a8_bf16s" else "fp32"
+        cs = [L.quantize_int4_g128(w[e], scale_dtype=sdt) for e in range(E)]
         wq = np.stack([F.pack_int4(c) for c, _ in cs])
         ws = np.stack([s for _, s in cs])
+        if sdt == "bf16":                       # the scales are bf16 values: exact conversion
+            ws_t = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(_dev())  # noqa
         fn = mq.moe_grouped_gemm_w4a8
         ref_fn = lambda: L.w4a8_rows(a_q, a_s, experts, lambda e: cs[e][0], lambda e: cs[e][1])  # noqa
     else:
@@ -322,15 +330,17 @@ def test_grouped_gemm_random(fmt, T, k, E, N, K, hot):
         ref_fn = lambda: L.fp8row_rows(a_q, a_s, experts, lambda e: qs[e][0], lambda e: qs[e][1])  # noqa
     ref = ref_fn()
     dq = lambda a: torch.from_numpy(a).to(_dev())  # noqa
-    out32 = fn(dq(a_q), dq(a_s), plan, dq(wq), dq(ws), epilogue=mq.EPI_NONE, out_dtype=torch.float32)
-    outbf = fn(dq(a_q), dq(a_s), plan, dq(wq), dq(ws), epilogue=mq.EPI_NONE, out_dtype=torch.bfloat16)
-    h = fn(dq(a_q), dq(a_s), plan, dq(wq), dq(ws), epilogue=mq.EPI_SILU_MUL)
+    out32 = fn(dq(a_q), dq(a_s), plan, dq(wq), ws_t(ws), epilogue=mq.EPI_NONE,
+               out_dtype=torch.float32)
+    outbf = fn(dq(a_q), dq(a_s), plan, dq(wq), ws_t(ws), epilogue=mq.EPI_NONE,
+               out_dtype=torch.bfloat16)
+    h = fn(dq(a_q), dq(a_s), plan, dq(wq), ws_t(ws), epilogue=mq.EPI_SILU_MUL)
     torch.cuda.synchronize()
     assert_close(to_np(out32), ref, rel=1e-4, max_abs_frac=1e-4, what="fp32 out")
     assert_close(to_np(outbf), F.bf16_round(ref), what="bf16 out")
     assert_close(to_np(h), L.silu_mul(ref), what="silu_mul")
     # determinism: a second run is bitwise identical
-    h2 = fn(dq(a_q), dq(a_s), plan, dq(wq), dq(ws), epilogue=mq.EPI_SILU_MUL)
+    h2 = fn(dq(a_q), dq(a_s), plan, dq(wq), ws_t(ws), epilogue=mq.EPI_SILU_MUL)
     assert torch.equal(h, h2)
 
 

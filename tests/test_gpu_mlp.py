@@ -35,9 +35,10 @@ def _setup(T, k, E, H, I, fmt, hot, seed):
     plan, xp_q, xp_s = mq.moe_permute(ids, E, x_q, x_s)
     w13 = torch.randn(E, 2 * I, H, device=_dev(), generator=g) * 0.02
     w2 = torch.randn(E, H, I, device=_dev(), generator=g) * 0.02
-    if fmt == "w4a8":
-        q13, s13 = mq.pack_int4_g128(w13)
-        q2, s2 = mq.pack_int4_g128(w2)
+    if fmt in ("w4a8", "w4a8_bf16s"):
+        sdt = torch.bfloat16 if fmt == "w4a8_bf16s" else torch.float32
+        q13, s13 = mq.pack_int4_g128(w13, scale_dtype=sdt)
+        q2, s2 = mq.pack_int4_g128(w2, scale_dtype=sdt)
     else:
         q13, s13 = mq.quant_fp8_per_token(w13)
         q2, s2 = mq.quant_fp8_per_token(w2)
@@ -46,7 +47,7 @@ def _setup(T, k, E, H, I, fmt, hot, seed):
 
 
 def _separate(c, fmt):
-    gemm = mq.moe_grouped_gemm_w4a8 if fmt == "w4a8" else mq.moe_grouped_gemm_fp8row
+    gemm = mq.moe_grouped_gemm_fp8row if fmt == "fp8row" else mq.moe_grouped_gemm_w4a8
     h = gemm(c["xp_q"], c["xp_s"], c["plan"], c["w13"], c["s13"], epilogue=mq.EPI_SILU_MUL)
     h_q, h_s = mq.quant_fp8_per_token(h)
     o = gemm(h_q, h_s, c["plan"], c["w2"], c["s2"], epilogue=mq.EPI_NONE)
@@ -54,11 +55,11 @@ def _separate(c, fmt):
 
 
 def _fused(c, fmt):
-    mlp = mq.moe_expert_mlp_w4a8 if fmt == "w4a8" else mq.moe_expert_mlp_fp8row
+    mlp = mq.moe_expert_mlp_fp8row if fmt == "fp8row" else mq.moe_expert_mlp_w4a8
     return mlp(c["xp_q"], c["xp_s"], c["plan"], c["w13"], c["s13"], c["w2"], c["s2"])
 
 
-@pytest.mark.parametrize("fmt", ["w4a8", "fp8row"])
+@pytest.mark.parametrize("fmt", ["w4a8", "fp8row", "w4a8_bf16s"])
 @pytest.mark.parametrize("T,k,E,H,I,hot", [
     (4, 6, 24, 4096, 2048, None),   # decode shape: the unrolled K sweeps
     (4, 6, 64, 512, 256, None),     # decode-like, looped K sweeps

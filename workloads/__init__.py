@@ -46,7 +46,7 @@ class LayerConfig:
     E: int                 # routed experts
     k: int                 # experts per token
     x_dtype: str           # "f32" or "bf16": dtype of the layer input x
-    weight_format: str     # "w4a8" (INT4 g128) or "fp8row"
+    weight_format: str     # "w4a8" (INT4 g128), "w4a8_bf16s" (bf16 group scales) or "fp8row"
     router: str            # "matmul": logits = x @ Wr^T ; "gaussian": logits ~ N(0,1);
                            # "gumbel_zipf": logits = Gumbel(0,1), bias = -s*ln(rank)
     router_scale: float    # std of the router weights (matmul) -- unused otherwise
