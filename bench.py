@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="weight sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-bf16-scales", action="store_true",
+                    help="skip the decode layer with bfloat16 INT4 group scales")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (a plain copy kernel of known "
                          "size, to scale the memory-traffic counters), then exit")
@@ -336,6 +338,24 @@ def main():
                                        (pres["per_call_us"]["gemm_gate_up"] * 1e-6) / 1e9, 1),
             "per_call_us": {k: round(v, 2) for k, v in pres["per_call_us"].items()},
         }
+    if not args.no_bf16_scales and cfg.name == "decode":
+        import dataclasses
+        bcfg = dataclasses.replace(cfg, weight_format="w4a8_bf16s")
+        bres = time_layer(bcfg, args.sets, args.steps, args.warmup, dev, graph=False)
+        bres.pop("layers")
+        bw13, bw2 = expert_bytes(bcfg)
+        bms = bres["ms_per_step"]
+        out["decode_bf16_scales"] = {
+            "workload": "decode as above with bfloat16 INT4 group scales (the 16-bit scales of "
+                        "the W4A8 checkpoint)",
+            "ms_per_step": round(bms, 5),
+            "weight_bytes_per_step": bres["distinct_mean"] * (bw13 + bw2),
+            "value": round(bres["distinct_mean"] * (bw13 + bw2) / (bms * 1e-3) / 1e9, 1),
+            "unit": "GB/s",
+            "gate_up_gemm_us": round(bres["split_call_us"]["gemm_gate_up"], 2),
+            "per_call_us": {k: round(v, 2) for k, v in bres["per_call_us"].items()},
+        }
+        torch.cuda.empty_cache()
     out["host"] = platform.node()
     print(json.dumps(out), flush=True)
 
