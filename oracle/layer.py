@@ -43,6 +43,18 @@ from .formats import (E4M3_MAX, GROUP, bf16_round, e4m3_decode, e4m3_encode,
 # ----------------------------------------------------------------- a1: routing
 
 
+def router_logits(x, w_router):
+    """Router scores, the linear layer in front of the top-k selection:
+    logits[t, e] = sum_h x[t, h] * Wr[e, h]  ("Inkling-512k-NVFP4-AQLM-hybrid",
+    intro: each token is routed to 6 of the 256 experts by its scores).
+    x [T, H] and Wr [E, H] hold fp32-representable values; the sum is formed in
+    float64 (the kernel accumulates in fp32).  Returns float64 [T, E].
+    """
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    w64 = np.asarray(w_router, dtype=np.float32).astype(np.float64)
+    return x64 @ w64.T
+
+
 def route_topk(logits, k: int, bias=None, renormalize: bool = True):
     """Top-k expert selection and routing weights.
 

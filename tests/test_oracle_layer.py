@@ -37,6 +37,23 @@ def _route_brute(s_row, k):
     return order[:k]
 
 
+def test_router_logits_brute_force_and_integer_case():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((3, 5)).astype(np.float32)
+    w = rng.standard_normal((4, 5)).astype(np.float32)
+    got = L.router_logits(x, w)
+    for t in range(3):
+        for e in range(4):
+            want = sum(float(x[t, h]) * float(w[e, h]) for h in range(5))
+            assert abs(got[t, e] - want) <= 1e-15 * sum(abs(float(x[t, h]) * float(w[e, h]))
+                                                          for h in range(5))
+    xi = rng.integers(-9, 10, (6, 128)).astype(np.float32)          # exact in any order
+    wi = rng.integers(-9, 10, (7, 128)).astype(np.float32)
+    gi = L.router_logits(xi, wi)
+    want = [[sum(int(a) * int(b) for a, b in zip(xi[t], wi[e])) for e in range(7)] for t in range(6)]
+    assert np.array_equal(gi, np.array(want, dtype=np.float64))
+
+
 def test_route_matches_brute_force_sort():
     rng = np.random.default_rng(3)
     for T, E, k in [(7, 8, 2), (5, 16, 6), (4, 256, 6), (3, 5, 5)]:
