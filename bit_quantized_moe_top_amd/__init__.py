@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "LIB_PATH", "lib", "MOEQ_F32", "MOEQ_BF16", "EPI_NONE", "EPI_SILU_MUL", "TILE_M",
     "MAX_EXPERTS", "MAX_TOPK", "MoeqError", "moe_abi_version", "moe_status_string",
-    "moe_plan_size", "moe_route_topk", "quant_fp8_per_token", "moe_permute",
+    "moe_plan_size", "moe_router_logits", "moe_route_topk", "quant_fp8_per_token", "moe_permute",
     "moe_route_quant_permute", "pack_int4_g128", "moe_requant_fp8_fnuz",
     "moe_grouped_gemm_w4a8", "moe_grouped_gemm_w4a8_bf16s", "moe_expert_mlp_w4a8",
     "moe_expert_mlp_w4a8_bf16s", "moe_expert_mlp_fp8row", "pack_int4_g128_bf16s", "moe_grouped_gemm_fp8row", "moe_combine", "moe_shared_gemm_bf16",
@@ -44,6 +44,7 @@ _SIGNATURES = {
     "moe_abi_version": (_I, []),
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_plan_size": (_SZ, [_I, _I]),
+    "moe_router_logits": (_I, [_P, _I, _I, _I, _P, _I, _P, _P]),
     "moe_route_topk": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "quant_fp8_per_token": (_I, [_P, _I, _I64, _I, _I64, _P, _P, _P]),
     "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _P, _SZ, _P]),
@@ -139,6 +140,25 @@ def plan_fields(plan: torch.Tensor, E: int, R: int) -> dict:
 
 
 # ----------------------------------------------------------------------- calls
+def moe_router_logits(x: torch.Tensor, w_router: torch.Tensor,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x [T, H] fp32/bf16, w_router [E, H] fp32 -> logits [T, E] fp32 = x . w_router^T."""
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _req(x, "x", x.dtype, 2)
+    _req(w_router, "w_router", torch.float32, 2)
+    T, H = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != H:
+        raise ValueError("w_router must be [E, H]")
+    if out is None:
+        out = torch.empty(T, E, dtype=torch.float32, device=x.device)
+    dt = MOEQ_BF16 if x.dtype == torch.bfloat16 else MOEQ_F32
+    _check("moe_router_logits", lib.moe_router_logits(_ptr(x), dt, T, H, _ptr(w_router), E,
+                                                      _ptr(out), _stream(x.device)))
+    return out
+
+
 def moe_route_topk(logits: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None,
                    renormalize: bool = True, ids: Optional[torch.Tensor] = None,
                    weights: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:

@@ -65,6 +65,21 @@ int moe_route_topk(const float* logits, const float* bias, int T, int E, int k, 
                                                topk_w, as_stream(stream)));
 }
 
+int moe_router_logits(const void* x, int x_dtype, int T, int H, const float* w_router, int E,
+                      float* logits, void* stream) {
+  if (T < 0 || H <= 0 || E <= 0) return MOEQ_ERR_INVALID_ARG;
+  if (x_dtype != MOEQ_F32 && x_dtype != MOEQ_BF16) return MOEQ_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !w_router || !logits)) return MOEQ_ERR_INVALID_ARG;
+  if (H % 16 != 0) return MOEQ_ERR_UNSUPPORTED;
+  if (int64_t(T) * E > 0x7FFFFFFF || int64_t(E) * H > 0x7FFFFFFF) return MOEQ_ERR_UNSUPPORTED;
+  if (T > 0 && (!aligned16(x) || !aligned16(w_router) || (reinterpret_cast<uintptr_t>(logits) & 3u)))
+    return MOEQ_ERR_INVALID_ARG;
+  if (T == 0) return MOEQ_OK;
+  if (int rc = check_device()) return rc;
+  return launch_status(
+      moeq::launch_router_logits(x, x_dtype, T, H, w_router, E, logits, as_stream(stream)));
+}
+
 int quant_fp8_per_token(const void* x, int x_dtype, int64_t M, int K, int64_t ld_x, uint8_t* q,
                         float* scale, void* stream) {
   if (M < 0 || K <= 0 || ld_x < K) return MOEQ_ERR_INVALID_ARG;

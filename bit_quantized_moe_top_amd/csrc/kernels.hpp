@@ -56,6 +56,9 @@ __host__ __device__ inline size_t plan_words(int E, int R) {
          2 * size_t(plan_max_tiles(E, R)) + size_t(plan_chunks(R)) * size_t(E);
 }
 
+// logits [T, E] = x [T, H] (fp32 or bf16) . Wr [E, H]^T, fp32 accumulation
+hipError_t launch_router_logits(const void* x, int x_dtype, int T, int H, const float* wr, int E,
+                                float* logits, hipStream_t stream);
 hipError_t launch_route_topk(const float* logits, const float* bias, int T, int E, int k,
                              int renormalize, int32_t* ids, float* w, hipStream_t stream);
 

@@ -1,8 +1,9 @@
 """One quantized MoE expert layer as a fixed sequence of libmoeq calls.
 
-    route + quantize x + permute (one call)
+    [router logits, when the layer holds the router weights]
+      -> route + quantize x + permute (one call; one launch for T <= 16)
       -> expert MLP: gate/up GEMM (+SiLU) -> quantize h -> down GEMM (one call;
-         a single launch for decode-sized batches)
+         two launches for decode-sized batches)
       -> combine (+ shared experts)
 
 Only orchestration lives here: buffers are torch allocations, reused across
@@ -16,7 +17,7 @@ import torch
 
 from . import (EPI_NONE, EPI_SILU_MUL, moe_combine, moe_expert_mlp_fp8row, moe_expert_mlp_w4a8,
                moe_grouped_gemm_fp8row, moe_grouped_gemm_w4a8, moe_plan_size,
-               moe_requant_fp8_fnuz, moe_route_quant_permute, moe_shared_gemm_bf16, pack_int4_g128,
+               moe_requant_fp8_fnuz, moe_route_quant_permute, moe_router_logits, moe_shared_gemm_bf16, pack_int4_g128,
                quant_fp8_per_token)
 
 
@@ -38,6 +39,7 @@ class MoELayer:
         self.device = torch.device(device)
         self.w13 = self.s13 = self.w2 = self.s2 = None
         self.ws13 = self.ws2 = None
+        self.w_router = None
         self._bufs = {}
 
     # --------------------------------------------------------------- weights
@@ -64,6 +66,11 @@ class MoELayer:
         self.w13, self.s13 = moe_requant_fp8_fnuz(w13_fnuz, s13_fnuz)
         self.w2, self.s2 = moe_requant_fp8_fnuz(w2_fnuz, s2_fnuz)
 
+    def set_router(self, w_router: Optional[torch.Tensor]):
+        """fp32 router weights [E, H]; forward() then takes logits=None and computes
+        them with moe_router_logits."""
+        self.w_router = w_router
+
     def set_shared(self, ws13: Optional[torch.Tensor], ws2: Optional[torch.Tensor]):
         self.ws13, self.ws2 = ws13, ws2
 
@@ -74,6 +81,7 @@ class MoELayer:
             H, I, E, k, d = self.H, self.I, self.E, self.k, self.device
             R = T * k
             b = {
+                "logits": torch.empty(T, E, dtype=torch.float32, device=d),
                 "ids": torch.empty(T, k, dtype=torch.int32, device=d),
                 "w": torch.empty(T, k, dtype=torch.float32, device=d),
                 "x_q": torch.empty(T, H, dtype=torch.uint8, device=d),
@@ -95,10 +103,12 @@ class MoELayer:
         return b
 
     # ---------------------------------------------------------------- forward
-    def forward(self, x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor] = None,
+    def forward(self, x: torch.Tensor, logits: Optional[torch.Tensor] = None,
+                bias: Optional[torch.Tensor] = None,
                 return_all: bool = False, events: Optional[list] = None,
                 split_mlp: bool = False):
-        """y = layer(x).  With `events` (a list), each call is bracketed by a pair of
+        """y = layer(x).  logits=None: the router's logits are computed from x and the
+        weights given to set_router.  With `events` (a list), each call is bracketed by a pair of
         timing events on the current stream, appended as (name, start, end).
         split_mlp runs the expert MLP as its three separate calls (same results)."""
         T = x.shape[0]
@@ -117,6 +127,10 @@ class MoELayer:
             events.append((name, s, e))
             return r
 
+        if logits is None:
+            if self.w_router is None:
+                raise ValueError("logits=None needs router weights (set_router)")
+            logits = step("router", moe_router_logits, x, self.w_router, out=b["logits"])
         step("route_quant_permute", moe_route_quant_permute, logits, x, self.k, bias,
              self.renormalize, out=b)
         if split_mlp:

@@ -92,6 +92,22 @@ const char* moe_status_string(int status);
 size_t moe_plan_size(int E, int R);
 
 /*
+ * moe_router_logits -- the router's linear layer, the step in front of the
+ * top-k selection: logits[t, e] = sum_h x[t, h] * w_router[e, h].
+ *
+ * Each token is routed by its scores over the experts ("Inkling-512k-NVFP4-
+ * AQLM-hybrid", intro: 6 of 256 routed experts per token); the pages do not
+ * give the router's precision, the reading implemented is fp32 weights and
+ * fp32 accumulation (fused multiply-adds; bf16 x is widened exactly).  A bias,
+ * if any, is added by moe_route_topk.
+ *
+ *   x [T, H] fp32 or bf16 (x_dtype)   w_router [E, H] fp32   logits [T, E] fp32 (out)
+ * Limits: T >= 0, H % 16 == 0, T*E and E*H < 2^31; x and w_router 16-byte aligned.
+ */
+int moe_router_logits(const void* x, int x_dtype, int T, int H, const float* w_router, int E,
+                      float* logits, void* stream);
+
+/*
  * moe_route_topk -- top-k routing.
  *
  * Inkling routes each token to 6 of its 256 routed experts

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     assert set(names) == set(mq.EXPORTED_SYMBOLS)
 
 
@@ -62,6 +62,12 @@ def test_argument_errors_are_reported_without_a_gpu():
     assert L.moe_route_topk(FAKE, N, 1, 2048, 2, 1, FAKE, FAKE, N) == UNSUPPORTED  # E > 1024
     assert L.moe_route_topk(FAKE, N, 1, 64, 9, 1, FAKE, FAKE, N) == UNSUPPORTED    # k > 8
     assert L.moe_route_topk(N, N, 0, 8, 2, 1, N, N, N) == OK                        # empty
+    # router logits
+    assert L.moe_router_logits(FAKE, 1, 4, 24, FAKE, 8, FAKE, N) == UNSUPPORTED        # H % 16
+    assert L.moe_router_logits(FAKE, 5, 4, 32, FAKE, 8, FAKE, N) == INVALID            # dtype
+    assert L.moe_router_logits(N, 1, 4, 32, FAKE, 8, FAKE, N) == INVALID               # null x
+    assert L.moe_router_logits(ctypes.c_void_p(4100), 1, 4, 32, FAKE, 8, FAKE, N) == INVALID
+    assert L.moe_router_logits(N, 1, 0, 32, N, 8, N, N) == OK                           # T = 0
     # quant
     assert L.quant_fp8_per_token(FAKE, 1, 4, 12, 12, FAKE, FAKE, N) == UNSUPPORTED  # K % 8
     assert L.quant_fp8_per_token(FAKE, 7, 4, 16, 16, FAKE, FAKE, N) == INVALID      # dtype

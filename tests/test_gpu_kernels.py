@@ -21,6 +21,37 @@ def _dev():
     return torch.device("cuda:0")
 
 
+# ------------------------------------------------------------- router logits ----
+@pytest.mark.parametrize("T,H,E,dtype", [(4, 4096, 256, torch.bfloat16), (16, 4096, 256, torch.float32),
+                                         (17, 4096, 256, torch.bfloat16), (130, 528, 100, torch.float32),
+                                         (1, 16, 1, torch.float32), (2048, 4096, 256, torch.bfloat16)])
+def test_router_logits(T, H, E, dtype):
+    g = torch.Generator().manual_seed(T + H + E)
+    x = torch.randn(T, H, generator=g).to(dtype)
+    w = torch.randn(E, H, generator=g) / 64
+    lg = mq.moe_router_logits(x.to(_dev()), w.to(_dev()))
+    torch.cuda.synchronize()
+    x64, w64 = x.float().numpy(), w.numpy()
+    ref = L.router_logits(x64, w64)
+    # fp32 accumulation of H products (fused multiply-adds, any order):
+    # |err| <= gamma_H * sum_h |x w|, gamma_H = H u / (1 - H u), u = 2^-24
+    u = 2.0 ** -24
+    bound = (H * u / (1 - H * u)) * (np.abs(x64).astype(np.float64) @ np.abs(w64).astype(np.float64).T)
+    err = np.abs(lg.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= bound), float((err / np.maximum(bound, 1e-300)).max())
+    # the ids the GPU routes to from its own logits equal the oracle's wherever
+    # the oracle's top-(k+1) scores are separated by more than twice the bound
+    k = min(6, E)
+    ids, _ = mq.moe_route_topk(lg, k)
+    torch.cuda.synchronize()
+    rid, _ = L.route_topk(ref, k)
+    srt = -np.sort(-ref, axis=1)[:, :k + 1]
+    gaps = -np.diff(srt, axis=1).min(axis=1) if k < E else np.full(T, np.inf)
+    clear = gaps > 2 * bound.max(axis=1)
+    assert clear.mean() > 0.9
+    np.testing.assert_array_equal(ids.cpu().numpy()[clear], rid[clear])
+
+
 # ------------------------------------------------------------------ routing ----
 @pytest.mark.parametrize("T,E,k", [(37, 256, 6), (16, 8, 2), (5, 1000, 8), (9, 8, 8), (64, 384, 1),
                                    (3, 64, 6)])

@@ -31,7 +31,7 @@ import torch
 
 __all__ = [
     "LayerConfig", "CONFIGS", "get_config", "tensor_seed", "make_activations",
-    "make_router", "expert_weight", "iter_expert_weights", "make_shared_weights",
+    "router_weights", "make_router", "expert_weight", "iter_expert_weights", "make_shared_weights",
     "make_layer_inputs",
 ]
 
@@ -111,17 +111,24 @@ def make_activations(cfg: LayerConfig, device="cpu") -> torch.Tensor:
     return x.to(torch.bfloat16) if cfg.x_dtype == "bf16" else x
 
 
+def router_weights(cfg: LayerConfig, device="cpu") -> torch.Tensor:
+    """The router matrix Wr [E, H] fp32 of a "matmul" router workload."""
+    g = _gen(device, cfg.seed, "router")
+    wr = torch.randn(cfg.E, cfg.H, generator=g, device=device, dtype=torch.float32)
+    return wr * cfg.router_scale
+
+
 def make_router(cfg: LayerConfig, x: torch.Tensor) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Router logits [T, E] fp32 and an optional per-expert bias [E] fp32.
 
     The router projection that produces the logits is the step *before* the
-    expert layer; it is done here, once, so both sides receive identical logits.
+    expert layer; it is done here, once (torch fp32 matmul), so both sides
+    receive identical logits.  Tests of the library's own router projection
+    (moe_router_logits) take router_weights instead.
     """
     device = x.device
     if cfg.router == "matmul":
-        g = _gen(device, cfg.seed, "router")
-        wr = torch.randn(cfg.E, cfg.H, generator=g, device=device, dtype=torch.float32)
-        wr = wr * cfg.router_scale
+        wr = router_weights(cfg, device)
         logits = torch.matmul(x.to(torch.float32), wr.t()).contiguous()
         return logits, None
     if cfg.router == "gaussian":
