@@ -9,6 +9,10 @@
   (bias 8), 3 mantissa bits; no infinities and no negative zero; 0x80 is the
   only NaN; largest finite magnitude 240 (0x7F).  Read only, to convert such
   checkpoints to OCP E4M3.
+* E2M1 (FP4, the NVFP4 element format of the hot experts in
+  "Inkling-512k-NVFP4-AQLM-hybrid", "Dequant math"): the 16 codes decode to
+  [0, .5, 1, 1.5, 2, 3, 4, 6, -0, -.5, -1, -1.5, -2, -3, -4, -6]; two codes per
+  byte, the low nibble first.
 * bfloat16: the top 16 bits of an IEEE binary32.
 * INT4: signed codes in [-8, 7] stored as nibble = code + 8, eight consecutive
   codes per little-endian 32-bit word with the first code in the least
@@ -94,6 +98,32 @@ def e4m3fnuz_decode(codes) -> np.ndarray:
     val = np.where(s == 1, -mag, mag)
     val = np.where(c == 0x80, np.nan, val)
     return val.astype(np.float64)
+
+
+E2M1_VALUES = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6],
+                       dtype=np.float64)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """Value of each 4-bit E2M1 code 0..15 (float64), by the card's table."""
+    return E2M1_VALUES[np.asarray(codes, dtype=np.int64) & 0xF]
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    """Bytes [..., K/2] -> codes [..., K], low nibble first (the card's order)."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def pack_fp4(codes) -> np.ndarray:
+    """Codes [..., K] (0..15) -> bytes [..., K/2], the first code in the low nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if c.shape[-1] % 2 or (c > 15).any():
+        raise ValueError("codes must be 0..15 with an even count")
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
 
 
 def fp32(v) -> np.ndarray:

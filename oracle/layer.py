@@ -37,8 +37,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import (E4M3_MAX, GROUP, bf16_round, e4m3_decode, e4m3_encode,
-                      e4m3fnuz_decode, fp32, pack_int4, unpack_int4)
+from .formats import (E4M3_MAX, GROUP, bf16_round, e2m1_decode, e4m3_decode, e4m3_encode,
+                      e4m3fnuz_decode, fp32, pack_int4, unpack_fp4, unpack_int4)
 
 # ----------------------------------------------------------------- a1: routing
 
@@ -283,6 +283,32 @@ def fp8row_rows(a_q, a_s, experts, wq_of, srow_of):
     return out
 
 # ------------------------------------------------------ a4 epilogue: SwiGLU
+
+
+def nvfp4_dequant(packed, block_scale, scale2):
+    """NVFP4 hot-expert weights ("Inkling-512k-NVFP4-AQLM-hybrid", "Dequant math",
+    hot): W = LUT[code] * scale[block of 16 along K] * scale2, with packed
+    [N, K/2] codes (low nibble first), block_scale [N, K/16] E4M3 bytes and the
+    per-expert fp32 scale2.  Exact in float64."""
+    codes = unpack_fp4(packed)
+    bs = e4m3_decode(block_scale)
+    return e2m1_decode(codes) * np.repeat(bs, 16, axis=-1) * float(np.float32(scale2))
+
+
+def nvfp4_rows(a_q, a_s, experts, packed_of, bscale_of, scale2_of):
+    """out[p, n] = a_s[p] * sum_k E4M3(a_q[p, k]) * W_e[n, k] with W_e the NVFP4
+    weights of row p's expert (nvfp4_dequant), float64; products exact."""
+    a = e4m3_decode(a_q)
+    R = a.shape[0]
+    out = None
+    for e in np.unique(experts):
+        rows = np.nonzero(experts == e)[0]
+        w = nvfp4_dequant(packed_of(e), bscale_of(e), scale2_of(e))
+        blk = (a[rows] @ w.T) * np.asarray(a_s, dtype=np.float64)[rows, None]
+        if out is None:
+            out = np.zeros((R, w.shape[0]), dtype=np.float64)
+        out[rows] = blk
+    return out if out is not None else np.zeros((R, 0))
 
 
 def silu(z):

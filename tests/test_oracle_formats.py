@@ -63,6 +63,28 @@ def test_e4m3fnuz_is_half_of_ocp_on_shared_finite_codes():
     assert np.array_equal(F.e4m3fnuz_decode(codes) * 2.0, F.e4m3_decode(codes))
 
 
+def test_e2m1_table_matches_the_format_definition():
+    # E2M1 (OCP microscaling formats): 1 sign, 2 exponent bits (bias 1), 1 mantissa
+    # bit; normal 2^(e-1) (1 + m/2), subnormal (e = 0) m/2 -- independent of the
+    # card's table that the oracle uses
+    for c in range(16):
+        s, e, m = c >> 3, (c >> 1) & 3, c & 1
+        v = 2.0 ** (e - 1) * (1 + m / 2) if e else m / 2
+        v = -v if s else v
+        got = F.e2m1_decode([c])[0]
+        assert got == v and np.signbit(got) == bool(s), c
+
+
+def test_fp4_packing_low_nibble_first():
+    # the card: "low nibble is the first weight of each pair"
+    assert F.unpack_fp4(np.array([[0x21, 0xF8]], dtype=np.uint8)).tolist() == [[1, 2, 8, 15]]
+    rng = np.random.default_rng(31)
+    c = rng.integers(0, 16, (5, 64)).astype(np.uint8)
+    assert np.array_equal(F.unpack_fp4(F.pack_fp4(c)), c)
+    with pytest.raises(ValueError):
+        F.pack_fp4(np.array([16, 0], dtype=np.uint8))
+
+
 def test_e4m3_roundtrip_every_finite_code():
     codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
     assert len(codes) == 254

@@ -337,6 +337,40 @@ def test_requant_fnuz_error_bound():
     assert np.all(np.abs(back - w) <= bound)
 
 
+def test_nvfp4_dequant_hand_example():
+    # one row of 32 codes: block 0 scale 0x38 (1.0), block 1 scale 0x41 (2.25),
+    # scale2 0.5: W = LUT[c] * block scale * 0.5
+    codes = np.array([[1, 7, 15, 0] + [4] * 12 + [3, 9] + [2] * 14], dtype=np.uint8)
+    w = L.nvfp4_dequant(F.pack_fp4(codes), np.array([[0x38, 0x41]], dtype=np.uint8), 0.5)
+    assert w[0, :4].tolist() == [0.25, 3.0, -3.0, 0.0]
+    assert w[0, 4] == 1.0                             # code 4 = 2.0 -> 2 * 1 * 0.5
+    assert w[0, 16] == 1.5 * 2.25 * 0.5 and w[0, 17] == -0.5 * 2.25 * 0.5
+    assert w[0, 18] == 1.0 * 2.25 * 0.5
+
+
+def test_nvfp4_rows_brute_force():
+    rng = np.random.default_rng(32)
+    E, N, K, R = 2, 3, 32, 4
+    codes = rng.integers(0, 16, (E, N, K)).astype(np.uint8)
+    bs = rng.integers(0x28, 0x48, (E, N, K // 16)).astype(np.uint8)
+    s2 = np.array([0.25, 0.125], dtype=np.float32)
+    a_q = F.e4m3_encode(rng.standard_normal((R, K)))
+    a_s = np.array([1.0, 0.5, 2.0, 0.75], dtype=np.float32)
+    experts = np.array([0, 0, 1, 1])
+    got = L.nvfp4_rows(a_q, a_s, experts, lambda e: F.pack_fp4(codes[e]), lambda e: bs[e],
+                       lambda e: s2[e])
+    tab = [0, .5, 1, 1.5, 2, 3, 4, 6]
+    for p in range(R):
+        e = experts[p]
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                c = int(codes[e, n, k])
+                wv = (-1 if c >= 8 else 1) * tab[c & 7] * float(F.e4m3_decode([bs[e, n, k // 16]])[0])
+                acc += float(F.e4m3_decode([a_q[p, k]])[0]) * wv
+            assert got[p, n] == pytest.approx(float(a_s[p]) * float(s2[e]) * acc, rel=1e-12, abs=1e-300)
+
+
 def test_silu_closed_forms():
     z = np.linspace(-30, 30, 1001)
     np.testing.assert_allclose(L.silu(z), z * scipy.special.expit(z), rtol=1e-14, atol=1e-300)
