@@ -21,7 +21,8 @@ __all__ = [
     "MAX_EXPERTS", "MAX_TOPK", "MoeqError", "moe_abi_version", "moe_status_string",
     "moe_plan_size", "moe_router_logits", "moe_route_topk", "quant_fp8_per_token", "moe_permute",
     "moe_route_quant_permute", "pack_int4_g128", "moe_requant_fp8_fnuz",
-    "moe_grouped_gemm_w4a8", "moe_grouped_gemm_w4a8_bf16s", "moe_expert_mlp_w4a8",
+    "moe_grouped_gemm_w4a8", "moe_grouped_gemm_w4a8_bf16s", "moe_grouped_gemm_nvfp4",
+    "moe_expert_mlp_w4a8",
     "moe_expert_mlp_w4a8_bf16s", "moe_expert_mlp_fp8row", "pack_int4_g128_bf16s", "moe_grouped_gemm_fp8row", "moe_combine", "moe_shared_gemm_bf16",
     "plan_fields", "EXPORTED_SYMBOLS",
 ]
@@ -56,6 +57,7 @@ _SIGNATURES = {
     "moe_grouped_gemm_w4a8": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_grouped_gemm_fp8row": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_grouped_gemm_w4a8_bf16s": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
+    "moe_grouped_gemm_nvfp4": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_expert_mlp_w4a8": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P,
                                  _P]),
     "moe_expert_mlp_w4a8_bf16s": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P,
@@ -338,6 +340,35 @@ def moe_grouped_gemm_w4a8_bf16s(a_q, a_s, plan, w_packed, w_scales, epilogue: in
     """moe_grouped_gemm_w4a8 with bfloat16 group scales w_scales [E, N, K/128]."""
     _req(w_scales, "w_scales", torch.bfloat16, 3)
     return moe_grouped_gemm_w4a8(a_q, a_s, plan, w_packed, w_scales, epilogue, out_dtype, out)
+
+
+def moe_grouped_gemm_nvfp4(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Tensor,
+                           w_fp4: torch.Tensor, w_block_scale: torch.Tensor,
+                           w_scale2: torch.Tensor, epilogue: int = EPI_NONE,
+                           out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """w_fp4 [E, N, K/2] uint8 (E2M1 pairs), w_block_scale [E, N, K/16] uint8 (E4M3),
+    w_scale2 [E] fp32."""
+    _req(a_q, "a_q", torch.uint8, 2)
+    _req(a_s, "a_s", torch.float32, 1)
+    _req(plan, "plan", torch.int32, 1)
+    _req(w_fp4, "w_fp4", torch.uint8, 3)
+    _req(w_block_scale, "w_block_scale", torch.uint8, 3)
+    _req(w_scale2, "w_scale2", torch.float32, 1)
+    E, N, K2 = w_fp4.shape
+    K = 2 * K2
+    if tuple(w_block_scale.shape) != (E, N, K // 16) or tuple(w_scale2.shape) != (E,):
+        raise ValueError("w_block_scale / w_scale2 shapes do not match w_fp4")
+    R = a_q.shape[0]
+    if a_q.shape[1] != K:
+        raise ValueError("a_q has the wrong K")
+    n_out = N // 2 if epilogue == EPI_SILU_MUL else N
+    if out is None:
+        out = torch.empty(R, n_out, dtype=out_dtype, device=a_q.device)
+    odt = MOEQ_BF16 if out.dtype == torch.bfloat16 else MOEQ_F32
+    _check("moe_grouped_gemm_nvfp4", lib.moe_grouped_gemm_nvfp4(
+        _ptr(a_q), _ptr(a_s), _ptr(plan), E, R, _ptr(w_fp4), _ptr(w_block_scale), _ptr(w_scale2),
+        N, K, epilogue, _ptr(out), odt, _stream(a_q.device)))
+    return out
 
 
 def moe_grouped_gemm_fp8row(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Tensor,

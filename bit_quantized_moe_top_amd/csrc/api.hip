@@ -201,6 +201,28 @@ int moe_grouped_gemm_w4a8_bf16s(const uint8_t* a_q, const float* a_s, const void
                      out, out_dtype, stream);
 }
 
+int moe_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
+                           const uint8_t* w_fp4, const uint8_t* w_block_scale,
+                           const float* w_scale2, int N, int K, int epilogue, void* out,
+                           int out_dtype, void* stream) {
+  if (R < 0 || E <= 0 || N <= 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;
+  if (epilogue != MOEQ_EPI_NONE && epilogue != MOEQ_EPI_SILU_MUL) return MOEQ_ERR_INVALID_ARG;
+  if (out_dtype != MOEQ_F32 && out_dtype != MOEQ_BF16) return MOEQ_ERR_INVALID_ARG;
+  if (epilogue == MOEQ_EPI_SILU_MUL && out_dtype != MOEQ_BF16) return MOEQ_ERR_INVALID_ARG;
+  if (E > MOEQ_MAX_EXPERTS) return MOEQ_ERR_UNSUPPORTED;
+  if (K % 128 != 0 || N % 128 != 0) return MOEQ_ERR_UNSUPPORTED;
+  if (int64_t(N / 32) * moeq::plan_max_tiles(E, R) > 0x7FFFFFF0) return MOEQ_ERR_UNSUPPORTED;
+  if (R > 0 && (!a_q || !a_s || !plan || !w_fp4 || !w_block_scale || !w_scale2 || !out))
+    return MOEQ_ERR_INVALID_ARG;
+  if (R > 0 && (!aligned16(a_q) || !aligned16(w_fp4) || !aligned16(w_block_scale)))
+    return MOEQ_ERR_INVALID_ARG;
+  if (R == 0) return MOEQ_OK;
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_grouped_gemm_nvfp4(a_q, a_s, plan, E, R, w_fp4, w_block_scale,
+                                                       w_scale2, N, K, epilogue, out, out_dtype,
+                                                       as_stream(stream)));
+}
+
 int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
                             const uint8_t* w_fp8, const float* w_row_scale, int N, int K,
                             int epilogue, void* out, int out_dtype, void* stream) {

@@ -86,6 +86,8 @@ template <int WFMT>
 struct ScaleOf { using type = float; };
 template <>
 struct ScaleOf<kW4G128Bf16> { using type = uint16_t; };
+template <>
+struct ScaleOf<kNvfp4> { using type = uint8_t; };      // E4M3 block scales
 template <int WFMT>
 using ScaleT = typename ScaleOf<WFMT>::type;
 
@@ -249,7 +251,10 @@ __device__ __forceinline__ void weight_rows(const uint8_t* w, const ScaleT<WFMT>
 template <int WFMT, int NB = 2>
 __device__ __forceinline__ void row_scales(const ScaleT<WFMT>* const (&srow)[NB], float (&rs)[NB]) {
 #pragma unroll
-  for (int j = 0; j < NB; ++j) rs[j] = (WFMT == kFp8Row) ? scale_value(srow[j][0]) : 1.0f;
+  for (int j = 0; j < NB; ++j) {
+    if constexpr (WFMT == kFp8Row) rs[j] = scale_value(srow[j][0]);
+    else rs[j] = 1.0f;
+  }
 }
 
 // SiLU-gated product of result row v (gate block 0, up block 1) as bf16

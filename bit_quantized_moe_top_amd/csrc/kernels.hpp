@@ -81,11 +81,18 @@ hipError_t launch_pack_int4(const float* w, int64_t rows, int K, uint8_t* packed
 
 // weight formats of the grouped GEMM: INT4 g128 with fp32 or bf16 group scales,
 // row-scaled E4M3 (fp32 row scales); w_scale points to scales of that type
-enum WeightFormat { kW4G128 = 0, kFp8Row = 1, kW4G128Bf16 = 2 };
+enum WeightFormat { kW4G128 = 0, kFp8Row = 1, kW4G128Bf16 = 2, kNvfp4 = 3 };
 
 hipError_t launch_grouped_gemm(int wfmt, const uint8_t* a_q, const float* a_s, const void* plan,
                                int E, int R, const uint8_t* w, const void* w_scale, int N, int K,
                                int epilogue, void* out, int out_dtype, hipStream_t stream);
+
+// NVFP4 weights: E2M1 codes [E, N, K/2], E4M3 block-16 scales [E, N, K/16], fp32
+// per-expert scale2 [E]
+hipError_t launch_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* plan, int E,
+                                     int R, const uint8_t* w, const uint8_t* w_block_scale,
+                                     const float* w_scale2, int N, int K, int epilogue, void* out,
+                                     int out_dtype, hipStream_t stream);
 
 // E is read from the plan header on the device.
 hipError_t launch_combine(const uint16_t* o, const void* plan, const float* w,

@@ -281,6 +281,30 @@ int moe_grouped_gemm_w4a8_bf16s(const uint8_t* a_q, const float* a_s, const void
                                 int K, int epilogue, void* out, int out_dtype, void* stream);
 
 /*
+ * moe_grouped_gemm_nvfp4 -- grouped GEMM over NVFP4 expert weights (the hot
+ * experts of the NVFP4 + AQLM hybrid checkpoint) with per-token FP8 activations.
+ *
+ * Weight format ("Inkling-512k-NVFP4-AQLM-hybrid", "On-disk tensor format" and
+ * "Dequant math", hot): E2M1 codes two per byte, the low nibble the first
+ * weight; one E4M3 scale per 16 consecutive input channels; one fp32 scale2
+ * per expert:  W[e, n, k] = e2m1(code) * e4m3(w_block_scale[e, n, k/16]) * w_scale2[e].
+ * For sorted row p of expert e (per the plan):
+ *   v[p, n] = a_s[p] * w_scale2[e] * sum_k E4M3(a_q[p, k]) * e2m1(c[e, n, k]) * s_b[e, n, k/16]
+ * with exact products and fp32 accumulation; epilogue and out as in
+ * moe_grouped_gemm_w4a8.  The activation format is this library's per-token
+ * FP8 (the card quantizes only the weights; the reading used here keeps the
+ * layer's activation path).
+ *
+ *   w_fp4 [E, N, K/2] bytes, w_block_scale [E, N, K/16] E4M3 bytes, w_scale2 [E] fp32
+ * Limits: K % 128 == 0, N % 128 == 0, 1 <= E <= MOEQ_MAX_EXPERTS; a_q, w_fp4 and
+ * w_block_scale 16-byte aligned.
+ */
+int moe_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
+                           const uint8_t* w_fp4, const uint8_t* w_block_scale,
+                           const float* w_scale2, int N, int K, int epilogue, void* out,
+                           int out_dtype, void* stream);
+
+/*
  * moe_grouped_gemm_fp8row -- grouped GEMM with row-scaled FP8 expert weights.
  *
  * Expert weights E4M3 with one fp32 scale per output channel, scale tensor

@@ -375,6 +375,60 @@ def test_grouped_gemm_random(fmt, T, k, E, N, K, hot):
     assert torch.equal(h, h2)
 
 
+# ------------------------------------------------------------- NVFP4 experts ----
+def _nvfp4_case(T, k, E, N, K, hot, seed, pow2_scales=False):
+    rng = np.random.default_rng(seed)
+    ids = _case_ids(T, k, E, rng, hot)
+    plan, experts = _plan_and_experts(ids, E)
+    codes = rng.integers(0, 16, (E, N, K)).astype(np.uint8)
+    if pow2_scales:                                   # 2^-3 .. 2^2 (E4M3 0x20 .. 0x48, m = 0)
+        bs = (rng.integers(4, 10, (E, N, K // 16)) * 8).astype(np.uint8)
+        s2 = np.ones(E, np.float32)
+    else:
+        bs = rng.integers(0x20, 0x50, (E, N, K // 16)).astype(np.uint8)
+        s2 = (rng.random(E) * 0.02 + 1e-3).astype(np.float32)
+    return rng, plan, experts, codes, F.pack_fp4(codes), bs, s2
+
+
+@pytest.mark.parametrize("T,k,E,N,K,hot", [(4, 6, 16, 256, 512, None), (40, 2, 8, 384, 256, 1),
+                                           (100, 3, 6, 512, 2048, 2), (4, 6, 8, 128, 6144, None)])
+def test_nvfp4_gemm_random(T, k, E, N, K, hot):
+    rng, plan, experts, codes, packed, bs, s2 = _nvfp4_case(T, k, E, N, K, hot, N + K + T)
+    R = T * k
+    x = (rng.standard_normal((R, K)) * rng.uniform(0.1, 10, (R, 1))).astype(np.float32)
+    a_q, a_s = L.quant_fp8_per_token(x)
+    ref = L.nvfp4_rows(a_q, a_s, experts, lambda e: packed[e], lambda e: bs[e], lambda e: s2[e])
+    d = lambda a: torch.from_numpy(a).to(_dev())  # noqa
+    args = (d(a_q), d(a_s), plan, d(packed), d(bs), d(s2))
+    out32 = mq.moe_grouped_gemm_nvfp4(*args, epilogue=mq.EPI_NONE, out_dtype=torch.float32)
+    outbf = mq.moe_grouped_gemm_nvfp4(*args, epilogue=mq.EPI_NONE)
+    h = mq.moe_grouped_gemm_nvfp4(*args, epilogue=mq.EPI_SILU_MUL)
+    torch.cuda.synchronize()
+    assert_close(to_np(out32), ref, rel=1e-4, max_abs_frac=1e-4, what="fp32 out")
+    assert_close(to_np(outbf), F.bf16_round(ref), what="bf16 out")
+    assert_close(to_np(h), L.silu_mul(ref), what="silu_mul")
+    h2 = mq.moe_grouped_gemm_nvfp4(*args, epilogue=mq.EPI_SILU_MUL)
+    assert torch.equal(h, h2)
+
+
+@pytest.mark.parametrize("T,k,E,N,K,hot", [(8, 2, 4, 128, 1024, None), (70, 1, 2, 256, 512, 0)])
+def test_nvfp4_gemm_exact(T, k, E, N, K, hot):
+    # small-integer activations, power-of-two block scales, scale2 = 1, unit
+    # activation scales: every product and partial sum is a multiple of 2^-4
+    # below 2^20, so the fp32 result is exact and must equal the oracle bit for bit
+    rng, plan, experts, codes, packed, bs, s2 = _nvfp4_case(T, k, E, N, K, hot, K + T, True)
+    R = T * k
+    int_code = {v: int(F.e4m3_encode([v])[0]) for v in range(-8, 9)}
+    a_q = np.vectorize(int_code.get)(rng.integers(-8, 9, (R, K))).astype(np.uint8)
+    a_s = np.ones(R, np.float32)
+    ref = L.nvfp4_rows(a_q, a_s, experts, lambda e: packed[e], lambda e: bs[e], lambda e: s2[e])
+    d = lambda a: torch.from_numpy(a).to(_dev())  # noqa
+    out = mq.moe_grouped_gemm_nvfp4(d(a_q), d(a_s), plan, d(packed), d(bs), d(s2),
+                                    epilogue=mq.EPI_NONE, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), ref)
+
+
 # ------------------------------------------------------------------ combine ----
 @pytest.mark.parametrize("T,k,E,H,shared", [(33, 6, 256, 4096, False), (16, 2, 8, 256, True),
                                             (5, 1, 3, 8, False)])
