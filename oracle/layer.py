@@ -311,6 +311,40 @@ def nvfp4_rows(a_q, a_s, experts, packed_of, bscale_of, scale2_of):
     return out if out is not None else np.zeros((R, 0))
 
 
+def aqlm_dequant(codes, books, row_scale):
+    """AQLM cold-expert weights ("Inkling-512k-NVFP4-AQLM-hybrid", "Dequant math",
+    cold): for output row r and group g of 8 input channels,
+    W[r, 8g:8g+8] = (sum over books b of book_b[codes_b[r, g]]) * row_scale[r].
+    codes: list of [N, K/8] arrays (uint8, or int16 whose negative values wrap to
+    the unsigned row, idx & 0xFFFF); books: list of fp16 [entries_b, 8];
+    row_scale: fp16 [N].  Exact in float64."""
+    acc = None
+    for c, bk in zip(codes, books):
+        idx = np.asarray(c).astype(np.int64) & 0xFFFF
+        rows = np.asarray(bk, dtype=np.float16).astype(np.float64)[idx]     # [N, K/8, 8]
+        acc = rows if acc is None else acc + rows
+    N, G, _ = acc.shape
+    w = acc.reshape(N, G * 8)
+    return w * np.asarray(row_scale, dtype=np.float16).astype(np.float64)[:, None]
+
+
+def aqlm_rows(a_q, a_s, experts, codes_of, books, scale_of):
+    """out[p, n] = a_s[p] * sum_k E4M3(a_q[p, k]) * W_e[n, k] with W_e the AQLM
+    weights of row p's expert (aqlm_dequant; the codebooks are shared by all
+    experts of the layer), float64."""
+    a = e4m3_decode(a_q)
+    R = a.shape[0]
+    out = None
+    for e in np.unique(experts):
+        rows = np.nonzero(experts == e)[0]
+        w = aqlm_dequant(codes_of(e), books, scale_of(e))
+        blk = (a[rows] @ w.T) * np.asarray(a_s, dtype=np.float64)[rows, None]
+        if out is None:
+            out = np.zeros((R, w.shape[0]), dtype=np.float64)
+        out[rows] = blk
+    return out if out is not None else np.zeros((R, 0))
+
+
 def silu(z):
     z = np.asarray(z, dtype=np.float64)
     return z / (1.0 + np.exp(-z))

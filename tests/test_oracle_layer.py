@@ -371,6 +371,41 @@ def test_nvfp4_rows_brute_force():
             assert got[p, n] == pytest.approx(float(a_s[p]) * float(s2[e]) * acc, rel=1e-12, abs=1e-300)
 
 
+def test_aqlm_dequant_hand_example_and_int16_wrap():
+    # two books: a 65536-entry book addressed by int16 codes (negative values wrap
+    # to idx & 0xFFFF) and a 256-entry book addressed by uint8 codes
+    b0 = np.zeros((65536, 8), np.float16)
+    b0[5] = np.arange(8, dtype=np.float16)               # 0..7
+    b0[0xFFFE] = np.float16(0.5)                         # reached by int16 code -2
+    b1 = np.zeros((256, 8), np.float16)
+    b1[3] = np.float16(-1.0)
+    codes0 = np.array([[5, -2]], dtype=np.int16)
+    codes1 = np.array([[3, 0]], dtype=np.uint8)
+    w = L.aqlm_dequant([codes0, codes1], [b0, b1], np.array([2.0], np.float16))
+    assert w[0, :8].tolist() == [2.0 * (i - 1.0) for i in range(8)]
+    assert w[0, 8:].tolist() == [1.0] * 8
+
+
+def test_aqlm_rows_brute_force():
+    rng = np.random.default_rng(33)
+    E, N, K, R = 2, 3, 32, 4
+    b0 = rng.standard_normal((300, 8)).astype(np.float16)
+    codes = rng.integers(0, 300, (E, N, K // 8)).astype(np.int16)
+    sc = (rng.random((E, N)) + 0.5).astype(np.float16)
+    a_q = F.e4m3_encode(rng.standard_normal((R, K)))
+    a_s = np.array([1.0, 0.5, 2.0, 0.75], dtype=np.float32)
+    experts = np.array([0, 1, 1, 0])
+    got = L.aqlm_rows(a_q, a_s, experts, lambda e: [codes[e]], [b0], lambda e: sc[e])
+    for p in range(R):
+        e = experts[p]
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                wv = float(b0[codes[e, n, k // 8], k % 8]) * float(sc[e, n])
+                acc += float(F.e4m3_decode([a_q[p, k]])[0]) * wv
+            assert got[p, n] == pytest.approx(float(a_s[p]) * acc, rel=1e-12, abs=1e-300)
+
+
 def test_silu_closed_forms():
     z = np.linspace(-30, 30, 1001)
     np.testing.assert_allclose(L.silu(z), z * scipy.special.expit(z), rtol=1e-14, atol=1e-300)
