@@ -22,6 +22,7 @@ __all__ = [
     "moe_plan_size", "moe_router_logits", "moe_route_topk", "quant_fp8_per_token", "moe_permute",
     "moe_route_quant_permute", "pack_int4_g128", "moe_requant_fp8_fnuz",
     "moe_grouped_gemm_w4a8", "moe_grouped_gemm_w4a8_bf16s", "moe_grouped_gemm_nvfp4",
+    "moe_grouped_gemm_aqlm",
     "moe_expert_mlp_w4a8",
     "moe_expert_mlp_w4a8_bf16s", "moe_expert_mlp_fp8row", "pack_int4_g128_bf16s", "moe_grouped_gemm_fp8row", "moe_combine", "moe_shared_gemm_bf16",
     "plan_fields", "EXPORTED_SYMBOLS",
@@ -57,7 +58,9 @@ _SIGNATURES = {
     "moe_grouped_gemm_w4a8": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_grouped_gemm_fp8row": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_grouped_gemm_w4a8_bf16s": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
-    "moe_grouped_gemm_nvfp4": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _I, _P, _I, _P]),
+    "moe_grouped_gemm_nvfp4": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P]),
+    "moe_grouped_gemm_aqlm": (_I, [_P, _P, _P, _I, _I, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _I,
+                                   _P]),
     "moe_expert_mlp_w4a8": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P,
                                  _P]),
     "moe_expert_mlp_w4a8_bf16s": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P,
@@ -345,19 +348,27 @@ def moe_grouped_gemm_w4a8_bf16s(a_q, a_s, plan, w_packed, w_scales, epilogue: in
 def moe_grouped_gemm_nvfp4(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Tensor,
                            w_fp4: torch.Tensor, w_block_scale: torch.Tensor,
                            w_scale2: torch.Tensor, epilogue: int = EPI_NONE,
-                           out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """w_fp4 [E, N, K/2] uint8 (E2M1 pairs), w_block_scale [E, N, K/16] uint8 (E4M3),
-    w_scale2 [E] fp32."""
+                           out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None,
+                           slab_of: Optional[torch.Tensor] = None, E: Optional[int] = None
+                           ) -> torch.Tensor:
+    """w_fp4 [S, N, K/2] uint8 (E2M1 pairs), w_block_scale [S, N, K/16] uint8 (E4M3),
+    w_scale2 [S] fp32; slab_of [E] int32 (-1: expert not NVFP4; rows left as they are)
+    or None (slab e = expert e, E = S)."""
     _req(a_q, "a_q", torch.uint8, 2)
     _req(a_s, "a_s", torch.float32, 1)
     _req(plan, "plan", torch.int32, 1)
     _req(w_fp4, "w_fp4", torch.uint8, 3)
     _req(w_block_scale, "w_block_scale", torch.uint8, 3)
     _req(w_scale2, "w_scale2", torch.float32, 1)
-    E, N, K2 = w_fp4.shape
+    S, N, K2 = w_fp4.shape
     K = 2 * K2
-    if tuple(w_block_scale.shape) != (E, N, K // 16) or tuple(w_scale2.shape) != (E,):
+    if tuple(w_block_scale.shape) != (S, N, K // 16) or tuple(w_scale2.shape) != (S,):
         raise ValueError("w_block_scale / w_scale2 shapes do not match w_fp4")
+    if slab_of is not None:
+        _req(slab_of, "slab_of", torch.int32, 1)
+        E = slab_of.shape[0]
+    elif E is None:
+        E = S
     R = a_q.shape[0]
     if a_q.shape[1] != K:
         raise ValueError("a_q has the wrong K")
@@ -366,8 +377,50 @@ def moe_grouped_gemm_nvfp4(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Ten
         out = torch.empty(R, n_out, dtype=out_dtype, device=a_q.device)
     odt = MOEQ_BF16 if out.dtype == torch.bfloat16 else MOEQ_F32
     _check("moe_grouped_gemm_nvfp4", lib.moe_grouped_gemm_nvfp4(
-        _ptr(a_q), _ptr(a_s), _ptr(plan), E, R, _ptr(w_fp4), _ptr(w_block_scale), _ptr(w_scale2),
+        _ptr(a_q), _ptr(a_s), _ptr(plan), E, R, _ptr(slab_of), _ptr(w_fp4), _ptr(w_block_scale),
+        _ptr(w_scale2),
         N, K, epilogue, _ptr(out), odt, _stream(a_q.device)))
+    return out
+
+
+def moe_grouped_gemm_aqlm(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Tensor,
+                          codes: list, codebooks: list, row_scale: torch.Tensor,
+                          epilogue: int = EPI_NONE, out_dtype=torch.bfloat16,
+                          out: Optional[torch.Tensor] = None,
+                          slab_of: Optional[torch.Tensor] = None,
+                          E: Optional[int] = None) -> torch.Tensor:
+    """codes: list (1 or 2) of [S, N, K/8] uint8 (book of <= 256 entries) or int16;
+    codebooks: list of fp16 [entries, 8]; row_scale [S, N] fp16; slab_of as for
+    moe_grouped_gemm_nvfp4."""
+    _req(a_q, "a_q", torch.uint8, 2)
+    _req(a_s, "a_s", torch.float32, 1)
+    _req(plan, "plan", torch.int32, 1)
+    _req(row_scale, "row_scale", torch.float16, 2)
+    nb = len(codes)
+    if nb != len(codebooks) or nb not in (1, 2):
+        raise ValueError("one or two books, with one code tensor each")
+    S, N = row_scale.shape
+    R, K = a_q.shape
+    for c, bk in zip(codes, codebooks):
+        _req(bk, "codebook", torch.float16, 2)
+        _req(c, "codes", torch.int16 if bk.shape[0] > 256 else torch.uint8, 3)
+        if tuple(c.shape) != (S, N, K // 8) or bk.shape[1] != 8:
+            raise ValueError("codes must be [S, N, K/8] and codebooks [entries, 8]")
+    if slab_of is not None:
+        _req(slab_of, "slab_of", torch.int32, 1)
+        E = slab_of.shape[0]
+    elif E is None:
+        E = S
+    n_out = N // 2 if epilogue == EPI_SILU_MUL else N
+    if out is None:
+        out = torch.empty(R, n_out, dtype=out_dtype, device=a_q.device)
+    odt = MOEQ_BF16 if out.dtype == torch.bfloat16 else MOEQ_F32
+    cptr = (ctypes.c_void_p * nb)(*[c.data_ptr() for c in codes])
+    bptr = (ctypes.c_void_p * nb)(*[b.data_ptr() for b in codebooks])
+    ents = (ctypes.c_int * nb)(*[b.shape[0] for b in codebooks])
+    _check("moe_grouped_gemm_aqlm", lib.moe_grouped_gemm_aqlm(
+        _ptr(a_q), _ptr(a_s), _ptr(plan), E, R, _ptr(slab_of), nb, cptr, ents, bptr,
+        _ptr(row_scale), N, K, epilogue, _ptr(out), odt, _stream(a_q.device)))
     return out
 
 

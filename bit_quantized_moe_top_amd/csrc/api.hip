@@ -202,7 +202,8 @@ int moe_grouped_gemm_w4a8_bf16s(const uint8_t* a_q, const float* a_s, const void
 }
 
 int moe_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
-                           const uint8_t* w_fp4, const uint8_t* w_block_scale,
+                           const int32_t* slab_of, const uint8_t* w_fp4,
+                           const uint8_t* w_block_scale,
                            const float* w_scale2, int N, int K, int epilogue, void* out,
                            int out_dtype, void* stream) {
   if (R < 0 || E <= 0 || N <= 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;
@@ -218,9 +219,43 @@ int moe_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* pla
     return MOEQ_ERR_INVALID_ARG;
   if (R == 0) return MOEQ_OK;
   if (int rc = check_device()) return rc;
-  return launch_status(moeq::launch_grouped_gemm_nvfp4(a_q, a_s, plan, E, R, w_fp4, w_block_scale,
+  return launch_status(moeq::launch_grouped_gemm_nvfp4(a_q, a_s, plan, E, R, slab_of, w_fp4,
+                                                       w_block_scale,
                                                        w_scale2, N, K, epilogue, out, out_dtype,
                                                        as_stream(stream)));
+}
+
+int moe_grouped_gemm_aqlm(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
+                          const int32_t* slab_of, int n_books, const void* const* codes,
+                          const int* book_entries, const uint16_t* const* codebooks,
+                          const uint16_t* row_scale, int N, int K, int epilogue, void* out,
+                          int out_dtype, void* stream) {
+  if (R < 0 || E <= 0 || N <= 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;
+  if (epilogue != MOEQ_EPI_NONE && epilogue != MOEQ_EPI_SILU_MUL) return MOEQ_ERR_INVALID_ARG;
+  if (out_dtype != MOEQ_F32 && out_dtype != MOEQ_BF16) return MOEQ_ERR_INVALID_ARG;
+  if (epilogue == MOEQ_EPI_SILU_MUL && out_dtype != MOEQ_BF16) return MOEQ_ERR_INVALID_ARG;
+  if (n_books < 1 || n_books > moeq::kAqlmMaxBooks) return MOEQ_ERR_UNSUPPORTED;
+  if (!codes || !book_entries || !codebooks) return MOEQ_ERR_INVALID_ARG;
+  for (int b = 0; b < n_books; ++b)
+    if (book_entries[b] < 1 || book_entries[b] > 65536) return MOEQ_ERR_UNSUPPORTED;
+  if (E > MOEQ_MAX_EXPERTS) return MOEQ_ERR_UNSUPPORTED;
+  if (K % 128 != 0 || N % 128 != 0) return MOEQ_ERR_UNSUPPORTED;
+  if (int64_t(N / 32) * moeq::plan_max_tiles(E, R) > 0x7FFFFFF0) return MOEQ_ERR_UNSUPPORTED;
+  if (R > 0 && (!a_q || !a_s || !plan || !row_scale || !out)) return MOEQ_ERR_INVALID_ARG;
+  for (int b = 0; R > 0 && b < n_books; ++b) {
+    if (!codes[b] || !codebooks[b]) return MOEQ_ERR_INVALID_ARG;
+    const uintptr_t align = book_entries[b] > 256 ? 7u : 3u;      // 8- or 4-byte code loads
+    if ((reinterpret_cast<uintptr_t>(codes[b]) & align) || !aligned16(codebooks[b]))
+      return MOEQ_ERR_INVALID_ARG;
+  }
+  if (R > 0 && (!aligned16(a_q) || (reinterpret_cast<uintptr_t>(row_scale) & 1u)))
+    return MOEQ_ERR_INVALID_ARG;
+  if (R == 0) return MOEQ_OK;
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_grouped_gemm_aqlm(a_q, a_s, plan, E, R, slab_of, n_books,
+                                                      codes, book_entries, codebooks, row_scale,
+                                                      N, K, epilogue, out, out_dtype,
+                                                      as_stream(stream)));
 }
 
 int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,

@@ -88,11 +88,14 @@ template <>
 struct ScaleOf<kW4G128Bf16> { using type = uint16_t; };
 template <>
 struct ScaleOf<kNvfp4> { using type = uint8_t; };      // E4M3 block scales
+template <>
+struct ScaleOf<kAqlm> { using type = _Float16; };      // per-row fp16 scales
 template <int WFMT>
 using ScaleT = typename ScaleOf<WFMT>::type;
 
 __device__ __forceinline__ float scale_value(float s) { return s; }
 __device__ __forceinline__ float scale_value(uint16_t s) { return bf16_to_f32(s); }
+__device__ __forceinline__ float scale_value(_Float16 s) { return static_cast<float>(s); }
 
 // n consecutive scales (n % 4 == 0) starting at p, as fp32: 16-byte (fp32) or
 // 8-byte (bf16) vector loads
@@ -252,7 +255,7 @@ template <int WFMT, int NB = 2>
 __device__ __forceinline__ void row_scales(const ScaleT<WFMT>* const (&srow)[NB], float (&rs)[NB]) {
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    if constexpr (WFMT == kFp8Row) rs[j] = scale_value(srow[j][0]);
+    if constexpr (WFMT == kFp8Row || WFMT == kAqlm) rs[j] = scale_value(srow[j][0]);
     else rs[j] = 1.0f;
   }
 }

@@ -81,18 +81,31 @@ hipError_t launch_pack_int4(const float* w, int64_t rows, int K, uint8_t* packed
 
 // weight formats of the grouped GEMM: INT4 g128 with fp32 or bf16 group scales,
 // row-scaled E4M3 (fp32 row scales); w_scale points to scales of that type
-enum WeightFormat { kW4G128 = 0, kFp8Row = 1, kW4G128Bf16 = 2, kNvfp4 = 3 };
+enum WeightFormat { kW4G128 = 0, kFp8Row = 1, kW4G128Bf16 = 2, kNvfp4 = 3, kAqlm = 4 };
 
 hipError_t launch_grouped_gemm(int wfmt, const uint8_t* a_q, const float* a_s, const void* plan,
                                int E, int R, const uint8_t* w, const void* w_scale, int N, int K,
                                int epilogue, void* out, int out_dtype, hipStream_t stream);
 
-// NVFP4 weights: E2M1 codes [E, N, K/2], E4M3 block-16 scales [E, N, K/16], fp32
-// per-expert scale2 [E]
+// NVFP4 weights: E2M1 codes [S, N, K/2], E4M3 block-16 scales [S, N, K/16], fp32
+// per-slab scale2 [S]; slab_of [E] maps experts to slabs (-1: not NVFP4), NULL
+// for the identity
 hipError_t launch_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* plan, int E,
-                                     int R, const uint8_t* w, const uint8_t* w_block_scale,
+                                     int R, const int32_t* slab_of, const uint8_t* w,
+                                     const uint8_t* w_block_scale,
                                      const float* w_scale2, int N, int K, int epilogue, void* out,
                                      int out_dtype, hipStream_t stream);
+
+// AQLM weights (1 or 2 codebooks of 8-wide fp16 rows): codes[b] [S, N, K/8]
+// (uint8 when book b has <= 256 entries, else int16), codebooks[b] [entries, 8]
+// fp16, row_scale [S, N] fp16; slab_of as for NVFP4
+constexpr int kAqlmMaxBooks = 2;
+hipError_t launch_grouped_gemm_aqlm(const uint8_t* a_q, const float* a_s, const void* plan, int E,
+                                    int R, const int32_t* slab_of, int n_books,
+                                    const void* const* codes, const int* book_entries,
+                                    const uint16_t* const* codebooks, const uint16_t* row_scale,
+                                    int N, int K, int epilogue, void* out, int out_dtype,
+                                    hipStream_t stream);
 
 // E is read from the plan header on the device.
 hipError_t launch_combine(const uint16_t* o, const void* plan, const float* w,

@@ -17,6 +17,11 @@
 // end.  One dequantization instruction per weight pair plus one multiply: no
 // per-block partial sums and no per-group FMAs.
 //
+// slab_of (optional, [E]): weight slab of each routed expert, -1 for experts
+// stored in another format (the hybrid card keeps hot experts as NVFP4 slabs
+// listed by hot_ids and cold ones as AQLM); tiles of such experts are skipped,
+// so the rows they own are left to the other format's kernel.
+//
 // Structure: the wave kernel of the INT4 path (gemm.hip) -- one wave per (plan
 // tile, 32 weight rows), 128-K chunks through a register ring; lane (n, kb)
 // holds K [32 kb, 32 kb + 32) of its row per chunk (16 bytes of codes and the
@@ -73,8 +78,8 @@ struct NvStage {
 template <int EPI>
 __global__ void __launch_bounds__(kThreads, 3)
 gemm_nvfp4_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int E, int R,
-                  const uint8_t* w, const uint8_t* w_bs, const float* w_scale2, int N, int K,
-                  void* out, int out_f32) {
+                  const int32_t* slab_of, const uint8_t* w, const uint8_t* w_bs,
+                  const float* w_scale2, int N, int K, void* out, int out_f32) {
   const int lane = threadIdx.x & 63;
   const int ln = lane & 15, kb = lane >> 4;
   const int units_per_tile = N / 32;
@@ -83,7 +88,10 @@ gemm_nvfp4_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int
   const int u = unit - tile * units_per_tile;
   if (tile >= plan[kPlanTiles]) return;                 // wave-uniform
   const TileInfo ti = tile_info(plan, E, R, tile);
-  const float scale2 = w_scale2[ti.e];
+  // weight slab of the tile's expert; experts stored in another format are skipped
+  const int slab = slab_of ? slab_of[ti.e] : ti.e;
+  if (slab < 0) return;                                 // wave-uniform
+  const float scale2 = w_scale2[slab];
   const int G = K >> 7;
 
   int col[2];
@@ -92,7 +100,7 @@ gemm_nvfp4_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int
   const uint8_t* srow[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int64_t n_glob = int64_t(ti.e) * N + col[j] + ln;
+    const int64_t n_glob = int64_t(slab) * N + col[j] + ln;
     wrow[j] = w + n_glob * (K >> 1);
     srow[j] = w_bs + n_glob * (K >> 4);
   }
@@ -155,7 +163,8 @@ gemm_nvfp4_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int
 }  // namespace
 
 hipError_t launch_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* plan, int E,
-                                     int R, const uint8_t* w, const uint8_t* w_block_scale,
+                                     int R, const int32_t* slab_of, const uint8_t* w,
+                                     const uint8_t* w_block_scale,
                                      const float* w_scale2, int N, int K, int epilogue, void* out,
                                      int out_dtype, hipStream_t stream) {
   if (R == 0) return hipSuccess;
@@ -165,10 +174,10 @@ hipError_t launch_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const
   const int32_t* p = static_cast<const int32_t*>(plan);
   if (epilogue == MOEQ_EPI_SILU_MUL)
     hipLaunchKernelGGL(gemm_nvfp4_kernel<MOEQ_EPI_SILU_MUL>, grid, dim3(kThreads), 0, stream, a_q,
-                       a_s, p, E, R, w, w_block_scale, w_scale2, N, K, out, out_f32);
+                       a_s, p, E, R, slab_of, w, w_block_scale, w_scale2, N, K, out, out_f32);
   else
     hipLaunchKernelGGL(gemm_nvfp4_kernel<MOEQ_EPI_NONE>, grid, dim3(kThreads), 0, stream, a_q, a_s,
-                       p, E, R, w, w_block_scale, w_scale2, N, K, out, out_f32);
+                       p, E, R, slab_of, w, w_block_scale, w_scale2, N, K, out, out_f32);
   return hipGetLastError();
 }
 

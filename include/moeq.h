@@ -295,14 +295,50 @@ int moe_grouped_gemm_w4a8_bf16s(const uint8_t* a_q, const float* a_s, const void
  * FP8 (the card quantizes only the weights; the reading used here keeps the
  * layer's activation path).
  *
- *   w_fp4 [E, N, K/2] bytes, w_block_scale [E, N, K/16] E4M3 bytes, w_scale2 [E] fp32
+ *   slab_of [E] int32 or NULL: weight slab of each routed expert, -1 for experts
+ *     stored in another format, whose rows this call leaves untouched (the hybrid
+ *     card's hot_ids list the routed expert of each NVFP4 slab; slab_of is its
+ *     inverse).  NULL: slab e is expert e.
+ *   w_fp4 [S, N, K/2] bytes, w_block_scale [S, N, K/16] E4M3 bytes, w_scale2 [S] fp32
  * Limits: K % 128 == 0, N % 128 == 0, 1 <= E <= MOEQ_MAX_EXPERTS; a_q, w_fp4 and
  * w_block_scale 16-byte aligned.
  */
 int moe_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
-                           const uint8_t* w_fp4, const uint8_t* w_block_scale,
+                           const int32_t* slab_of, const uint8_t* w_fp4,
+                           const uint8_t* w_block_scale,
                            const float* w_scale2, int N, int K, int epilogue, void* out,
                            int out_dtype, void* stream);
+
+/*
+ * moe_grouped_gemm_aqlm -- grouped GEMM over AQLM expert weights (the cold
+ * experts of the NVFP4 + AQLM hybrid checkpoint) with per-token FP8 activations.
+ *
+ * Weight format ("Inkling-512k-NVFP4-AQLM-hybrid", "On-disk tensor format" and
+ * "Dequant math", cold): groups of 8 input channels; per book b a code per
+ * (row, group) -- uint8 for books of <= 256 entries, else int16 read as
+ * idx & 0xFFFF -- selecting an 8-wide fp16 codebook row; one fp16 scale per
+ * output row:
+ *   W[e, n, 8g:8g+8] = (sum_b codebook_b[codes_b[e, n, g]]) * row_scale[e, n]
+ *   v[p, n] = a_s[p] * sum_k E4M3(a_q[p, k]) * W[e, n, k]
+ * with exact products and fp32 accumulation (each book's rows enter the sum
+ * separately, never added to each other in fp16); epilogue and out as in
+ * moe_grouped_gemm_w4a8.
+ *
+ *   slab_of [E] int32 or NULL -- as in moe_grouped_gemm_nvfp4 (cold_ids inverse)
+ *   n_books 1 or 2; codes, book_entries, codebooks: HOST arrays of n_books
+ *     entries: device pointers to codes_b [S, N, K/8], the entry counts
+ *     (1 .. 65536), device pointers to codebook_b [entries_b, 8] fp16
+ *   row_scale [S, N] fp16
+ * Codes at or past a book's entry count are invalid input; they read the
+ * book's last row.
+ * Limits: K % 128 == 0, N % 128 == 0, 1 <= E <= MOEQ_MAX_EXPERTS; a_q and the
+ * codebooks 16-byte aligned, int16 codes 8-byte and uint8 codes 4-byte aligned.
+ */
+int moe_grouped_gemm_aqlm(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
+                          const int32_t* slab_of, int n_books, const void* const* codes,
+                          const int* book_entries, const uint16_t* const* codebooks,
+                          const uint16_t* row_scale, int N, int K, int epilogue, void* out,
+                          int out_dtype, void* stream);
 
 /*
  * moe_grouped_gemm_fp8row -- grouped GEMM with row-scaled FP8 expert weights.

@@ -429,6 +429,105 @@ def test_nvfp4_gemm_exact(T, k, E, N, K, hot):
     np.testing.assert_array_equal(out.cpu().numpy(), ref)
 
 
+# -------------------------------------------------------------- AQLM experts ----
+def _aqlm_case(E, N, K, books, rng, int_books=False):
+    codes, cbs = [], []
+    for entries in books:
+        if int_books:
+            bk = rng.integers(-4, 5, (entries, 8)).astype(np.float16)
+        else:
+            bk = (rng.standard_normal((entries, 8)) * 0.05).astype(np.float16)
+        if entries > 256:
+            c = rng.integers(0, entries, (E, N, K // 8)).astype(np.int64)
+            c = np.where(c >= 32768, c - 65536, c).astype(np.int16)     # int16 wrap
+        else:
+            c = rng.integers(0, entries, (E, N, K // 8)).astype(np.uint8)
+        codes.append(c)
+        cbs.append(bk)
+    return codes, cbs
+
+
+@pytest.mark.parametrize("books", [(65536,), (65536, 256), (200,), (300, 70)])
+@pytest.mark.parametrize("T,k,E,N,K,hot", [(4, 6, 16, 256, 512, None), (40, 2, 6, 384, 1024, 1)])
+def test_aqlm_gemm_random(books, T, k, E, N, K, hot):
+    rng = np.random.default_rng(N + K + T + sum(books))
+    ids = _case_ids(T, k, E, rng, hot)
+    plan, experts = _plan_and_experts(ids, E)
+    R = T * k
+    codes, cbs = _aqlm_case(E, N, K, books, rng)
+    sc = (rng.random((E, N)) + 0.5).astype(np.float16)
+    x = (rng.standard_normal((R, K)) * rng.uniform(0.1, 10, (R, 1))).astype(np.float32)
+    a_q, a_s = L.quant_fp8_per_token(x)
+    ref = L.aqlm_rows(a_q, a_s, experts, lambda e: [c[e] for c in codes], cbs, lambda e: sc[e])
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(_dev())  # noqa
+    args = (d(a_q), d(a_s), plan, [d(c) for c in codes], [d(b) for b in cbs], d(sc))
+    out32 = mq.moe_grouped_gemm_aqlm(*args, epilogue=mq.EPI_NONE, out_dtype=torch.float32)
+    h = mq.moe_grouped_gemm_aqlm(*args, epilogue=mq.EPI_SILU_MUL)
+    torch.cuda.synchronize()
+    assert_close(to_np(out32), ref, rel=1e-4, max_abs_frac=1e-4, what="fp32 out")
+    assert_close(to_np(h), L.silu_mul(ref), what="silu_mul")
+
+
+def test_aqlm_gemm_exact():
+    # integer codebook entries, small-integer activations, unit scales: exact sums
+    rng = np.random.default_rng(77)
+    T, k, E, N, K = 8, 2, 4, 128, 512
+    ids = _case_ids(T, k, E, rng)
+    plan, experts = _plan_and_experts(ids, E)
+    R = T * k
+    codes, cbs = _aqlm_case(E, N, K, (65536, 256), rng, int_books=True)
+    sc = np.ones((E, N), np.float16)
+    int_code = {v: int(F.e4m3_encode([v])[0]) for v in range(-8, 9)}
+    a_q = np.vectorize(int_code.get)(rng.integers(-8, 9, (R, K))).astype(np.uint8)
+    a_s = np.ones(R, np.float32)
+    ref = L.aqlm_rows(a_q, a_s, experts, lambda e: [c[e] for c in codes], cbs, lambda e: sc[e])
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(_dev())  # noqa
+    out = mq.moe_grouped_gemm_aqlm(d(a_q), d(a_s), plan, [d(c) for c in codes],
+                                   [d(b) for b in cbs], d(sc), epilogue=mq.EPI_NONE,
+                                   out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), ref)
+
+
+def test_hybrid_nvfp4_and_aqlm_slabs():
+    # hot experts as NVFP4 slabs, cold ones as AQLM slabs (the hybrid card's
+    # hot_ids / cold_ids); each call fills only the rows of its own experts
+    rng = np.random.default_rng(5)
+    T, k, E, N, K = 12, 4, 10, 256, 512
+    ids = _case_ids(T, k, E, rng)
+    plan, experts = _plan_and_experts(ids, E)
+    R = T * k
+    hot_ids = np.array([1, 4, 7], np.int32)
+    cold_ids = np.array([e for e in range(E) if e not in hot_ids], np.int32)
+    hot_of = np.full(E, -1, np.int32); hot_of[hot_ids] = np.arange(len(hot_ids))
+    cold_of = np.full(E, -1, np.int32); cold_of[cold_ids] = np.arange(len(cold_ids))
+    packed = F.pack_fp4(rng.integers(0, 16, (len(hot_ids), N, K)).astype(np.uint8))
+    bs = rng.integers(0x20, 0x50, (len(hot_ids), N, K // 16)).astype(np.uint8)
+    s2 = (rng.random(len(hot_ids)) * 0.02 + 1e-3).astype(np.float32)
+    codes, cbs = _aqlm_case(len(cold_ids), N, K, (65536, 256), rng)
+    sc = (rng.random((len(cold_ids), N)) + 0.5).astype(np.float16)
+    x = rng.standard_normal((R, K)).astype(np.float32)
+    a_q, a_s = L.quant_fp8_per_token(x)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(_dev())  # noqa
+    out = torch.full((R, N), float("nan"), device=_dev())
+    mq.moe_grouped_gemm_nvfp4(d(a_q), d(a_s), plan, d(packed), d(bs), d(s2), epilogue=mq.EPI_NONE,
+                              out_dtype=torch.float32, out=out, slab_of=d(hot_of))
+    mq.moe_grouped_gemm_aqlm(d(a_q), d(a_s), plan, [d(c) for c in codes], [d(b) for b in cbs],
+                             d(sc), epilogue=mq.EPI_NONE, out_dtype=torch.float32, out=out,
+                             slab_of=d(cold_of))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert not np.isnan(got).any()                    # every row written by exactly one format
+    hot_rows = np.isin(experts, hot_ids)
+    ref_h = L.nvfp4_rows(a_q[hot_rows], a_s[hot_rows], experts[hot_rows],
+                         lambda e: packed[hot_of[e]], lambda e: bs[hot_of[e]],
+                         lambda e: s2[hot_of[e]])
+    ref_c = L.aqlm_rows(a_q[~hot_rows], a_s[~hot_rows], experts[~hot_rows],
+                        lambda e: [c[cold_of[e]] for c in codes], cbs, lambda e: sc[cold_of[e]])
+    assert_close(got[hot_rows], ref_h, rel=1e-4, max_abs_frac=1e-4, what="hot rows")
+    assert_close(got[~hot_rows], ref_c, rel=1e-4, max_abs_frac=1e-4, what="cold rows")
+
+
 # ------------------------------------------------------------------ combine ----
 @pytest.mark.parametrize("T,k,E,H,shared", [(33, 6, 256, 4096, False), (16, 2, 8, 256, True),
                                             (5, 1, 3, 8, False)])
