@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="weight sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-hybrid", action="store_true",
+                    help="skip the NVFP4 + AQLM hybrid decode layer")
     ap.add_argument("--no-bf16-scales", action="store_true",
                     help="skip the decode layer with bfloat16 INT4 group scales")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -167,6 +169,67 @@ def time_layer(cfg, n_sets, steps, warmup, dev, graph=False, split_events=False)
             "per_call_us": per_call_us, "split_call_us": split_us,
             "distinct_mean": sum(steps_distinct) / steps, "distinct_per_set": distinct,
             "layers": layers}
+
+
+def time_hybrid(cfg, n_sets, steps, warmup, dev):
+    """The NVFP4 + AQLM hybrid layer (hot NVFP4 slabs, cold AQLM slabs): wall time
+    per step over `steps` passes rotating `n_sets` independently drawn layers,
+    per-call times, and the algorithmic bytes each step streams."""
+    import dataclasses
+
+    import torch
+
+    import bit_quantized_moe_top_amd as mq
+    import workloads as W
+    layers = []
+    for s in range(n_sets):
+        c = dataclasses.replace(cfg, seed=cfg.seed + 1000 * s)
+        hot, cold = W.hybrid_partition(c)
+        layer = mq.HybridMoELayer(c.H, c.I, c.E, c.k, device=dev)
+        layer.set_hybrid_weights(hot, cold, W.make_nvfp4_slabs(c, len(hot), dev),
+                                 W.make_aqlm_slabs(c, len(cold), dev))
+        inp = W.make_layer_inputs(c, device=dev, weights=False)
+        layers.append((layer, inp, set(hot.tolist())))
+        torch.cuda.synchronize()
+        log(f"{cfg.name}: weight set {s + 1}/{n_sets} ready")
+    # bytes per expert: hot = E2M1 codes + E4M3 block scales (+ scale2); cold = the
+    # code tensors of every book + fp16 row scales; the codebooks once per step
+    H, I = cfg.H, cfg.I
+    hot_b = (2 * I * H // 2 + 2 * I * H // 16 + 4) + (H * I // 2 + H * I // 16 + 4)
+    cold_b = sum((2 * I * H // 8) * (2 if n > 256 else 1) for n in W.AQLM_BOOKS["w13"]) + \
+        2 * I * 2 + sum((H * I // 8) * (2 if n > 256 else 1) for n in W.AQLM_BOOKS["w2"]) + H * 2
+    book_b = 16 * (sum(W.AQLM_BOOKS["w13"]) + sum(W.AQLM_BOOKS["w2"]))
+    step_bytes, n_hot_touched = [], []
+    for layer, inp, hot in layers:
+        ids, _ = mq.moe_route_topk(inp["logits"], cfg.k, inp["bias"])
+        touched = set(torch.unique(ids).tolist())
+        nh = len(touched & hot)
+        n_hot_touched.append(nh)
+        step_bytes.append(nh * hot_b + (len(touched) - nh) * cold_b + book_b)
+    for i in range(warmup):
+        layer, inp, _ = layers[i % n_sets]
+        layer.forward(inp["x"], inp["logits"], inp["bias"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        layer, inp, _ = layers[i % n_sets]
+        layer.forward(inp["x"], inp["logits"], inp["bias"])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = []
+    for i in range(steps):
+        layer, inp, _ = layers[i % n_sets]
+        layer.forward(inp["x"], inp["logits"], inp["bias"], events=ev)
+    torch.cuda.synchronize()
+    per_call = {}
+    for name, s_, e_ in ev:
+        per_call.setdefault(name, []).append(s_.elapsed_time(e_))
+    del layers
+    ms = 1e3 * wall / steps
+    mean_bytes = sum(step_bytes[i % n_sets] for i in range(steps)) / steps
+    return {"ms_per_step": ms, "bytes_per_step": mean_bytes,
+            "hot_experts_touched": sum(n_hot_touched) / n_sets,
+            "per_call_us": {k: 1e3 * sum(v) / len(v) for k, v in per_call.items()}}
 
 
 def measured_traffic(kernel_bytes: float, name: str = "gemm_gate_up_decode_T4_traffic"):
@@ -354,6 +417,22 @@ def main():
             "unit": "GB/s",
             "gate_up_gemm_us": round(bres["split_call_us"]["gemm_gate_up"], 2),
             "per_call_us": {k: round(v, 2) for k, v in bres["per_call_us"].items()},
+        }
+        torch.cuda.empty_cache()
+    if not args.no_hybrid and cfg.name == "decode":
+        hcfg = W.get_config("hybrid_decode")
+        hres = time_hybrid(hcfg, args.sets, args.steps, args.warmup, dev)
+        hms = hres["ms_per_step"]
+        out["hybrid_decode"] = {
+            "workload": f"NVFP4 + AQLM hybrid decode: T={hcfg.T}, hidden {hcfg.H}, {hcfg.E} "
+                        f"experts of width {hcfg.I}, top-{hcfg.k}, "
+                        f"{round(W.HYBRID_HOT_FRACTION * 100, 1)}% hot (NVFP4), cold AQLM 2-bit "
+                        f"(w13 one 65536-entry book, w2 65536 + 256)",
+            "ms_per_step": round(hms, 5),
+            "weight_bytes_per_step": round(hres["bytes_per_step"]),
+            "hot_experts_touched_per_step": hres["hot_experts_touched"],
+            "value": round(hres["bytes_per_step"] / (hms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "per_call_us": {k: round(v, 2) for k, v in hres["per_call_us"].items()},
         }
         torch.cuda.empty_cache()
     out["host"] = platform.node()

@@ -535,4 +535,4 @@ def moe_shared_gemm_bf16(a: torch.Tensor, w: torch.Tensor, epilogue: int = EPI_N
     return out
 
 
-from .layer import MoELayer  # noqa: E402,F401  (composition of the calls above)
+from .layer import HybridMoELayer, MoELayer  # noqa: E402,F401  (composition of the calls above)

@@ -16,7 +16,8 @@ from typing import Optional
 import torch
 
 from . import (EPI_NONE, EPI_SILU_MUL, moe_combine, moe_expert_mlp_fp8row, moe_expert_mlp_w4a8,
-               moe_grouped_gemm_fp8row, moe_grouped_gemm_w4a8, moe_plan_size,
+               moe_grouped_gemm_aqlm, moe_grouped_gemm_fp8row, moe_grouped_gemm_nvfp4,
+               moe_grouped_gemm_w4a8, moe_plan_size,
                moe_requant_fp8_fnuz, moe_route_quant_permute, moe_router_logits, moe_shared_gemm_bf16, pack_int4_g128,
                quant_fp8_per_token)
 
@@ -149,6 +150,82 @@ class MoELayer:
             shared = step("shared_down", moe_shared_gemm_bf16, b["sh_h"], self.ws2, EPI_NONE,
                           out=b["shared"])
         step("combine", moe_combine, b["o"], b["plan"], b["w"], shared, y=b["y"])
+        return b if return_all else b["y"]
+
+    __call__ = forward
+
+
+class HybridMoELayer(MoELayer):
+    """The NVFP4 + AQLM hybrid expert layer: each routed expert is either hot
+    (an NVFP4 slab) or cold (an AQLM slab).  hot_ids / cold_ids list the routed
+    expert of each slab and together partition 0 .. E-1.
+
+    Hot slabs:  w13 [n_hot, 2I, H/2] E2M1 pairs, w13_bs [n_hot, 2I, H/16] E4M3,
+                w13_s2 [n_hot] fp32; w2 [n_hot, H, I/2], w2_bs [n_hot, H, I/16], w2_s2.
+    Cold slabs: per projection a list of code tensors ([n_cold, out, in/8], one
+                per book), the list of fp16 codebooks [entries, 8], and the fp16
+                row scales [n_cold, out].
+    Each GEMM step runs both formats' kernels; each fills only its experts' rows.
+    """
+
+    def __init__(self, H: int, I: int, E: int, k: int, renormalize: bool = True, device="cuda"):
+        super().__init__(H, I, E, k, "w4a8", renormalize, device)
+        self.weight_format = "hybrid"
+        self.hot = self.cold = None
+
+    def set_hybrid_weights(self, hot_ids, cold_ids, hot: dict, cold: dict):
+        """hot: w13, w13_bs, w13_s2, w2, w2_bs, w2_s2; cold: w13_codes (list), w13_books
+        (list), w13_scale, w2_codes, w2_books, w2_scale."""
+        d = self.device
+        hot_ids = torch.as_tensor(hot_ids, dtype=torch.int64)
+        cold_ids = torch.as_tensor(cold_ids, dtype=torch.int64)
+        if torch.cat([hot_ids, cold_ids]).sort().values.tolist() != list(range(self.E)):
+            raise ValueError("hot_ids and cold_ids must partition the experts")
+        hot_of = torch.full((self.E,), -1, dtype=torch.int32)
+        cold_of = torch.full((self.E,), -1, dtype=torch.int32)
+        hot_of[hot_ids] = torch.arange(len(hot_ids), dtype=torch.int32)
+        cold_of[cold_ids] = torch.arange(len(cold_ids), dtype=torch.int32)
+        self.hot_of, self.cold_of = hot_of.to(d), cold_of.to(d)
+        self.hot, self.cold = hot, cold
+
+    def _gemm_both(self, a_q, a_s, plan, proj: str, epilogue, out):
+        h, c = self.hot, self.cold
+        if h is not None and h[proj].shape[0] > 0:
+            moe_grouped_gemm_nvfp4(a_q, a_s, plan, h[proj], h[proj + "_bs"], h[proj + "_s2"],
+                                   epilogue=epilogue, out=out, slab_of=self.hot_of)
+        if c is not None and c[proj + "_scale"].shape[0] > 0:
+            moe_grouped_gemm_aqlm(a_q, a_s, plan, c[proj + "_codes"], c[proj + "_books"],
+                                  c[proj + "_scale"], epilogue=epilogue, out=out,
+                                  slab_of=self.cold_of)
+        return out
+
+    def forward(self, x: torch.Tensor, logits: Optional[torch.Tensor] = None,
+                bias: Optional[torch.Tensor] = None, return_all: bool = False,
+                events: Optional[list] = None, split_mlp: bool = True):
+        T = x.shape[0]
+        b = self.buffers(T)
+
+        def step(name, fn, *args, **kw):
+            if events is None:
+                return fn(*args, **kw)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            r = fn(*args, **kw)
+            e.record()
+            events.append((name, s, e))
+            return r
+
+        if logits is None:
+            if self.w_router is None:
+                raise ValueError("logits=None needs router weights (set_router)")
+            logits = step("router", moe_router_logits, x, self.w_router, out=b["logits"])
+        step("route_quant_permute", moe_route_quant_permute, logits, x, self.k, bias,
+             self.renormalize, out=b)
+        step("gemm_gate_up", self._gemm_both, b["xp_q"], b["xp_s"], b["plan"], "w13",
+             EPI_SILU_MUL, b["h"])
+        step("quant_h", quant_fp8_per_token, b["h"], q=b["h_q"], scale=b["h_s"])
+        step("gemm_down", self._gemm_both, b["h_q"], b["h_s"], b["plan"], "w2", EPI_NONE, b["o"])
+        step("combine", moe_combine, b["o"], b["plan"], b["w"], None, y=b["y"])
         return b if return_all else b["y"]
 
     __call__ = forward

@@ -31,7 +31,8 @@ import torch
 
 __all__ = [
     "LayerConfig", "CONFIGS", "get_config", "tensor_seed", "make_activations",
-    "router_weights", "make_router", "expert_weight", "iter_expert_weights", "make_shared_weights",
+    "router_weights", "make_router", "expert_weight", "hybrid_partition", "make_nvfp4_slabs",
+    "make_aqlm_slabs", "iter_expert_weights", "make_shared_weights",
     "make_layer_inputs",
 ]
 
@@ -78,7 +79,17 @@ CONFIGS = {
                           zipf_s=1.1, n_shared=2),
     "fp8row": LayerConfig("fp8row", T=2048, H=4096, I=2048, E=384, k=6, x_dtype="bf16",
                           weight_format="fp8row", router="matmul", router_scale=1.0 / 64.0),
+    # the NVFP4 + AQLM hybrid card's layer: hidden 6144, 256 experts of width 3072
+    # (w13 [6144, 6144], w2 [6144, 3072]), 6 active, 14.8% of the experts hot
+    "hybrid_decode": LayerConfig("hybrid_decode", T=4, H=6144, I=3072, E=256, k=6, x_dtype="bf16",
+                                 weight_format="hybrid", router="gaussian", router_scale=0.0),
+    "hybrid_tiny": LayerConfig("hybrid_tiny", T=16, H=256, I=128, E=8, k=2, x_dtype="f32",
+                               weight_format="hybrid", router="gaussian", router_scale=0.0,
+                               x_scale=1.0 / 16.0),
 }
+HYBRID_HOT_FRACTION = 0.148     # hot (NVFP4) share of the routed experts
+# AQLM books: w13 one 65536-entry book; w2 a 65536-entry and a 256-entry book
+AQLM_BOOKS = {"w13": (65536,), "w2": (65536, 256)}
 
 
 def get_config(name: str, **overrides) -> LayerConfig:
@@ -87,7 +98,7 @@ def get_config(name: str, **overrides) -> LayerConfig:
 
 # tensor ids used to key the generators
 _TID = {"x": 1, "router": 2, "logits": 3, "w13": 4, "w2": 5, "zipf_rank": 6,
-        "shared13": 7, "shared2": 8}
+        "shared13": 7, "shared2": 8, "hybrid": 9, "nvfp4": 10, "aqlm": 11}
 
 
 def tensor_seed(seed: int, tensor: str, index: int = 0) -> int:
@@ -204,3 +215,51 @@ def make_layer_inputs(cfg: LayerConfig, device="cpu", weights: bool = True) -> d
 def expected_distinct_experts(E: int, T: int, k: int) -> float:
     """E[#distinct experts] for T tokens each picking k of E uniformly (context only)."""
     return E * (1.0 - ((E - k) / E) ** T)
+
+
+# ----------------------------------------------------------- hybrid experts
+def hybrid_partition(cfg: LayerConfig) -> Tuple[np.ndarray, np.ndarray]:
+    """(hot_ids, cold_ids): a seeded split of the experts, HYBRID_HOT_FRACTION hot."""
+    rng = np.random.default_rng(tensor_seed(cfg.seed, "hybrid"))
+    n_hot = max(1, int(round(HYBRID_HOT_FRACTION * cfg.E)))
+    perm = rng.permutation(cfg.E)
+    return np.sort(perm[:n_hot]).astype(np.int32), np.sort(perm[n_hot:]).astype(np.int32)
+
+
+def make_nvfp4_slabs(cfg: LayerConfig, n_hot: int, device="cpu") -> dict:
+    """Random NVFP4 slabs: uniform E2M1 code pairs, E4M3 block scales drawn from
+    the bytes 0x30 .. 0x3F (0.5 .. 0.94), and per-slab scale2 around w_std / 4 (so
+    the weights have roughly the spread of the other workloads)."""
+    g = _gen(device, cfg.seed, "nvfp4")
+    out = {}
+    for proj, (n, k) in (("w13", (2 * cfg.I, cfg.H)), ("w2", (cfg.H, cfg.I))):
+        out[proj] = torch.randint(0, 256, (n_hot, n, k // 2), generator=g, device=device,
+                                  dtype=torch.uint8)
+        out[proj + "_bs"] = torch.randint(0x30, 0x40, (n_hot, n, k // 16), generator=g,
+                                          device=device, dtype=torch.uint8)
+        out[proj + "_s2"] = (torch.rand(n_hot, generator=g, device=device) * 0.5 + 0.75) * (
+            cfg.w_std / 4)
+    return out
+
+
+def make_aqlm_slabs(cfg: LayerConfig, n_cold: int, device="cpu") -> dict:
+    """Random AQLM slabs: uniform codes over each book (int16 wraps above 32767),
+    fp16 codebooks ~ N(0, w_std), fp16 row scales in [0.5, 1.5)."""
+    g = _gen(device, cfg.seed, "aqlm")
+    out = {}
+    for proj, (n, k) in (("w13", (2 * cfg.I, cfg.H)), ("w2", (cfg.H, cfg.I))):
+        codes, books = [], []
+        for entries in AQLM_BOOKS[proj]:
+            books.append((torch.randn(entries, 8, generator=g, device=device) * cfg.w_std).to(
+                torch.float16))
+            c = torch.randint(0, entries, (n_cold, n, k // 8), generator=g, device=device,
+                              dtype=torch.int32)
+            if entries > 256:
+                codes.append(torch.where(c >= 32768, c - 65536, c).to(torch.int16))
+            else:
+                codes.append(c.to(torch.uint8))
+        out[proj + "_codes"] = codes
+        out[proj + "_books"] = books
+        out[proj + "_scale"] = (torch.rand(n_cold, n, generator=g, device=device) + 0.5).to(
+            torch.float16)
+    return out
