@@ -1,5 +1,6 @@
 // Dense bf16 GEMM for the shared experts: out = epilogue(a @ w^T), fp32 accumulate,
-// on v_mfma_f32_16x16x32_bf16.
+// on v_mfma_f32_16x16x32_bf16.  Two tilings: the large-tile kernel below for
+// prefill-sized M, the small-tile one for small M or shapes it does not cover.
 //
 // Workgroup tile: 128 rows of a x 128 rows of w (the weight rows: for EPI_NONE
 // the 128 output columns nt*128.., for EPI_SILU_MUL the 64 gate rows nt*64..
@@ -39,9 +40,8 @@ shared_gemm_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ 
 
   // staging: thread -> (tile row tid/2, 16-element half tid%2) for both A and B
   const int sr = tid >> 1, sh = tid & 1;
-  const int a_row = m0 + sr;
-  const bool a_ok = a_row < M;
-  const uint16_t* a_src = a + int64_t(a_ok ? a_row : 0) * K + sh * 16;
+  // rows past M re-read row M - 1: their results are never stored
+  const uint16_t* a_src = a + int64_t(min(m0 + sr, M - 1)) * K + sh * 16;
   int w_row;
   if (EPI == MOEQ_EPI_SILU_MUL) w_row = sr < 64 ? nt * 64 + sr : (N >> 1) + nt * 64 + (sr - 64);
   else w_row = nt * kBNw + sr;
@@ -61,30 +61,25 @@ shared_gemm_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ 
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[i][q] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  auto gload = [&](int k0, uint4 (&ra)[2], uint4 (&rb)[2]) {
-    const uint4* pa = reinterpret_cast<const uint4*>(a_src + k0);
-    const uint4* pb = reinterpret_cast<const uint4*>(w_src + k0);
-    if (a_ok) { ra[0] = pa[0]; ra[1] = pa[1]; }
-    else { ra[0] = make_uint4(0, 0, 0, 0); ra[1] = ra[0]; }
-    rb[0] = pb[0];
-    rb[1] = pb[1];
-  };
-  auto sstore = [&](int buf, const uint4 (&ra)[2], const uint4 (&rb)[2]) {
-    uint4* da = reinterpret_cast<uint4*>(&As[buf][sr * kStrideH + sh * 16]);
-    uint4* db = reinterpret_cast<uint4*>(&Bs[buf][sr * kStrideH + sh * 16]);
-    da[0] = ra[0]; da[1] = ra[1];
-    db[0] = rb[0]; db[1] = rb[1];
-  };
-
-  uint4 ra[2], rb[2];
-  gload(0, ra, rb);
-  sstore(0, ra, rb);
+  // staging registers as plain scalars (arrays passed to lambdas by reference
+  // were left in scratch memory)
+  uint4 ra0, ra1, rb0, rb1;
+  const uint4* pa = reinterpret_cast<const uint4*>(a_src);
+  const uint4* pb = reinterpret_cast<const uint4*>(w_src);
+  ra0 = pa[0]; ra1 = pa[1]; rb0 = pb[0]; rb1 = pb[1];
+  uint4* da = reinterpret_cast<uint4*>(&As[0][sr * kStrideH + sh * 16]);
+  uint4* db = reinterpret_cast<uint4*>(&Bs[0][sr * kStrideH + sh * 16]);
+  constexpr int kBufA = kBM * kStrideH / 8, kBufB = kBNw * kStrideH / 8;  // in uint4
+  da[0] = ra0; da[1] = ra1; db[0] = rb0; db[1] = rb1;
   __syncthreads();
   const int steps = K / kBK;
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
     const bool more = s + 1 < steps;
-    if (more) gload((s + 1) * kBK, ra, rb);
+    if (more) {
+      const int o = (s + 1) * kBK / 8;
+      ra0 = pa[o]; ra1 = pa[o + 1]; rb0 = pb[o]; rb1 = pb[o + 1];
+    }
     v8bf bop[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -96,7 +91,11 @@ shared_gemm_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ 
       for (int q = 0; q < 4; ++q)
         acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[q], acc[i][q], 0, 0, 0);
     }
-    if (more) sstore(buf ^ 1, ra, rb);
+    if (more) {
+      const int nb = buf ^ 1;
+      da[nb * kBufA] = ra0; da[nb * kBufA + 1] = ra1;
+      db[nb * kBufB] = rb0; db[nb * kBufB + 1] = rb1;
+    }
     __syncthreads();
   }
 
@@ -120,11 +119,172 @@ shared_gemm_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------- large tiles
+// For the shared experts' prefill shapes (M in the thousands, N % 256 == 0,
+// K % 64 == 0): workgroup tile 128 rows of a x 256 weight rows, K advancing 64
+// per barrier; four waves in a 2 x 2 arrangement, each owning 64 rows x 8
+// column blocks of 16 (32 MFMAs of 16x16x32 per 32-K sub-step, 128 fp32
+// accumulators per lane).  Per sub-step a wave reads 4 A and 8 B operands
+// (12 x 16 B per lane) from LDS for 32 MFMAs -- a third of the LDS bytes per
+// MFMA of the small-tile kernel -- and the next step's global loads (12 x 16 B
+// per thread) are in flight during the current step's MFMAs.  With EPI_SILU_MUL
+// the 256 weight rows are 128 gate rows and their 128 up rows; column block q
+// of a wave (q < 4) is gate, q + 4 the matching up block.
+constexpr int kBM2 = 128, kBN2 = 256, kBK2 = 64;
+constexpr int kStride2 = kBK2 + 8;         // bf16 per LDS row: 144 B, conflict-free 16 B reads
+
+template <int EPI>
+__global__ void __launch_bounds__(kT, 1)
+shared_gemm_big_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ w, int M,
+                       int N, int K, uint16_t* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem2[];
+  uint16_t* As = smem2;                                  // [2][kBM2 * kStride2]
+  uint16_t* Bs = smem2 + 2 * kBM2 * kStride2;            // [2][kBN2 * kStride2]
+  const int n_ntiles = N / kBN2;
+  const int mt = blockIdx.x / n_ntiles;
+  const int nt = blockIdx.x - mt * n_ntiles;
+  const int m0 = mt * kBM2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ln = lane & 15, kq = lane >> 4;
+
+  // staging: 16-byte chunk c of the step's tiles -> (row c / 8, piece c % 8);
+  // A: chunks tid + 256 i (i < 4, rows tid / 8 + 32 i), B: chunks tid + 256 i
+  // (i < 8; rows 32 apart are 32 K elements apart).
+  const int srow = tid >> 3, spiece = (tid & 7) * 8;
+  const int64_t row_step = int64_t(32) * K;
+  // rows past M re-read row M - 1: their results are never stored, and rows
+  // of a product do not mix
+  const uint16_t* a_r0 = a + int64_t(min(m0 + srow, M - 1)) * K + spiece;
+  const uint16_t* a_r1 = a + int64_t(min(m0 + srow + 32, M - 1)) * K + spiece;
+  const uint16_t* a_r2 = a + int64_t(min(m0 + srow + 64, M - 1)) * K + spiece;
+  const uint16_t* a_r3 = a + int64_t(min(m0 + srow + 96, M - 1)) * K + spiece;
+  const uint16_t* w_base;        // rows of B chunks i < 4 (gate rows for EPI_SILU_MUL)
+  const uint16_t* w_base_hi;     // rows of B chunks i >= 4 (the matching up rows)
+  if (EPI == MOEQ_EPI_SILU_MUL) {
+    w_base = w + int64_t(nt * 128 + srow) * K + spiece;
+    w_base_hi = w + int64_t((N >> 1) + nt * 128 + srow) * K + spiece;
+  } else {
+    w_base = w + int64_t(nt * kBN2 + srow) * K + spiece;
+    w_base_hi = w_base + 4 * row_step;
+  }
+  // B-tile row of column block q of this wave
+  int cb[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    if (EPI == MOEQ_EPI_SILU_MUL) cb[q] = (q < 4 ? 0 : 128) + 64 * wn + 16 * (q & 3);
+    else cb[q] = 128 * wn + 16 * q;
+  }
+
+  v4f acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[i][q] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3, rb4, rb5, rb6, rb7;
+#define SG_LD(p) (*reinterpret_cast<const uint4*>(p))
+#define SG_GLOAD(k0)                                                             \
+  do {                                                                           \
+    ra0 = SG_LD(a_r0 + (k0));                                                    \
+    ra1 = SG_LD(a_r1 + (k0));                                                    \
+    ra2 = SG_LD(a_r2 + (k0));                                                    \
+    ra3 = SG_LD(a_r3 + (k0));                                                    \
+    rb0 = SG_LD(w_base + (k0));                                                  \
+    rb1 = SG_LD(w_base + row_step + (k0));                                       \
+    rb2 = SG_LD(w_base + 2 * row_step + (k0));                                   \
+    rb3 = SG_LD(w_base + 3 * row_step + (k0));                                   \
+    rb4 = SG_LD(w_base_hi + (k0));                                               \
+    rb5 = SG_LD(w_base_hi + row_step + (k0));                                    \
+    rb6 = SG_LD(w_base_hi + 2 * row_step + (k0));                                \
+    rb7 = SG_LD(w_base_hi + 3 * row_step + (k0));                                \
+  } while (0)
+#define SG_ST(base, r, v) (*reinterpret_cast<uint4*>(&(base)[((r) * 32 + srow) * kStride2 + spiece]) = (v))
+#define SG_SSTORE(buf)                                                           \
+  do {                                                                           \
+    uint16_t* as_ = As + (buf) * kBM2 * kStride2;                                \
+    uint16_t* bs_ = Bs + (buf) * kBN2 * kStride2;                                \
+    SG_ST(as_, 0, ra0); SG_ST(as_, 1, ra1); SG_ST(as_, 2, ra2); SG_ST(as_, 3, ra3); \
+    SG_ST(bs_, 0, rb0); SG_ST(bs_, 1, rb1); SG_ST(bs_, 2, rb2); SG_ST(bs_, 3, rb3); \
+    SG_ST(bs_, 4, rb4); SG_ST(bs_, 5, rb5); SG_ST(bs_, 6, rb6); SG_ST(bs_, 7, rb7); \
+  } while (0)
+
+  SG_GLOAD(0);
+  SG_SSTORE(0);
+  __syncthreads();
+  const int steps = K / kBK2;
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    const bool more = s + 1 < steps;
+    if (more) SG_GLOAD((s + 1) * kBK2);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* A = As + buf * kBM2 * kStride2;
+    const uint16_t* B = Bs + buf * kBN2 * kStride2;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kk = sub * 32 + kq * 8;
+      v8bf aop[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        aop[i] = *reinterpret_cast<const v8bf*>(&A[(64 * wm + 16 * i + ln) * kStride2 + kk]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const v8bf bop = *reinterpret_cast<const v8bf*>(&B[(cb[q] + ln) * kStride2 + kk]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[i], bop, acc[i][q], 0, 0, 0);
+      }
+      // keep each sub-step's LDS reads next to its MFMAs (hoisting them all
+      // ahead would not fit the register file)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) {
+      __syncthreads();                 // every wave is done reading buf ^ 1 (step s - 1)
+      SG_SSTORE(buf ^ 1);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = m0 + 64 * wm + 16 * i + 4 * kq + v;
+      if (m >= M) continue;
+      if (EPI == MOEQ_EPI_SILU_MUL) {
+        uint16_t* o = out + int64_t(m) * (N >> 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          o[nt * 128 + cb[q] + ln] = f32_to_bf16(silu_f32(acc[i][q][v]) * acc[i][q + 4][v]);
+      } else {
+        uint16_t* o = out + int64_t(m) * N;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[nt * kBN2 + cb[q] + ln] = f32_to_bf16(acc[i][q][v]);
+      }
+    }
+  }
+}
+#undef SG_LD
+#undef SG_GLOAD
+#undef SG_ST
+#undef SG_SSTORE
+
 }  // namespace
 
 hipError_t launch_shared_gemm_bf16(const uint16_t* a, const uint16_t* w, int M, int N, int K,
                                    int epilogue, uint16_t* out, hipStream_t stream) {
   if (M == 0) return hipSuccess;
+  if (M >= 256 && N % kBN2 == 0 && K % kBK2 == 0) {
+    const int64_t blocks2 = int64_t((M + kBM2 - 1) / kBM2) * (N / kBN2);
+    const size_t lds = size_t(2) * (kBM2 + kBN2) * kStride2 * sizeof(uint16_t);
+    auto fn = (epilogue == MOEQ_EPI_SILU_MUL) ? shared_gemm_big_kernel<MOEQ_EPI_SILU_MUL>
+                                              : shared_gemm_big_kernel<MOEQ_EPI_NONE>;
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(fn, dim3(unsigned(blocks2)), dim3(kT), lds, stream, a, w, M, N, K, out);
+    return hipGetLastError();
+  }
   const int64_t blocks = int64_t((M + kBM - 1) / kBM) * (N / kBNw);
   if (epilogue == MOEQ_EPI_SILU_MUL)
     hipLaunchKernelGGL(shared_gemm_kernel<MOEQ_EPI_SILU_MUL>, dim3(unsigned(blocks)), dim3(kT), 0,

@@ -551,7 +551,11 @@ def test_combine(T, k, E, H, shared):
 
 
 # ------------------------------------------------------------- shared GEMM ----
-@pytest.mark.parametrize("M,N,K", [(37, 256, 256), (128, 512, 4096), (200, 128, 96)])
+# M < 256 or N % 256 or K % 64 takes the 32-row kernel, the rest the 128x256 one
+# (ragged last row tile, one K step, several column tiles)
+@pytest.mark.parametrize("M,N,K", [(37, 256, 256), (128, 512, 4096), (200, 128, 96),
+                                   (256, 256, 64), (300, 512, 320), (777, 1024, 192),
+                                   (513, 768, 4096)])
 def test_shared_gemm_bf16(M, N, K):
     g = torch.Generator().manual_seed(M + N + K)
     a = torch.randn(M, K, generator=g).to(torch.bfloat16)
