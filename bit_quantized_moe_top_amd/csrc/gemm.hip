@@ -15,34 +15,82 @@ namespace {
 // restrict-qualified read-only pointers may be hoisted by instruction selection
 // past the scheduling barriers of the sweep, which pulls the whole unrolled
 // sweep's loads to the top of the kernel and spills them.
+//
+// One workgroup per K-split unit (tile, 16 NB weight rows): wave q sweeps K
+// quarter q of the unit for each 16-row block of the tile, the quarters meet
+// in LDS, and wave 0 stores the block.  With GS > 0 (G = GS) each quarter's
+// sweep is unrolled over its GS / 4 groups; GS == 0 takes any G.
 template <int WFMT, int EPI, int GS, int NB>
 __global__ void __launch_bounds__(kThreads, 3)   // >= 3 waves per SIMD
 gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int E, int R,
                  const uint8_t* w, const ScaleT<WFMT>* w_scale, int N, int K, void* out,
                  int out_f32) {
-  const int lane = threadIdx.x & 63;
+  static_assert(GS % 4 == 0, "quarters of a compile-time sweep must be whole groups");
+  constexpr int GQ = GS / 4;
+  // 16-row blocks with at most kStageRows rows (decode) stage a K quarter of
+  // up to kStageK bytes of each activation row in LDS: the two 16-byte loads
+  // per group of the direct path are mostly masked off for so few rows, and
+  // still take a vector memory instruction each
+  constexpr int kStageRows = 4, kStageK = 1024, kStageStride = kStageK + 16;
+  __shared__ __align__(16) uint8_t a_stage[4][kStageRows][kStageStride];
+  __shared__ v4f red[NB * kWave];
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int ln = lane & 15, kb = lane >> 4;
   const int units_per_tile = N / (16 * NB);
-  // wave-uniform (readfirstlane): the unit, its tile and the plan entries read
-  // from it stay in scalar registers
-  const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6));
-  const int tile = unit / units_per_tile;
-  const int u = unit - tile * units_per_tile;
-  if (tile >= plan[kPlanTiles]) return;                 // wave-uniform
-  const TileInfo ti = tile_info(plan, E, R, tile);
+  const int tile = blockIdx.x / units_per_tile;
+  const int u = blockIdx.x - tile * units_per_tile;
+  TileInfo ti;
+  if (!tile_info(plan, E, R, tile, ti)) return;   // workgroup-uniform
 
   int col[NB];
   unit_columns<EPI, NB>(N, u, col);
   const uint8_t* wrow[NB];
   const ScaleT<WFMT>* srow[NB];
   weight_rows<WFMT, NB>(w, w_scale, ti.e, N, K, col, ln, wrow, srow);
+  const int G = K >> 7;
+  const int g0 = quarter_g0(G, q);
+  quarter_rows<WFMT, NB>(g0, wrow, srow);
+  const int kq = (GS > 0 ? GQ : quarter_groups(G, q)) * 128;   // K of this wave's quarter
 
   const int nrb = (ti.rows + 15) >> 4;
   for (int rb = 0; rb < nrb; ++rb) {
     v4f acc[NB];
-    wave_sweep<WFMT, NB, GS, false>(acc, a_q, K, ti.row0, ti.rows, rb, wrow, srow, ln, kb, [] {});
-    store_block<WFMT, EPI, NB>(acc, rb, ti.row0, ti.rows, [a_s](int p) { return a_s[p]; }, srow,
-                               col, ln, kb, N, out, out_f32);
+    const int rrows = min(16, ti.rows - 16 * rb);
+    if (rrows <= kStageRows && kq <= kStageK) {
+      // the block's activation quarter through LDS: one 16-byte load per lane
+      // and row, issued ahead of the weight loads
+      uint8_t* stage = &a_stage[q][0][0];
+      const uint8_t* src = a_q + int64_t(ti.row0 + 16 * rb) * K + g0 * 128 + lane * 16;
+      const bool on = lane * 16 < kq;
+      // (scalars, not an array: an array captured by the lambda stays in scratch)
+      uint4 v0 = {}, v1 = {}, v2 = {}, v3 = {};
+      static_assert(kStageRows == 4, "one register per staged row");
+      if (on) {
+        v0 = *reinterpret_cast<const uint4*>(src);
+        if (rrows > 1) v1 = *reinterpret_cast<const uint4*>(src + K);
+        if (rrows > 2) v2 = *reinterpret_cast<const uint4*>(src + 2 * int64_t(K));
+        if (rrows > 3) v3 = *reinterpret_cast<const uint4*>(src + 3 * int64_t(K));
+      }
+      wave_sweep<WFMT, NB, GQ, true, kALds>(
+          acc, stage, kq, 0, rrows, 0, wrow, srow, ln, kb,
+          [&] {
+            if (on) {
+              uint8_t* d = stage + lane * 16;
+              *reinterpret_cast<uint4*>(d) = v0;
+              if (rrows > 1) *reinterpret_cast<uint4*>(d + kStageStride) = v1;
+              if (rrows > 2) *reinterpret_cast<uint4*>(d + 2 * kStageStride) = v2;
+              if (rrows > 3) *reinterpret_cast<uint4*>(d + 3 * kStageStride) = v3;
+            }
+          },
+          kStageStride);
+    } else {
+      wave_sweep<WFMT, NB, GQ, false>(acc, a_q + g0 * 128, kq, ti.row0, ti.rows, rb, wrow, srow,
+                                      ln, kb, [] {}, K);
+    }
+    quarter_reduce<NB>(acc, red, q, lane);
+    if (q == 0)
+      store_block<WFMT, EPI, NB>(acc, rb, ti.row0, ti.rows, [a_s](int p) { return a_s[p]; },
+                                 srow, col, ln, kb, N, out, out_f32);
   }
 }
 
@@ -94,8 +142,8 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
   if (logical >= total) return;
   const int tile = logical / n_ntiles;
   const int nt = logical - tile * n_ntiles;
-  if (tile >= plan[kPlanTiles]) return;                 // workgroup-uniform
-  const TileInfo ti = tile_info(plan, E, R, tile);
+  TileInfo ti;
+  if (!tile_info(plan, E, R, tile, ti)) return;   // workgroup-uniform
   const int nrb = (ti.rows + 15) >> 4;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -228,11 +276,10 @@ hipError_t launch_kernels(const uint8_t* a_q, const float* a_s, const void* plan
                           int out_f32, hipStream_t stream) {
   const int32_t* p = static_cast<const int32_t*>(plan);
   if (R <= 64) {
-    // few rows per expert: independent waves, one per (tile, 16 NB weight rows)
+    // few rows per expert: one workgroup per K-split unit (tile, 16 NB weight rows)
     constexpr int NB = (EPI == MOEQ_EPI_SILU_MUL) ? 2 : MOEQ_WAVE_NB;
     const int64_t units = int64_t(plan_max_tiles(E, R)) * (N / (16 * NB));
-    const int64_t blocks = (units + 3) / 4;
-    hipLaunchKernelGGL((gemm_wave_kernel<WFMT, EPI, GS, NB>), dim3(unsigned(blocks)),
+    hipLaunchKernelGGL((gemm_wave_kernel<WFMT, EPI, GS, NB>), dim3(unsigned(units)),
                        dim3(kThreads), 0, stream, a_q, a_s, p, E, R, w, w_scale, N, K, out,
                        out_f32);
   } else {

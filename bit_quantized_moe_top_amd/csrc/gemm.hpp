@@ -97,23 +97,37 @@ __device__ __forceinline__ float scale_value(float s) { return s; }
 __device__ __forceinline__ float scale_value(uint16_t s) { return bf16_to_f32(s); }
 __device__ __forceinline__ float scale_value(_Float16 s) { return static_cast<float>(s); }
 
-// n consecutive scales (n % 4 == 0) starting at p, as fp32: 16-byte (fp32) or
-// 8-byte (bf16) vector loads
+// n consecutive scales (n = 1, 2 or a multiple of 4; p aligned to n scales)
+// starting at p, as fp32: one vector load per 4 scales (16 bytes fp32, 8 bf16)
 template <int n>
 __device__ __forceinline__ void load_scales(const float* p, float* out) {
+  if constexpr (n == 1) {
+    out[0] = p[0];
+  } else if constexpr (n == 2) {
+    const float2 f = *reinterpret_cast<const float2*>(p);
+    out[0] = f.x; out[1] = f.y;
+  } else {
 #pragma unroll
-  for (int i = 0; i < n; i += 4) {
-    const float4 f = *reinterpret_cast<const float4*>(p + i);
-    out[i] = f.x; out[i + 1] = f.y; out[i + 2] = f.z; out[i + 3] = f.w;
+    for (int i = 0; i < n; i += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(p + i);
+      out[i] = f.x; out[i + 1] = f.y; out[i + 2] = f.z; out[i + 3] = f.w;
+    }
   }
 }
 template <int n>
 __device__ __forceinline__ void load_scales(const uint16_t* p, float* out) {
+  if constexpr (n == 1) {
+    out[0] = u2f(uint32_t(p[0]) << 16);
+  } else if constexpr (n == 2) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+    out[0] = u2f(u << 16); out[1] = u2f(u & 0xFFFF0000u);
+  } else {
 #pragma unroll
-  for (int i = 0; i < n; i += 4) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p + i);
-    out[i] = u2f(u.x << 16); out[i + 1] = u2f(u.x & 0xFFFF0000u);
-    out[i + 2] = u2f(u.y << 16); out[i + 3] = u2f(u.y & 0xFFFF0000u);
+    for (int i = 0; i < n; i += 4) {
+      const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+      out[i] = u2f(u.x << 16); out[i + 1] = u2f(u.x & 0xFFFF0000u);
+      out[i + 2] = u2f(u.y << 16); out[i + 3] = u2f(u.y & 0xFFFF0000u);
+    }
   }
 }
 
@@ -224,13 +238,25 @@ struct TileInfo {
   int e, row0, rows;
 };
 
-__device__ __forceinline__ TileInfo tile_info(const int32_t* plan, int E, int R, int tile) {
+// The tile's expert, first row and row count, from one round of independent
+// plan loads (nothing waits on the expert id): tiles list the active experts'
+// rows in order, 64 at a time, so a tile's rows end where the next tile's
+// begin, and the last tile's at offsets[E].  Returns whether tile is one of the
+// plan's tiles (ti is meaningful only then); the loads stay inside the tile
+// list for any tile >= 0.
+__device__ __forceinline__ bool tile_info(const int32_t* plan, int E, int R, int tile,
+                                          TileInfo& ti) {
   const PlanView pv = plan_view(const_cast<int32_t*>(plan), E, R);
-  TileInfo t;
-  t.e = pv.tile_expert[tile];
-  t.row0 = pv.tile_row0[tile];
-  t.rows = min(MOEQ_TILE_M, pv.offsets[t.e + 1] - t.row0);
-  return t;
+  const int tl = min(tile, pv.max_tiles - 1);
+  const int n = plan[kPlanTiles];
+  const int e = pv.tile_expert[tl];
+  const int row0 = pv.tile_row0[tl];
+  const int next = pv.tile_row0[min(tl + 1, pv.max_tiles - 1)];
+  const int end_all = pv.offsets[E];
+  ti.e = e;
+  ti.row0 = row0;
+  ti.rows = min(MOEQ_TILE_M, (tile + 1 < n ? next : end_all) - row0);
+  return tile < n;
 }
 
 // weight-row bases (16-row block j of this wave) and their scale rows
@@ -366,14 +392,14 @@ __device__ __forceinline__ void pipeline(int G, IssueF&& issue, ConsumeF&& consu
 // Group scales of this lane's two weight rows (col[0] + ln and col[1] + ln).
 // With G = GS known at compile time the G scales of a row are spread over its
 // four lanes (ln, kb): lane kb holds groups [kb G/4, (kb+1) G/4), fetched with
-// 16-byte loads once per sweep, and the scale of group g comes from lane
+// one vector load per four scales once per sweep, and the scale of group g comes from lane
 // (ln, g / (G/4)) by a cross-lane read.  This keeps the per-group scale reads
 // (16 rows x 4 bytes, 16 cache lines per instruction) out of the vector memory
 // pipeline, which they would otherwise congest as much as the weights do.
 // Otherwise (any G) one load per row and group.
 template <int WFMT, int GS, int NB = 2>
 struct GroupScales {
-  static constexpr bool kPreload = kIsW4<WFMT> && GS > 0 && GS % 16 == 0;
+  static constexpr bool kPreload = kIsW4<WFMT> && GS > 0 && GS % 4 == 0;
   static constexpr int kPerLane = kPreload ? GS / 4 : 1;
   float v[NB][kPerLane];
   const ScaleT<WFMT>* row[NB];
@@ -422,8 +448,8 @@ __device__ __forceinline__ void unit_columns(int N, int u, int (&col)[NB]) {
 }
 
 // Where a wave sweep reads its activation rows: global memory (row r of the
-// tile at a_q + (row0 + r) K) or LDS (row r at a_q + r * a_stride, a_q an LDS
-// address).
+// tile at a_q + (row0 + r) a_stride, a_stride = K when 0) or LDS (row r at
+// a_q + r * a_stride, a_q an LDS address).
 enum ASource { kAGlobal = 0, kALds = 1 };
 
 // One K sweep of a wave unit over the 16-row block rb of a tile (rows row0 ..
@@ -443,7 +469,7 @@ __device__ __forceinline__ void wave_sweep(v4f (&acc)[NB], const uint8_t* a_q, i
   const bool a_ok = 16 * rb + ln < rows;
   const int a_row = a_ok ? 16 * rb + ln : 0;
   const uint8_t* a_src = (ASRC == kALds) ? a_q + a_row * a_stride + kb * 32
-                                         : a_q + int64_t(row0 + a_row) * K + kb * 32;
+                                         : a_q + int64_t(row0 + a_row) * (a_stride ? a_stride : K) + kb * 32;
   constexpr int kDepth = Depth<WFMT>::value;
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -507,6 +533,52 @@ __device__ __forceinline__ void wave_sweep(v4f (&acc)[NB], const uint8_t* a_q, i
   } else {
     pipeline<kDepth, GS, true>(G, issue, consume);
   }
+}
+
+// ------------------------------------------------------ K-split wave units
+// A K-split unit is one workgroup whose wave q sweeps the groups
+// [q G / 4, (q + 1) G / 4) of the unit's K (the K quarters); the partial sums
+// meet in LDS.  A unit then streams its weight rows on all four SIMDs of a CU
+// at once and ends about four times sooner than as one wave, so the
+// dispatcher balances the CUs at that finer granularity (the end of a launch
+// is no longer set by the slowest of thousands of long waves).
+
+// groups of quarter q of G: [g0, g0 + n)
+__device__ __forceinline__ int quarter_g0(int G, int q) { return (q * G) >> 2; }
+__device__ __forceinline__ int quarter_groups(int G, int q) { return (((q + 1) * G) >> 2) - ((q * G) >> 2); }
+
+// Moves this wave's weight-row and scale pointers to the first group g0 of
+// its quarter.
+template <int WFMT, int NB>
+__device__ __forceinline__ void quarter_rows(int g0, const uint8_t* (&wrow)[NB],
+                                             const ScaleT<WFMT>* (&srow)[NB]) {
+  constexpr int kGroupBytes = kIsW4<WFMT> ? 64 : 128;   // bytes of one row's 128-K group
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    wrow[j] += g0 * kGroupBytes;
+    if constexpr (kIsW4<WFMT>) srow[j] += g0;             // per-group scales; FP8-row: per row
+  }
+}
+
+// Sums the four waves' partial accumulators into wave 0 in the fixed order
+// acc0 + (acc1 + (acc2 + acc3)), through red (NB x 64 v4f of LDS).  Every
+// wave of the workgroup calls it (it holds barriers); afterwards red is free.
+template <int NB>
+__device__ __forceinline__ void quarter_reduce(v4f (&acc)[NB], v4f* red, int q, int lane) {
+#pragma unroll
+  for (int step = 3; step >= 1; --step) {
+    if (q == step) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        red[j * kWave + lane] = (step == 3) ? acc[j] : acc[j] + red[j * kWave + lane];
+    }
+    __syncthreads();
+  }
+  if (q == 0) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j] = acc[j] + red[j * kWave + lane];
+  }
+  __syncthreads();
 }
 
 }  // namespace

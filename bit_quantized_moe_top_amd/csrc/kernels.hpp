@@ -14,10 +14,6 @@ constexpr int kPlanHeader = 16;
 enum PlanWord { kPlanR = 0, kPlanE = 1, kPlanActive = 2, kPlanTiles = 3, kPlanT = 4, kPlanK = 5,
                 kPlanDropped = 6 };
 
-// Largest R for which the expert MLP's down GEMM quantizes h itself (every tile
-// then fits one 64-row MFMA tile).
-constexpr int kMlpMaxRows = MOEQ_TILE_M;
-
 struct PlanView {
   int32_t* base;
   int32_t* offsets;      // [E+1]
@@ -120,8 +116,7 @@ hipError_t launch_front(const float* logits, const float* bias, int T, int E, in
                         uint8_t* x_q, float* x_s, uint8_t* xp_q, float* xp_s, void* plan,
                         hipStream_t stream);
 
-// gate/up GEMM + SiLU, FP8 quantization of h and down GEMM: two launches for
-// R <= kMlpMaxRows (the down GEMM quantizes h), three otherwise.
+// gate/up GEMM + SiLU, FP8 quantization of h and down GEMM (three launches)
 hipError_t launch_expert_mlp(int wfmt, const uint8_t* xp_q, const float* xp_s, const void* plan,
                              int E,
                              int R, const uint8_t* w13, const void* s13, const uint8_t* w2,

@@ -86,8 +86,8 @@ gemm_nvfp4_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int
   const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6));
   const int tile = unit / units_per_tile;
   const int u = unit - tile * units_per_tile;
-  if (tile >= plan[kPlanTiles]) return;                 // wave-uniform
-  const TileInfo ti = tile_info(plan, E, R, tile);
+  TileInfo ti;
+  if (!tile_info(plan, E, R, tile, ti)) return;   // wave-uniform
   // weight slab of the tile's expert; experts stored in another format are skipped
   const int slab = slab_of ? slab_of[ti.e] : ti.e;
   if (slab < 0) return;                                 // wave-uniform
