@@ -3,8 +3,10 @@
 // launch for small batches.
 //
 // At decode-sized T the separate launches are almost pure latency (a few
-// microseconds each for a few kilobytes of work).  One 1024-thread workgroup
-// does all of it in three phases separated by two barriers:
+// microseconds each for a few kilobytes of work).  1024-thread workgroups do
+// all of it in three phases separated by two barriers -- one workgroup per row
+// when R = T k <= 64 (each routing every token and building the plan for
+// itself), else one workgroup for all rows:
 //   1. the waves of each row load their 8-element chunks of x into registers;
 //      waves t < T route token t (expert ids into LDS); each wave then writes
 //      the max |x| of its chunks to LDS;
@@ -37,6 +39,13 @@ __host__ __device__ inline int front_waves_per_row(int T, int H) {
   return wpr * cap >= cpr ? wpr : 0;
 }
 
+// With R <= 64 the launch takes one workgroup per row (T > 1): each routes
+// every token and builds the plan in LDS (the routing and the plan are a few
+// microseconds of latency, the same in every workgroup), and quantizes and
+// places only its own row, so the VALU work of the codes spreads over T CUs;
+// workgroup 0 alone stores the routing and the plan.
+__host__ __device__ inline bool front_per_row(int T, int k) { return T > 1 && T * k <= kWave; }
+
 template <typename XT, int NS>
 __global__ void __launch_bounds__(kPlanThreads)
 front_small_kernel(const float* __restrict__ logits, const float* __restrict__ bias, int T, int E,
@@ -50,44 +59,73 @@ front_small_kernel(const float* __restrict__ logits, const float* __restrict__ b
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = T * k;
   const int cpr = H >> 3;                     // 8-element chunks per row
-  const int wpr = front_waves_per_row(T, H);
-  const int row = wave / wpr, sub = wave - row * wpr;
+  // one row per workgroup (several workgroups), or all rows in one
+  const bool per_row = gridDim.x > 1;
+  const bool lead = blockIdx.x == 0;          // stores the routing and the plan
+  const int wpr = front_waves_per_row(per_row ? 1 : T, H);
+  int row, sub;
+  if (per_row) {
+    row = wave < wpr ? int(blockIdx.x) : T;
+    sub = wave;
+  } else {
+    row = wave / wpr;
+    sub = wave - row * wpr;
+  }
+  const int w0 = per_row ? 0 : row * wpr;     // first wave of the row
   const bool qrow = row < T;                  // this wave quantizes part of row `row`
   const auto chunk = [&](int i) { return (i * wpr + sub) * kWave + lane; };
 
-  // ---- phase 1: chunk loads in flight, routing, per-wave max |x|
+  // ---- phase 1: chunk loads in flight, routing, per-wave max |x|.  Every
+  // global load of the kernel is issued here, unconditionally (clamped
+  // indices; lanes without a chunk drop theirs from the maximum), and every
+  // global store comes after the last load is consumed: a wait for a load
+  // also waits for the stores issued before it.
   XChunk<XT> xc[kFrontChunksPerThread];
+  if (T > 0) {                                  // T = 0: x holds no row to read
+    const int64_t xrow = min(row, T - 1);
 #pragma unroll
-  for (int i = 0; i < kFrontChunksPerThread; ++i)
-    if (qrow && chunk(i) < cpr) xc[i].load(x + int64_t(row) * H + chunk(i) * 8);
-  for (int t = wave; t < T; t += kPlanWaves) {
-    const int e = route_token_wave<NS>(logits + int64_t(t) * E, bias, E, k, renormalize,
-                                       ids + int64_t(t) * k, w + int64_t(t) * k, lane);
-    if (lane < k) s_ids[t * k + lane] = e;
+    for (int i = 0; i < kFrontChunksPerThread; ++i)
+      xc[i].load(x + xrow * H + min(chunk(i), cpr - 1) * 8);
   }
+  const bool router = wave < T;                 // T <= kFrontSmallT <= kPlanWaves
+  int my_e = 0;
+  float my_w = 0.0f;
+  if (router)
+    my_e = route_token_values<NS>(logits + int64_t(wave) * E, bias, E, k, renormalize, lane, my_w);
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < kFrontChunksPerThread; ++i) {
-    if (qrow && chunk(i) < cpr) {
-      float v[8];
-      xc[i].values(v);
+    float v[8];
+    xc[i].values(v);
+    const bool mine = qrow && chunk(i) < cpr;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    }
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, mine ? fabsf(v[j]) : 0.0f);
   }
   amax = wave_max(amax);
   if (lane == 0) s_part[wave] = amax;
+  if (router && lane < k) {
+    if (lead) {
+      ids[wave * k + lane] = my_e;
+      w[wave * k + lane] = my_w;
+    }
+    s_ids[wave * k + lane] = my_e;
+  }
   lds_barrier();
 
-  // ---- phase 2: plan, and E4M3 codes of this thread's chunks
-  if (R <= kWave && wave == kPlanWaves - 1)
+  // ---- phase 2: plan, and E4M3 codes of this thread's chunks.  The plan wave
+  // runs at raised priority: it shares its SIMD with quantizing waves, and the
+  // plan, not the codes, is what phase 3 waits for.
+  if (R <= kWave && wave == kPlanWaves - 1) {
+    __builtin_amdgcn_s_setprio(2);
     plan_build_wave<NS>(s_ids, T, k, E, plan, reinterpret_cast<unsigned long long*>(smem),
-                        smem + 2 * E, s_pos, lane);
+                        smem + 2 * E, s_pos, lane, lead);
+    __builtin_amdgcn_s_setprio(0);
+  }
   float scale = 0.0f;
   uint2 codes[kFrontChunksPerThread] = {};
   if (qrow) {
     float m = 0.0f;
-    for (int i = 0; i < wpr; ++i) m = fmaxf(m, s_part[row * wpr + i]);
+    for (int i = 0; i < wpr; ++i) m = fmaxf(m, s_part[w0 + i]);
     scale = fp8_scale(m);
 #pragma unroll
     for (int i = 0; i < kFrontChunksPerThread; ++i) {
@@ -136,8 +174,9 @@ hipError_t launch_small(const float* logits, const float* bias, int T, int E, in
       (err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(lds))) != hipSuccess)
     return err;
-  hipLaunchKernelGGL(fn, dim3(1), dim3(kPlanThreads), lds, stream, logits, bias, T, E, k,
-                     renormalize, x, H, ids, w, x_q, x_s, xp_q, xp_s, plan);
+  hipLaunchKernelGGL(fn, dim3(front_per_row(T, k) ? unsigned(T) : 1u), dim3(kPlanThreads), lds,
+                     stream, logits, bias, T, E, k, renormalize, x, H, ids, w, x_q, x_s, xp_q,
+                     xp_s, plan);
   return hipGetLastError();
 }
 
@@ -147,7 +186,7 @@ hipError_t launch_front(const float* logits, const float* bias, int T, int E, in
                         int renormalize, const void* x, int x_dtype, int H, int32_t* ids, float* w,
                         uint8_t* x_q, float* x_s, uint8_t* xp_q, float* xp_s, void* plan,
                         hipStream_t stream) {
-  if (T > kFrontSmallT || front_waves_per_row(T, H) == 0) {
+  if (T > kFrontSmallT || front_waves_per_row(front_per_row(T, k) ? 1 : T, H) == 0) {
     // routing, then the plan, then x quantized once per token straight into
     // x_q and its k plan positions (rows of <= 4096 elements)
     hipError_t err;

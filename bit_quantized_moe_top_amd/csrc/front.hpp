@@ -44,23 +44,27 @@ __device__ __forceinline__ int wave_best(uint32_t key, int idx, uint32_t* best_k
 
 // One wave routes one token.  k rounds of a wave-wide argmax pick the experts
 // best first; the order (score descending, expert index ascending) makes ties go
-// to the lower index and the result independent of the reduction order.  Lanes
-// j < k write slot j.  Returns the expert chosen in slot `lane` (valid for lane < k).
+// to the lower index and the result independent of the reduction order.
+// Returns the expert chosen in slot `lane` and its weight in w_out (valid for
+// lane < k); nothing is stored.
 template <int NS>
-__device__ __forceinline__ int route_token_wave(const float* row, const float* bias, int E, int k,
-                                                int renormalize, int32_t* ids_row, float* w_row,
-                                                int lane) {
-  float s[NS];
+__device__ __forceinline__ int route_token_values(const float* row, const float* bias, int E,
+                                                  int k, int renormalize, int lane, float& w_out) {
+  // every load issued before the first use (clamped indices, no branch around
+  // them), so the NS slots cost one memory latency, not NS in a row; the bias
+  // is added only when given (adding 0 would turn -0 into +0)
+  float s[NS], b[NS];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int e = j * kWave + lane;
-    float v = -INFINITY;
-    if (e < E) {
-      v = row[e];
-      if (bias) v = v + bias[e];
-    }
-    s[j] = v;
+  for (int j = 0; j < NS; ++j) s[j] = row[min(j * kWave + lane, E - 1)];
+  if (bias) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) b[j] = bias[min(j * kWave + lane, E - 1)];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) s[j] = s[j] + b[j];
   }
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+    if (j * kWave + lane >= E) s[j] = -INFINITY;
   uint32_t key[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) key[j] = (j * kWave + lane < E) ? score_key(s[j]) : 0u;
@@ -105,9 +109,20 @@ __device__ __forceinline__ int route_token_wave(const float* row, const float* b
 #pragma unroll
   for (int r = 1; r < MOEQ_MAX_TOPK; ++r)
     if (r == lane) { v = sel_v[r]; e = sel_e[r]; }
+  w_out = expf(v - smax) / den;
+  return e;
+}
+
+// route_token_values, with lanes j < k writing slot j to ids_row and w_row.
+template <int NS>
+__device__ __forceinline__ int route_token_wave(const float* row, const float* bias, int E, int k,
+                                                int renormalize, int32_t* ids_row, float* w_row,
+                                                int lane) {
+  float wt;
+  const int e = route_token_values<NS>(row, bias, E, k, renormalize, lane, wt);
   if (lane < k) {
     ids_row[lane] = e;
-    w_row[lane] = expf(v - smax) / den;
+    w_row[lane] = wt;
   }
   return e;
 }
@@ -377,11 +392,13 @@ __device__ __forceinline__ void lds_wave_sync() {
 // offsets, and ballots the active list.  With at most 64 rows every active
 // expert owns exactly one tile.  The result equals plan_build_workgroup's.
 // NS: passes of 64 experts covering E.  s_mask: E 64-bit words of LDS, s_off:
-// E ints of LDS; s_pos[r] receives row_pos[r].
+// E ints of LDS; s_pos[r] receives row_pos[r].  With write_plan false the plan
+// is only computed (s_pos), not stored.
 template <int NS>
 __device__ __forceinline__ void plan_build_wave(const int* s_ids, int T, int k, int E,
                                                 int32_t* plan, unsigned long long* s_mask,
-                                                int* s_off, int* s_pos, int lane) {
+                                                int* s_off, int* s_pos, int lane,
+                                                bool write_plan = true) {
   const int R = T * k;
   PlanView pv = plan_view(plan, E, R);
   const int e = lane < R ? s_ids[lane] : -1;
@@ -404,10 +421,10 @@ __device__ __forceinline__ void plan_build_wave(const int* s_ids, int T, int k, 
     carry += readlane(incl, kWave - 1);
     const uint64_t nz = __ballot(c > 0);
     if (x < E) {
-      pv.offsets[x] = off;
+      if (write_plan) pv.offsets[x] = off;
       s_off[x] = off;
     }
-    if (c > 0) {
+    if (c > 0 && write_plan) {
       const int a = act_carry + __popcll(nz & ((1ull << lane) - 1ull));
       pv.active[a] = x;
       pv.tile_expert[a] = x;
@@ -415,7 +432,7 @@ __device__ __forceinline__ void plan_build_wave(const int* s_ids, int T, int k, 
     }
     act_carry += __popcll(nz);
   }
-  if (lane == 0) {
+  if (lane == 0 && write_plan) {
     pv.offsets[E] = carry;
     plan[kPlanR] = R;
     plan[kPlanE] = E;
@@ -425,15 +442,15 @@ __device__ __forceinline__ void plan_build_wave(const int* s_ids, int T, int k, 
     plan[kPlanK] = k;
     plan[kPlanDropped] = dropped;
   }
-  if (lane > kPlanDropped && lane < kPlanHeader) plan[lane] = 0;
+  if (lane > kPlanDropped && lane < kPlanHeader && write_plan) plan[lane] = 0;
   lds_wave_sync();
   if (lane < R) {
     int p = -1;
     if (valid) {
       p = s_off[e] + __popcll(s_mask[e] & ((1ull << lane) - 1ull));
-      pv.sorted_rows[p] = lane;
+      if (write_plan) pv.sorted_rows[p] = lane;
     }
-    pv.row_pos[lane] = p;
+    if (write_plan) pv.row_pos[lane] = p;
     s_pos[lane] = p;
   }
 }
