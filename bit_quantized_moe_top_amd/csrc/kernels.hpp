@@ -116,7 +116,8 @@ hipError_t launch_front(const float* logits, const float* bias, int T, int E, in
                         uint8_t* x_q, float* x_s, uint8_t* xp_q, float* xp_s, void* plan,
                         hipStream_t stream);
 
-// gate/up GEMM + SiLU, FP8 quantization of h and down GEMM (three launches)
+// gate/up GEMM + SiLU, FP8 quantization of h and down GEMM: two launches for
+// R <= 64 and I <= 2048 (the down GEMM quantizes h), three otherwise.
 hipError_t launch_expert_mlp(int wfmt, const uint8_t* xp_q, const float* xp_s, const void* plan,
                              int E,
                              int R, const uint8_t* w13, const void* s13, const uint8_t* w2,

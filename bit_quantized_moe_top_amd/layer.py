@@ -2,7 +2,8 @@
 
     [router logits, when the layer holds the router weights]
       -> route + quantize x + permute (one call; one launch for T <= 16)
-      -> expert MLP: gate/up GEMM (+SiLU) -> quantize h -> down GEMM (one call)
+      -> expert MLP: gate/up GEMM (+SiLU) -> quantize h -> down GEMM (one call;
+         two launches for decode-sized batches)
       -> combine (+ shared experts)
 
 Only orchestration lives here: buffers are torch allocations, reused across
