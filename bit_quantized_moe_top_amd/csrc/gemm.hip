@@ -33,7 +33,7 @@ gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
   // still take a vector memory instruction each
   constexpr int kStageRows = 4, kStageK = 1024, kStageStride = kStageK + 16;
   __shared__ __align__(16) uint8_t a_stage[4][kStageRows][kStageStride];
-  __shared__ v4f red[NB * kWave];
+  __shared__ v4f red[3 * NB * kWave];           // quarter sums of waves 1..3
   const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int ln = lane & 15, kb = lane >> 4;
   const int units_per_tile = N / (16 * NB);
@@ -87,7 +87,7 @@ gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
       wave_sweep<WFMT, NB, GQ, false>(acc, a_q + g0 * 128, kq, ti.row0, ti.rows, rb, wrow, srow,
                                       ln, kb, [] {}, K);
     }
-    quarter_reduce<NB>(acc, red, q, lane);
+    quarter_reduce<NB>(acc, red, q, lane, rb + 1 < nrb);
     if (q == 0)
       store_block<WFMT, EPI, NB>(acc, rb, ti.row0, ti.rows, [a_s](int p) { return a_s[p]; },
                                  srow, col, ln, kb, N, out, out_f32);

@@ -561,24 +561,26 @@ __device__ __forceinline__ void quarter_rows(int g0, const uint8_t* (&wrow)[NB],
 }
 
 // Sums the four waves' partial accumulators into wave 0 in the fixed order
-// acc0 + (acc1 + (acc2 + acc3)), through red (NB x 64 v4f of LDS).  Every
-// wave of the workgroup calls it (it holds barriers); afterwards red is free.
+// acc0 + (acc1 + (acc2 + acc3)): waves 1..3 write theirs to red (3 x NB x 64
+// v4f of LDS), one barrier, wave 0 adds.  Every wave of the workgroup calls it;
+// red is free again after the next barrier of the caller (or this function's
+// next call, whose writes come after wave 0's reads only if the caller
+// separates them -- callers looping over blocks pass again_after = true).
 template <int NB>
-__device__ __forceinline__ void quarter_reduce(v4f (&acc)[NB], v4f* red, int q, int lane) {
+__device__ __forceinline__ void quarter_reduce(v4f (&acc)[NB], v4f* red, int q, int lane,
+                                               bool again_after) {
+  if (q > 0) {
 #pragma unroll
-  for (int step = 3; step >= 1; --step) {
-    if (q == step) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        red[j * kWave + lane] = (step == 3) ? acc[j] : acc[j] + red[j * kWave + lane];
-    }
-    __syncthreads();
-  }
-  if (q == 0) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) acc[j] = acc[j] + red[j * kWave + lane];
+    for (int j = 0; j < NB; ++j) red[((q - 1) * NB + j) * kWave + lane] = acc[j];
   }
   __syncthreads();
+  if (q == 0) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      acc[j] = acc[j] + (red[j * kWave + lane] +
+                         (red[(NB + j) * kWave + lane] + red[(2 * NB + j) * kWave + lane]));
+  }
+  if (again_after) __syncthreads();
 }
 
 }  // namespace

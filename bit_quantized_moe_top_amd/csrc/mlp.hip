@@ -37,7 +37,7 @@ down_hq_kernel(const uint16_t* h, const int32_t* plan, int E, int R, const uint8
   __shared__ __align__(16) uint8_t a_stage[4][kHqRows][kHqStride];   // E4M3 codes
   __shared__ float s_part[4][kHqRows];          // per-quarter max |h| of each row
   __shared__ float s_scale[kHqRows];
-  __shared__ v4f red[2 * kWave];
+  __shared__ v4f red[3 * 2 * kWave];           // quarter sums of waves 1..3
   const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int ln = lane & 15, kb = lane >> 4;
   const int upt = H >> 5;                       // units per tile
@@ -115,13 +115,14 @@ down_hq_kernel(const uint16_t* h, const int32_t* plan, int E, int R, const uint8
     v4f acc[2];
     wave_sweep<WFMT, 2, GQ, true, kALds>(acc, stage, kq, 0, rrows, 0, wrow, srow, ln, kb,
                                          quantize, kHqStride);
-    quarter_reduce<2>(acc, red, q, lane);
+    quarter_reduce<2>(acc, red, q, lane, rb + 1 < nrb);
     if (q == 0)
       store_block<WFMT, MOEQ_EPI_NONE>(acc, rb, ti.row0, ti.rows,
                                        [&](int p) { return s_scale[p - p0]; }, srow, col, ln, kb,
                                        H, o, 0);
-    // s_part and s_scale are rewritten by the next block (quarter_reduce's
-    // barriers already order them after every read of this block)
+    // the next block rewrites s_part after every wave has passed this block's
+    // reduction barrier (all reads of s_part precede it); s_scale is written
+    // and read by wave 0 alone
   }
 }
 
