@@ -120,27 +120,36 @@ shared_gemm_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------- large tiles
-// For the shared experts' prefill shapes (M in the thousands, N % 256 == 0,
-// K % 64 == 0): workgroup tile 128 rows of a x 256 weight rows, K advancing 64
-// per barrier; four waves in a 2 x 2 arrangement, each owning 64 rows x 8
-// column blocks of 16 (32 MFMAs of 16x16x32 per 32-K sub-step, 128 fp32
-// accumulators per lane).  Per sub-step a wave reads 4 A and 8 B operands
-// (12 x 16 B per lane) from LDS for 32 MFMAs -- a third of the LDS bytes per
-// MFMA of the small-tile kernel -- and the next step's global loads (12 x 16 B
-// per thread) are in flight during the current step's MFMAs.  With EPI_SILU_MUL
-// the 256 weight rows are 128 gate rows and their 128 up rows; column block q
-// of a wave (q < 4) is gate, q + 4 the matching up block.
-constexpr int kBM2 = 128, kBN2 = 256, kBK2 = 64;
-constexpr int kStride2 = kBK2 + 8;         // bf16 per LDS row: 144 B, conflict-free 16 B reads
+// For the shared experts' prefill shapes (M in the thousands, K % 32 == 0):
+// workgroup tile 128 rows of a x BN weight rows (BN = 256, or 128 when 256
+// would leave fewer than two workgroups per CU), K advancing 32 per barrier
+// through double-buffered LDS (61 KB at BN = 256: two workgroups per CU).
+// Four waves in a 2 x 2 arrangement, each owning 64 rows x BN/2 columns
+// (NQ = BN/32 column blocks of 16; 4 NQ MFMAs of 16x16x32 per K step, 16 NQ
+// fp32 accumulators per lane).  Per step a wave reads 4 A and NQ B operands
+// (16 B per lane each) from LDS, and the next step's global loads are in
+// flight during the current step's MFMAs.  With EPI_SILU_MUL the BN weight
+// rows are BN/2 gate rows and their BN/2 up rows; column block q of a wave
+// (q < NQ/2) is gate, q + NQ/2 the matching up block.
+constexpr int kBM2 = 128, kBK2 = 32;
+constexpr int kStride2 = kBK2 + 8;         // bf16 per LDS row: 80 B, conflict-free 16 B reads
 
-template <int EPI>
-__global__ void __launch_bounds__(kT, 1)
+template <int BN>
+__host__ __device__ constexpr size_t big_lds_bytes() {
+  return size_t(2) * (kBM2 + BN) * kStride2 * sizeof(uint16_t);
+}
+
+template <int EPI, int BN>
+__global__ void __launch_bounds__(kT, 2)
 shared_gemm_big_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ w, int M,
                        int N, int K, uint16_t* __restrict__ out) {
+  static_assert(BN == 256 || BN == 128, "tile width");
+  constexpr int NQ = BN / 32;              // column blocks per wave
+  constexpr int BP = BN / 64;              // B staging passes of 64 rows
   extern __shared__ __attribute__((aligned(16))) uint16_t smem2[];
   uint16_t* As = smem2;                                  // [2][kBM2 * kStride2]
-  uint16_t* Bs = smem2 + 2 * kBM2 * kStride2;            // [2][kBN2 * kStride2]
-  const int n_ntiles = N / kBN2;
+  uint16_t* Bs = smem2 + 2 * kBM2 * kStride2;            // [2][BN * kStride2]
+  const int n_ntiles = N / BN;
   const int mt = blockIdx.x / n_ntiles;
   const int nt = blockIdx.x - mt * n_ntiles;
   const int m0 = mt * kBM2;
@@ -148,65 +157,64 @@ shared_gemm_big_kernel(const uint16_t* __restrict__ a, const uint16_t* __restric
   const int wm = wave >> 1, wn = wave & 1;
   const int ln = lane & 15, kq = lane >> 4;
 
-  // staging: 16-byte chunk c of the step's tiles -> (row c / 8, piece c % 8);
-  // A: chunks tid + 256 i (i < 4, rows tid / 8 + 32 i), B: chunks tid + 256 i
-  // (i < 8; rows 32 apart are 32 K elements apart).
-  const int srow = tid >> 3, spiece = (tid & 7) * 8;
-  const int64_t row_step = int64_t(32) * K;
+  // staging: thread -> (row tid / 4, 16-byte piece tid % 4) of each 64-row
+  // pass; A takes two passes, B takes BP (for EPI_SILU_MUL the first BP/2 are
+  // gate rows, the rest the matching up rows)
+  const int srow = tid >> 2, spiece = (tid & 3) * 8;
+  const int64_t pass_step = int64_t(64) * K;
   // rows past M re-read row M - 1: their results are never stored, and rows
   // of a product do not mix
   const uint16_t* a_r0 = a + int64_t(min(m0 + srow, M - 1)) * K + spiece;
-  const uint16_t* a_r1 = a + int64_t(min(m0 + srow + 32, M - 1)) * K + spiece;
-  const uint16_t* a_r2 = a + int64_t(min(m0 + srow + 64, M - 1)) * K + spiece;
-  const uint16_t* a_r3 = a + int64_t(min(m0 + srow + 96, M - 1)) * K + spiece;
-  const uint16_t* w_base;        // rows of B chunks i < 4 (gate rows for EPI_SILU_MUL)
-  const uint16_t* w_base_hi;     // rows of B chunks i >= 4 (the matching up rows)
+  const uint16_t* a_r1 = a + int64_t(min(m0 + srow + 64, M - 1)) * K + spiece;
+  const uint16_t* w_lo;          // passes 0 .. BP/2 - 1
+  const uint16_t* w_hi;          // passes BP/2 .. BP - 1
   if (EPI == MOEQ_EPI_SILU_MUL) {
-    w_base = w + int64_t(nt * 128 + srow) * K + spiece;
-    w_base_hi = w + int64_t((N >> 1) + nt * 128 + srow) * K + spiece;
+    w_lo = w + int64_t(nt * (BN / 2) + srow) * K + spiece;
+    w_hi = w + int64_t((N >> 1) + nt * (BN / 2) + srow) * K + spiece;
   } else {
-    w_base = w + int64_t(nt * kBN2 + srow) * K + spiece;
-    w_base_hi = w_base + 4 * row_step;
+    w_lo = w + int64_t(nt * BN + srow) * K + spiece;
+    w_hi = w_lo + (BP / 2) * pass_step;
   }
   // B-tile row of column block q of this wave
-  int cb[8];
+  int cb[NQ];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    if (EPI == MOEQ_EPI_SILU_MUL) cb[q] = (q < 4 ? 0 : 128) + 64 * wn + 16 * (q & 3);
-    else cb[q] = 128 * wn + 16 * q;
+  for (int q = 0; q < NQ; ++q) {
+    if (EPI == MOEQ_EPI_SILU_MUL) cb[q] = (q < NQ / 2 ? 0 : BN / 2) + (BN / 4) * wn + 16 * (q % (NQ / 2));
+    else cb[q] = (BN / 2) * wn + 16 * q;
   }
 
-  v4f acc[4][8];
+  v4f acc[4][NQ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[i][q] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < NQ; ++q) acc[i][q] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3, rb4, rb5, rb6, rb7;
+  // staging registers as scalars (arrays captured by lambdas stay in scratch);
+  // rb2, rb3 are used only when BN = 256
+  uint4 ra0, ra1, rb0, rb1, rb2 = {}, rb3 = {};
 #define SG_LD(p) (*reinterpret_cast<const uint4*>(p))
 #define SG_GLOAD(k0)                                                             \
   do {                                                                           \
     ra0 = SG_LD(a_r0 + (k0));                                                    \
     ra1 = SG_LD(a_r1 + (k0));                                                    \
-    ra2 = SG_LD(a_r2 + (k0));                                                    \
-    ra3 = SG_LD(a_r3 + (k0));                                                    \
-    rb0 = SG_LD(w_base + (k0));                                                  \
-    rb1 = SG_LD(w_base + row_step + (k0));                                       \
-    rb2 = SG_LD(w_base + 2 * row_step + (k0));                                   \
-    rb3 = SG_LD(w_base + 3 * row_step + (k0));                                   \
-    rb4 = SG_LD(w_base_hi + (k0));                                               \
-    rb5 = SG_LD(w_base_hi + row_step + (k0));                                    \
-    rb6 = SG_LD(w_base_hi + 2 * row_step + (k0));                                \
-    rb7 = SG_LD(w_base_hi + 3 * row_step + (k0));                                \
+    if (BP == 4) {                                                               \
+      rb0 = SG_LD(w_lo + (k0));                                                  \
+      rb1 = SG_LD(w_lo + pass_step + (k0));                                      \
+      rb2 = SG_LD(w_hi + (k0));                                                  \
+      rb3 = SG_LD(w_hi + pass_step + (k0));                                      \
+    } else {                                                                     \
+      rb0 = SG_LD(w_lo + (k0));                                                  \
+      rb1 = SG_LD(w_hi + (k0));                                                  \
+    }                                                                            \
   } while (0)
-#define SG_ST(base, r, v) (*reinterpret_cast<uint4*>(&(base)[((r) * 32 + srow) * kStride2 + spiece]) = (v))
+#define SG_ST(base, pass, v) (*reinterpret_cast<uint4*>((base) + (pass) * 64 * kStride2) = (v))
 #define SG_SSTORE(buf)                                                           \
   do {                                                                           \
-    uint16_t* as_ = As + (buf) * kBM2 * kStride2;                                \
-    uint16_t* bs_ = Bs + (buf) * kBN2 * kStride2;                                \
-    SG_ST(as_, 0, ra0); SG_ST(as_, 1, ra1); SG_ST(as_, 2, ra2); SG_ST(as_, 3, ra3); \
-    SG_ST(bs_, 0, rb0); SG_ST(bs_, 1, rb1); SG_ST(bs_, 2, rb2); SG_ST(bs_, 3, rb3); \
-    SG_ST(bs_, 4, rb4); SG_ST(bs_, 5, rb5); SG_ST(bs_, 6, rb6); SG_ST(bs_, 7, rb7); \
+    uint16_t* as_ = As + (buf) * kBM2 * kStride2 + srow * kStride2 + spiece;     \
+    uint16_t* bs_ = Bs + (buf) * BN * kStride2 + srow * kStride2 + spiece;       \
+    SG_ST(as_, 0, ra0); SG_ST(as_, 1, ra1);                                      \
+    SG_ST(bs_, 0, rb0); SG_ST(bs_, 1, rb1);                                      \
+    if (BP == 4) { SG_ST(bs_, 2, rb2); SG_ST(bs_, 3, rb3); }                     \
   } while (0)
 
   SG_GLOAD(0);
@@ -219,25 +227,20 @@ shared_gemm_big_kernel(const uint16_t* __restrict__ a, const uint16_t* __restric
     if (more) SG_GLOAD((s + 1) * kBK2);
     __builtin_amdgcn_sched_barrier(0);
     const uint16_t* A = As + buf * kBM2 * kStride2;
-    const uint16_t* B = Bs + buf * kBN2 * kStride2;
+    const uint16_t* B = Bs + buf * BN * kStride2;
+    const int kk = kq * 8;
+    v8bf aop[4];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int kk = sub * 32 + kq * 8;
-      v8bf aop[4];
+    for (int i = 0; i < 4; ++i)
+      aop[i] = *reinterpret_cast<const v8bf*>(&A[(64 * wm + 16 * i + ln) * kStride2 + kk]);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const v8bf bop = *reinterpret_cast<const v8bf*>(&B[(cb[q] + ln) * kStride2 + kk]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        aop[i] = *reinterpret_cast<const v8bf*>(&A[(64 * wm + 16 * i + ln) * kStride2 + kk]);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const v8bf bop = *reinterpret_cast<const v8bf*>(&B[(cb[q] + ln) * kStride2 + kk]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[i], bop, acc[i][q], 0, 0, 0);
-      }
-      // keep each sub-step's LDS reads next to its MFMAs (hoisting them all
-      // ahead would not fit the register file)
-      __builtin_amdgcn_sched_barrier(0);
+        acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[i], bop, acc[i][q], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (more) {
       __syncthreads();                 // every wave is done reading buf ^ 1 (step s - 1)
       SG_SSTORE(buf ^ 1);
@@ -254,12 +257,12 @@ shared_gemm_big_kernel(const uint16_t* __restrict__ a, const uint16_t* __restric
       if (EPI == MOEQ_EPI_SILU_MUL) {
         uint16_t* o = out + int64_t(m) * (N >> 1);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          o[nt * 128 + cb[q] + ln] = f32_to_bf16(silu_f32(acc[i][q][v]) * acc[i][q + 4][v]);
+        for (int q = 0; q < NQ / 2; ++q)
+          o[nt * (BN / 2) + cb[q] + ln] = f32_to_bf16(silu_f32(acc[i][q][v]) * acc[i][q + NQ / 2][v]);
       } else {
         uint16_t* o = out + int64_t(m) * N;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) o[nt * kBN2 + cb[q] + ln] = f32_to_bf16(acc[i][q][v]);
+        for (int q = 0; q < NQ; ++q) o[nt * BN + cb[q] + ln] = f32_to_bf16(acc[i][q][v]);
       }
     }
   }
@@ -269,21 +272,32 @@ shared_gemm_big_kernel(const uint16_t* __restrict__ a, const uint16_t* __restric
 #undef SG_ST
 #undef SG_SSTORE
 
+template <int BN>
+hipError_t launch_big(const uint16_t* a, const uint16_t* w, int M, int N, int K, int epilogue,
+                      uint16_t* out, hipStream_t stream) {
+  const int64_t blocks = int64_t((M + kBM2 - 1) / kBM2) * (N / BN);
+  const size_t lds = big_lds_bytes<BN>();
+  auto fn = (epilogue == MOEQ_EPI_SILU_MUL) ? shared_gemm_big_kernel<MOEQ_EPI_SILU_MUL, BN>
+                                            : shared_gemm_big_kernel<MOEQ_EPI_NONE, BN>;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(fn, dim3(unsigned(blocks)), dim3(kT), lds, stream, a, w, M, N, K, out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_shared_gemm_bf16(const uint16_t* a, const uint16_t* w, int M, int N, int K,
                                    int epilogue, uint16_t* out, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  if (M >= 256 && N % kBN2 == 0 && K % kBK2 == 0) {
-    const int64_t blocks2 = int64_t((M + kBM2 - 1) / kBM2) * (N / kBN2);
-    const size_t lds = size_t(2) * (kBM2 + kBN2) * kStride2 * sizeof(uint16_t);
-    auto fn = (epilogue == MOEQ_EPI_SILU_MUL) ? shared_gemm_big_kernel<MOEQ_EPI_SILU_MUL>
-                                              : shared_gemm_big_kernel<MOEQ_EPI_NONE>;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(fn, dim3(unsigned(blocks2)), dim3(kT), lds, stream, a, w, M, N, K, out);
-    return hipGetLastError();
+  if (M >= 256 && K % kBK2 == 0) {
+    // 128 x 256 tiles when they give at least two workgroups per CU (512),
+    // else 128 x 128
+    const int64_t mtiles = (M + kBM2 - 1) / kBM2;
+    if (N % 256 == 0 && mtiles * (N / 256) >= 512)
+      return launch_big<256>(a, w, M, N, K, epilogue, out, stream);
+    if (N % 128 == 0) return launch_big<128>(a, w, M, N, K, epilogue, out, stream);
   }
   const int64_t blocks = int64_t((M + kBM - 1) / kBM) * (N / kBNw);
   if (epilogue == MOEQ_EPI_SILU_MUL)

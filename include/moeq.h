@@ -430,7 +430,7 @@ int moe_combine(const uint16_t* o, const void* plan, const float* topk_w, const 
  *   SILU_MUL: out[m, i] = bf16(silu(acc[m, i]) * acc[m, N/2+i])  [M, N/2]
  *
  *   a [M, K] bf16, w [N, K] bf16 (out, in orientation)
- * Limits: M >= 0, K % 64 == 0, N % 128 == 0; a and w 16-byte aligned.
+ * Limits: M >= 0, K % 32 == 0, N % 128 == 0; a and w 16-byte aligned.
  */
 int moe_shared_gemm_bf16(const uint16_t* a, const uint16_t* w, int M, int N, int K, int epilogue,
                          uint16_t* out, void* stream);

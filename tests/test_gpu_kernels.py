@@ -551,11 +551,12 @@ def test_combine(T, k, E, H, shared):
 
 
 # ------------------------------------------------------------- shared GEMM ----
-# M < 256 or N % 256 or K % 64 takes the 32-row kernel, the rest the 128x256 one
-# (ragged last row tile, one K step, several column tiles)
+# M < 256 or K % 32 takes the 128x128 small-tile kernel; the large-tile kernel
+# runs 128x256 tiles when they make >= 512 workgroups, else 128x128 (ragged
+# last row tile, one K step, several column tiles)
 @pytest.mark.parametrize("M,N,K", [(37, 256, 256), (128, 512, 4096), (200, 128, 96),
                                    (256, 256, 64), (300, 512, 320), (777, 1024, 192),
-                                   (513, 768, 4096)])
+                                   (513, 768, 4096), (256, 128, 32), (2000, 8192, 96)])
 def test_shared_gemm_bf16(M, N, K):
     g = torch.Generator().manual_seed(M + N + K)
     a = torch.randn(M, K, generator=g).to(torch.bfloat16)
