@@ -461,7 +461,7 @@ def _expert_mlp(fn_name: str, xp_q, xp_s, plan, E, w13, s13, w2, s2, H, I, out):
 def moe_expert_mlp_w4a8(xp_q: torch.Tensor, xp_s: torch.Tensor, plan: torch.Tensor,
                         w13: torch.Tensor, w13_scales: torch.Tensor, w2: torch.Tensor,
                         w2_scales: torch.Tensor, out: Optional[dict] = None) -> dict:
-    """gate/up GEMM + SiLU, FP8 quantization of h, down GEMM (two launches for R <= 64
+    """gate/up GEMM + SiLU, FP8 quantization of h, down GEMM (two launches for R <= 192
     and I <= 2048, else three).
     w13 [E, 2I, H/2], w13_scales [E, 2I, H/128], w2 [E, H, I/2], w2_scales [E, H, I/128].
     Scales fp32, or both bfloat16 (then moe_expert_mlp_w4a8_bf16s).

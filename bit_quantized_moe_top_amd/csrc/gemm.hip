@@ -275,7 +275,7 @@ hipError_t launch_kernels(const uint8_t* a_q, const float* a_s, const void* plan
                           const uint8_t* w, const ScaleT<WFMT>* w_scale, int N, int K, void* out,
                           int out_f32, hipStream_t stream) {
   const int32_t* p = static_cast<const int32_t*>(plan);
-  if (R <= 64) {
+  if (R <= kWaveMaxRows) {
     // few rows per expert: one workgroup per K-split unit (tile, 16 NB weight rows)
     constexpr int NB = (EPI == MOEQ_EPI_SILU_MUL) ? 2 : MOEQ_WAVE_NB;
     const int64_t units = int64_t(plan_max_tiles(E, R)) * (N / (16 * NB));

@@ -9,6 +9,12 @@
 
 namespace moeq {
 
+// Largest R for which the grouped GEMMs and the expert MLP take the K-split
+// wave units (decode-sized batches, about one row per active expert) instead
+// of the 64-row tile kernel; measured crossover between 192 and 250 at the
+// Inkling-Small shapes with top-6 of 256 experts.
+constexpr int kWaveMaxRows = 192;
+
 // plan word offsets (see moe_plan_size in moeq.h)
 constexpr int kPlanHeader = 16;
 enum PlanWord { kPlanR = 0, kPlanE = 1, kPlanActive = 2, kPlanTiles = 3, kPlanT = 4, kPlanK = 5,
@@ -117,7 +123,7 @@ hipError_t launch_front(const float* logits, const float* bias, int T, int E, in
                         hipStream_t stream);
 
 // gate/up GEMM + SiLU, FP8 quantization of h and down GEMM: two launches for
-// R <= 64 and I <= 2048 (the down GEMM quantizes h), three otherwise.
+// R <= kWaveMaxRows and I <= 2048 (the down GEMM quantizes h), three otherwise.
 hipError_t launch_expert_mlp(int wfmt, const uint8_t* xp_q, const float* xp_s, const void* plan,
                              int E,
                              int R, const uint8_t* w13, const void* s13, const uint8_t* w2,

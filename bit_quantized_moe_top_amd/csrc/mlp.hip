@@ -1,7 +1,7 @@
 // The routed experts' MLP: gate/up GEMM with the SiLU-gated product, per-row
 // FP8 quantization of h, down GEMM.
 //
-// For few routed rows (R <= 64, the decode regime) and I <= 2048 the down GEMM
+// For few routed rows (R <= kWaveMaxRows, the decode regime) and I <= 2048 the down GEMM
 // quantizes h itself, so the MLP is two launches instead of three.  It runs
 // the grouped GEMM's K-split units (one workgroup per (tile, 32 weight rows),
 // wave q sweeping K quarter q).  Before its weight loads each wave loads its
@@ -151,7 +151,7 @@ hipError_t launch_expert_mlp(int wfmt, const uint8_t* xp_q, const float* xp_s, c
   hipError_t err = launch_grouped_gemm(wfmt, xp_q, xp_s, plan, E, R, w13, s13, 2 * I, H,
                                        MOEQ_EPI_SILU_MUL, h, MOEQ_BF16, stream);
   if (err != hipSuccess) return err;
-  if (R <= MOEQ_TILE_M && I <= 4 * kHqMaxQuarter) {
+  if (R <= kWaveMaxRows && I <= 4 * kHqMaxQuarter) {
     switch (wfmt) {
       case kW4G128:
         return launch_down_hq<kW4G128>(h, plan, E, R, w2, static_cast<const float*>(s2), H, I,

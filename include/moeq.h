@@ -364,7 +364,7 @@ int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* pl
  *   moe_grouped_gemm_w4a8(xp_q, xp_s, w13, N = 2I, K = H, SILU_MUL) -> h
  *   quant_fp8_per_token(h)                                          -> h_q, h_s
  *   moe_grouped_gemm_w4a8(h_q, h_s, w2, N = H, K = I, NONE)          -> o (bf16)
- * with bit-identical results.  For R <= MOEQ_TILE_M (decode-sized batches) and
+ * with bit-identical results.  For R <= 192 (decode-sized batches) and
  * I <= 2048 the down GEMM quantizes h itself -- each of its waves quantizes its
  * K quarter of the rows of h into LDS while its weight loads are in flight --
  * so the call makes two launches instead of three; otherwise the three.

@@ -69,7 +69,8 @@ def _fused(c, fmt):
     (12, 4, 8, 4096, 256, None),    # H = 4096 with a narrow expert (unrolled gate/up sweep)
     (4, 6, 8, 256, 2048, 3),        # I = 2048 (unrolled down sweep), a hot expert
     (60, 1, 4, 128, 1024, None),    # many rows per expert: row blocks past four rows
-    (30, 4, 16, 256, 128, None),    # R = 120 > 64: the three-launch path
+    (30, 4, 16, 256, 128, None),    # R = 120: 64-row tiles of the two-launch path
+    (50, 4, 16, 256, 128, None),    # R = 200 > 192: the tile kernels, three launches
     (4, 2, 8, 128, 2560, None),     # I > 2048: the three-launch path
     (4, 6, 24, 256, 640, None),     # I = 640: uneven K quarters (1, 1, 1, 2 groups)
 ])
