@@ -336,8 +336,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the layer shards by experts or by width across GPUs, which this build "
-              f"does not run).", file=sys.stderr)
+              f"(the layer would shard by experts or by width across GPUs; this library "
+              f"runs on one GPU).", file=sys.stderr)
         sys.exit(2)
     import torch
 
