@@ -160,7 +160,9 @@ def time_layer(cfg, n_sets, steps, warmup, dev, graph=False, split_events=False)
         per_call = {}
         for name, s, e in ev:
             per_call.setdefault(name, []).append(s.elapsed_time(e))
-        return {k: 1e3 * sum(v) / len(v) for k, v in per_call.items()}
+        # medians: one stalled call (a rare host or device hiccup) must not
+        # stand for the call's duration
+        return {k: 1e3 * sorted(v)[len(v) // 2] for k, v in per_call.items()}
 
     per_call_us = call_times(split_events)
     # the expert MLP's calls one by one (its gate/up launch is the layer's dominant kernel)
@@ -257,7 +259,7 @@ def time_hybrid(cfg, n_sets, steps, warmup, dev):
     mean_bytes = sum(step_bytes[i % n_sets] for i in range(steps)) / steps
     return {"ms_per_step": ms, "bytes_per_step": mean_bytes,
             "hot_experts_touched": sum(n_hot_touched) / n_sets,
-            "per_call_us": {k: 1e3 * sum(v) / len(v) for k, v in per_call.items()}}
+            "per_call_us": {k: 1e3 * sorted(v)[len(v) // 2] for k, v in per_call.items()}}
 
 
 def measured_traffic(kernel_bytes: float, name: str = "gemm_gate_up_decode_T4_traffic"):

@@ -137,7 +137,7 @@ def plan_fields(plan: torch.Tensor, E: int, R: int) -> dict:
     chunks = max(1, (R + 1023) // 1024)
     o = PLAN_HEADER
     f = {"header": plan[:PLAN_HEADER]}
-    for name, n in (("offsets", E + 1), ("sorted_rows", R), ("row_pos", R), ("active", E),
+    for name, n in (("row_pos", R), ("sorted_rows", R), ("offsets", E + 1), ("active", E),
                     ("tile_expert", max_tiles), ("tile_row0", max_tiles), ("scratch", chunks * E)):
         f[name] = plan[o:o + n]
         o += n

@@ -25,21 +25,35 @@ combine_kernel(const uint16_t* __restrict__ o, const int32_t* __restrict__ plan,
   const int t = blockIdx.x / chunks;
   const int c = ((blockIdx.x - t * chunks) * 256 + threadIdx.x) * 8;
   if (c >= H) return;
-  const int E = plan[kPlanE];
-  const PlanView pv = plan_view(const_cast<int32_t*>(plan), E, T * k);
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int j = 0; j < k; ++j) {
-    const int p = pv.row_pos[t * k + j];
-    if (p < 0) continue;
-    const float wt = w[t * k + j];
-    float v[8];
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(o + int64_t(p) * H + c), v);
+  // row_pos leads the plan after its header: no dependent read of E.  Every
+  // slot's position and weight are loaded before any is used, then every
+  // slot's row, so the combine costs two memory round trips, not 2k.
+  const int32_t* row_pos = plan + kPlanHeader;
+  int pos[MOEQ_MAX_TOPK];
+  float wt[MOEQ_MAX_TOPK];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wt, v[i], acc[i]);
+  for (int j = 0; j < MOEQ_MAX_TOPK; ++j) {
+    pos[j] = j < k ? row_pos[t * k + j] : -1;
+    wt[j] = j < k ? w[t * k + j] : 0.0f;
+  }
+  uint4 raw[MOEQ_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOEQ_MAX_TOPK; ++j)
+    if (pos[j] >= 0) raw[j] = *reinterpret_cast<const uint4*>(o + int64_t(pos[j]) * H + c);
+  uint4 sh = {};
+  if (shared) sh = *reinterpret_cast<const uint4*>(shared + int64_t(t) * H + c);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < MOEQ_MAX_TOPK; ++j) {
+    if (pos[j] < 0) continue;                 // slots past k, or rows dropped by the permute
+    float v[8];
+    bf16x8_to_f32(raw[j], v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wt[j], v[i], acc[i]);
   }
   if (shared) {
     float v[8];
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(shared + int64_t(t) * H + c), v);
+    bf16x8_to_f32(sh, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += v[i];
   }

@@ -22,9 +22,9 @@ enum PlanWord { kPlanR = 0, kPlanE = 1, kPlanActive = 2, kPlanTiles = 3, kPlanT 
 
 struct PlanView {
   int32_t* base;
-  int32_t* offsets;      // [E+1]
+  int32_t* row_pos;      // [R]   (first: located from R alone)
   int32_t* sorted_rows;  // [R]
-  int32_t* row_pos;      // [R]
+  int32_t* offsets;      // [E+1]
   int32_t* active;       // [E]
   int32_t* tile_expert;  // [max_tiles]
   int32_t* tile_row0;    // [max_tiles]
@@ -42,10 +42,10 @@ __host__ __device__ inline int plan_chunks(int R) { return (R + 1023) / 1024 > 0
 __host__ __device__ inline PlanView plan_view(void* plan, int E, int R) {
   PlanView v;
   v.base = static_cast<int32_t*>(plan);
-  v.offsets = v.base + kPlanHeader;
-  v.sorted_rows = v.offsets + (E + 1);
-  v.row_pos = v.sorted_rows + R;
-  v.active = v.row_pos + R;
+  v.row_pos = v.base + kPlanHeader;
+  v.sorted_rows = v.row_pos + R;
+  v.offsets = v.sorted_rows + R;
+  v.active = v.offsets + (E + 1);
   v.tile_expert = v.active + E;
   v.max_tiles = plan_max_tiles(E, R);
   v.tile_row0 = v.tile_expert + v.max_tiles;

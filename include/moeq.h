@@ -79,9 +79,9 @@ const char* moe_status_string(int status);
  * the combine; callers may read it but must not modify it:
  *   [0] R   [1] E   [2] n_active   [3] n_tiles   [4] T   [5] k
  *   [6] number of ids outside [0, E) that were dropped   [7..15] reserved (0)
+ *   row_pos     [R]        routed row r = t*k + j -> sorted position p (-1 if dropped)
+ *   sorted_rows [R]        sorted position p -> routed row r
  *   offsets     [E+1]      offsets[e] = first sorted position of expert e
- *   sorted_rows [R]        sorted position p -> routed row r = t*k + j
- *   row_pos     [R]        routed row r -> sorted position p (-1 if dropped)
  *   active      [E]        experts with at least one row, increasing (n_active used)
  *   tile_expert [max_tiles] expert of each MOEQ_TILE_M-row tile (n_tiles used)
  *   tile_row0   [max_tiles] first sorted position of each tile
