@@ -182,11 +182,20 @@ struct RowQuant {
   uint2 codes[CPL];
   float scale;
   __device__ __forceinline__ void run(const XT* row, int K, int lane) {
+    load(row, K, lane);
+    finish(K, lane);
+  }
+  // the row's loads (to be issued ahead of other memory work)
+  __device__ __forceinline__ void load(const XT* row, int K, int lane) {
     const int chunks = K >> 3;
-    float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
       if (lane + kWave * i < chunks) xc[i].load(row + (lane + kWave * i) * 8);
+  }
+  // max |x|, the scale and the codes of the loaded row
+  __device__ __forceinline__ void finish(int K, int lane) {
+    const int chunks = K >> 3;
+    float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       if (lane + kWave * i < chunks) {

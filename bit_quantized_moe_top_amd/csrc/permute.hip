@@ -88,20 +88,41 @@ plan_scan_kernel(int T, int k, int E, int32_t* __restrict__ plan) {
   const int tid = threadIdx.x;
   if (tid == 0) placed = 0;
   __syncthreads();
-  for (int x = tid; x < E; x += kPlanThreads) {
+  // E <= kPlanThreads: thread x owns expert x.  Up to kRegChunks chunk counts
+  // stay in registers, all loaded before any is used and none reloaded after
+  // the base stores (a load issued after a store also waits for the store).
+  constexpr int kRegChunks = 16;
+  const bool in_regs = n_chunks <= kRegChunks;
+  int nc[kRegChunks];
+  if (tid < E) {
     int s = 0;
-    for (int c = 0; c < n_chunks; ++c) s += pv.scratch[c * E + x];
-    cnt[x] = s;
+    if (in_regs) {
+#pragma unroll
+      for (int c = 0; c < kRegChunks; ++c) nc[c] = c < n_chunks ? pv.scratch[c * E + tid] : 0;
+#pragma unroll
+      for (int c = 0; c < kRegChunks; ++c) s += nc[c];
+    } else {
+      for (int c = 0; c < n_chunks; ++c) s += pv.scratch[c * E + tid];
+    }
+    cnt[tid] = s;
     atomicAdd(&placed, s);
   }
   __syncthreads();
   plan_finish_counts(cnt, scan_tmp, T, k, E, R - placed, plan);
-  for (int x = tid; x < E; x += kPlanThreads) {
-    int base = cnt[x];                    // offsets[x]
-    for (int c = 0; c < n_chunks; ++c) {
-      const int n = pv.scratch[c * E + x];
-      pv.scratch[c * E + x] = base;
-      base += n;
+  if (tid < E) {
+    int base = cnt[tid];                  // offsets[tid]
+    if (in_regs) {
+#pragma unroll
+      for (int c = 0; c < kRegChunks; ++c) {
+        if (c < n_chunks) pv.scratch[c * E + tid] = base;
+        base += nc[c];
+      }
+    } else {
+      for (int c = 0; c < n_chunks; ++c) {
+        const int n = pv.scratch[c * E + tid];
+        pv.scratch[c * E + tid] = base;
+        base += n;
+      }
     }
   }
 }
@@ -163,10 +184,13 @@ quant_scatter_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;                                   // wave-uniform
   PlanView pv = plan_view(plan, E, T * k);
+  // x's loads first: place_row stores, and a load issued after a store also
+  // waits for it
+  RowQuant<XT, CPL> rq;
+  rq.load(x + int64_t(t) * H, H, lane);
   int pos = -1;
   if (lane < k) pos = kPlace ? place_row(ids, t * k + lane, E, pv) : pv.row_pos[t * k + lane];
-  RowQuant<XT, CPL> rq;
-  rq.run(x + int64_t(t) * H, H, lane);
+  rq.finish(H, lane);
   rq.store(x_q + int64_t(t) * H, H, lane);
   if (lane == 0) x_s[t] = rq.scale;
   for (int j = 0; j < k; ++j) {
