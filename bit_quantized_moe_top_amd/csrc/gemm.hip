@@ -40,7 +40,12 @@ gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
   const int tile = blockIdx.x / units_per_tile;
   const int u = blockIdx.x - tile * units_per_tile;
   TileInfo ti;
-  if (!tile_info(plan, E, R, tile, ti)) return;   // workgroup-uniform
+  const bool active = tile_info(plan, E, R, tile, ti);
+  // the kernel arguments used after the exit test are loaded ahead of it, with
+  // the ones the lookup needs (an asm statement ahead of the plan loads would
+  // turn them into vector loads)
+  asm volatile("" ::"s"(a_q), "s"(a_s), "s"(w), "s"(w_scale), "s"(out));
+  if (!active) return;                          // workgroup-uniform
 
   int col[NB];
   unit_columns<EPI, NB>(N, u, col);

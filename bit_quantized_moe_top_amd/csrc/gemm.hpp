@@ -253,6 +253,12 @@ __device__ __forceinline__ bool tile_info(const int32_t* plan, int E, int R, int
   const int row0 = pv.tile_row0[tl];
   const int next = pv.tile_row0[min(tl + 1, pv.max_tiles - 1)];
   const int end_all = pv.offsets[E];
+  // Every value is consumed here, ahead of the caller's exit test: otherwise
+  // the compiler sinks the loads the exit path does not need (and the kernel
+  // arguments they address with) below the test, and the lookup takes several
+  // scalar memory round trips in a row instead of one.  The values are uniform
+  // over the caller's wave.
+  asm volatile("" ::"s"(n), "s"(e), "s"(row0), "s"(next), "s"(end_all));
   ti.e = e;
   ti.row0 = row0;
   ti.rows = min(MOEQ_TILE_M, (tile + 1 < n ? next : end_all) - row0);

@@ -44,7 +44,12 @@ down_hq_kernel(const uint16_t* h, const int32_t* plan, int E, int R, const uint8
   const int tile = blockIdx.x / upt;
   const int u = blockIdx.x - tile * upt;
   TileInfo ti;
-  if (!tile_info(plan, E, R, tile, ti)) return;   // workgroup-uniform
+  const bool active = tile_info(plan, E, R, tile, ti);
+  // the kernel arguments used after the exit test are loaded ahead of it, with
+  // the ones the lookup needs (an asm statement ahead of the plan loads would
+  // turn them into vector loads)
+  asm volatile("" ::"s"(h), "s"(w2), "s"(s2), "s"(h_q), "s"(h_s), "s"(o));
+  if (!active) return;                          // workgroup-uniform
   const bool writer = u == 0;                   // the tile's first workgroup stores h_q, h_s
 
   int col[2];
