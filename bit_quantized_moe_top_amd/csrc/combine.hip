@@ -23,29 +23,39 @@ combine_kernel(const uint16_t* __restrict__ o, const int32_t* __restrict__ plan,
                int H, uint16_t* __restrict__ y) {
   const int chunks = (H / 8 + 255) / 256;
   const int t = blockIdx.x / chunks;
-  const int c = ((blockIdx.x - t * chunks) * 256 + threadIdx.x) * 8;
-  if (c >= H) return;
+  const int c_raw = ((blockIdx.x - t * chunks) * 256 + threadIdx.x) * 8;
+  const bool live = c_raw < H;
+  const int c = live ? c_raw : 0;
   // row_pos leads the plan after its header: no dependent read of E.  Every
-  // slot's position and weight are loaded before any is used, then every
-  // slot's row, so the combine costs two memory round trips, not 2k.
+  // slot's position and weight are loaded before any is used (slots past k
+  // re-read slot k - 1 and are dropped below), then every slot's row (a row
+  // that is not there reads row 0 and is dropped), so the combine costs two
+  // memory round trips, not 2k: a load under a branch of its own becomes a
+  // round trip of its own.
   const int32_t* row_pos = plan + kPlanHeader;
   int pos[MOEQ_MAX_TOPK];
   float wt[MOEQ_MAX_TOPK];
 #pragma unroll
   for (int j = 0; j < MOEQ_MAX_TOPK; ++j) {
-    pos[j] = j < k ? row_pos[t * k + j] : -1;
-    wt[j] = j < k ? w[t * k + j] : 0.0f;
+    const int slot = t * k + min(j, k - 1);
+    pos[j] = row_pos[slot];
+    wt[j] = w[slot];
   }
+  // every position and weight consumed here, so that the compiler sinks none
+  // of their loads into the accumulation's branches (the values are uniform
+  // over the workgroup)
+#pragma unroll
+  for (int j = 0; j < MOEQ_MAX_TOPK; ++j) asm volatile("" ::"s"(pos[j]), "s"(wt[j]));
   uint4 raw[MOEQ_MAX_TOPK];
 #pragma unroll
   for (int j = 0; j < MOEQ_MAX_TOPK; ++j)
-    if (pos[j] >= 0) raw[j] = *reinterpret_cast<const uint4*>(o + int64_t(pos[j]) * H + c);
+    raw[j] = *reinterpret_cast<const uint4*>(o + int64_t(max(pos[j], 0)) * H + c);
   uint4 sh = {};
   if (shared) sh = *reinterpret_cast<const uint4*>(shared + int64_t(t) * H + c);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < MOEQ_MAX_TOPK; ++j) {
-    if (pos[j] < 0) continue;                 // slots past k, or rows dropped by the permute
+    if (j >= k || pos[j] < 0) continue;       // slots past k, or rows dropped by the permute
     float v[8];
     bf16x8_to_f32(raw[j], v);
 #pragma unroll
@@ -62,7 +72,7 @@ combine_kernel(const uint16_t* __restrict__ o, const int32_t* __restrict__ plan,
   out.y = uint32_t(f32_to_bf16(acc[2])) | (uint32_t(f32_to_bf16(acc[3])) << 16);
   out.z = uint32_t(f32_to_bf16(acc[4])) | (uint32_t(f32_to_bf16(acc[5])) << 16);
   out.w = uint32_t(f32_to_bf16(acc[6])) | (uint32_t(f32_to_bf16(acc[7])) << 16);
-  *reinterpret_cast<uint4*>(y + int64_t(t) * H + c) = out;
+  if (live) *reinterpret_cast<uint4*>(y + int64_t(t) * H + c) = out;
 }
 
 }  // namespace

@@ -57,6 +57,11 @@ front_small_kernel(const float* __restrict__ logits, const float* __restrict__ b
   __shared__ int s_pos[kFrontMaxRows];
   __shared__ float s_part[kPlanWaves];        // per-wave max |x|
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // every kernel argument in one round of loads ahead of the first branch
+  // (the compiler otherwise loads each behind the branch that first needs it)
+  asm volatile("" ::"s"(logits), "s"(bias), "s"(x), "s"(ids), "s"(w), "s"(x_q), "s"(x_s),
+               "s"(xp_q), "s"(xp_s), "s"(plan), "s"(E), "s"(k), "s"(renormalize), "s"(H),
+               "s"(gridDim.x));
   const int R = T * k;
   const int cpr = H >> 3;                     // 8-element chunks per row
   // one row per workgroup (several workgroups), or all rows in one
