@@ -420,20 +420,30 @@ __device__ __forceinline__ void plan_build_wave(const int* s_ids, int T, int k, 
   if (valid) atomicOr(&s_mask[e], 1ull << lane);
   lds_wave_sync();
 
+  // all NS mask reads first, then the NS scans (independent of each other,
+  // so their cross-lane steps interleave), then the running carries: one LDS
+  // round trip instead of one per pass
+  int c[NS], incl[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int x = lane + j * kWave;
+    c[j] = x < E ? __popcll(s_mask[x]) : 0;
+  }
+  const uint64_t mine = valid ? s_mask[e] : 0ull;   // this row's expert's rows
+#pragma unroll
+  for (int j = 0; j < NS; ++j) incl[j] = wave_inclusive_scan(c[j]);
   int carry = 0, act_carry = 0;
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const int x = lane + j * kWave;
-    const int c = x < E ? __popcll(s_mask[x]) : 0;
-    const int incl = wave_inclusive_scan(c);
-    const int off = carry + incl - c;
-    carry += readlane(incl, kWave - 1);
-    const uint64_t nz = __ballot(c > 0);
+    const int off = carry + incl[j] - c[j];
+    carry += readlane(incl[j], kWave - 1);
+    const uint64_t nz = __ballot(c[j] > 0);
     if (x < E) {
       if (write_plan) pv.offsets[x] = off;
       s_off[x] = off;
     }
-    if (c > 0 && write_plan) {
+    if (c[j] > 0 && write_plan) {
       const int a = act_carry + __popcll(nz & ((1ull << lane) - 1ull));
       pv.active[a] = x;
       pv.tile_expert[a] = x;
@@ -456,7 +466,7 @@ __device__ __forceinline__ void plan_build_wave(const int* s_ids, int T, int k, 
   if (lane < R) {
     int p = -1;
     if (valid) {
-      p = s_off[e] + __popcll(s_mask[e] & ((1ull << lane) - 1ull));
+      p = s_off[e] + __popcll(mine & ((1ull << lane) - 1ull));
       if (write_plan) pv.sorted_rows[p] = lane;
     }
     if (write_plan) pv.row_pos[lane] = p;
