@@ -529,8 +529,26 @@ def test_hybrid_nvfp4_and_aqlm_slabs():
 
 
 # ------------------------------------------------------------------ combine ----
+def _assert_combine_close(got, ref, o, row_pos, w, k, shared):
+    """The GPU sums in fp32 (slot order) and rounds once to bf16; the reference
+    rounds the exact sum.  Bound: one bf16 ulp of the result, plus the fp32
+    accumulation error of <= k + 1 terms (k u sum|terms|, u = 2^-24), which
+    matters only where the terms cancel."""
+    T = w.shape[0]
+    rp = np.asarray(row_pos).reshape(T, k)
+    mag = np.zeros_like(ref, dtype=np.float64)
+    for j in range(k):
+        mag += np.abs(w[:, j:j + 1].astype(np.float64) * np.asarray(o, dtype=np.float64)[rp[:, j]])
+    if shared is not None:
+        mag += np.abs(np.asarray(shared, dtype=np.float64))
+    bound = np.abs(ref) * 2.0 ** -7 + (k + 1) * 2.0 ** -24 * mag * 2.0 + 1e-30
+    assert np.all(np.abs(got - ref) <= bound)
+    assert np.mean(got == ref) > 0.99
+
+
+# k = MOEQ_MAX_TOPK, and a row narrower than one block of 256 threads x 8 columns
 @pytest.mark.parametrize("T,k,E,H,shared", [(33, 6, 256, 4096, False), (16, 2, 8, 256, True),
-                                            (5, 1, 3, 8, False)])
+                                            (5, 1, 3, 8, False), (7, 8, 16, 2056, True)])
 def test_combine(T, k, E, H, shared):
     rng = np.random.default_rng(T + H)
     ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
@@ -544,10 +562,47 @@ def test_combine(T, k, E, H, shared):
                        None if sh is None else torch.from_numpy(sh).to(torch.bfloat16).to(_dev()))
     torch.cuda.synchronize()
     ref = L.combine(o, ref_plan["row_pos"], w, k, sh)
-    # fp32 accumulation of <= 9 terms then one bf16 rounding: at most one bf16 ulp apart
-    got = to_np(y)
-    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -7 + 1e-30)
-    assert np.mean(got == ref) > 0.99
+    _assert_combine_close(to_np(y), ref, o, ref_plan["row_pos"], w, k, sh)
+
+
+@pytest.mark.parametrize("T,k,E,H", [(7, 8, 16, 2056), (3, 2, 4, 64), (40, 6, 256, 512)])
+def test_permute_and_combine_drop_out_of_range_ids(T, k, E, H):
+    """Ids outside [0, E) (never produced by routing) are dropped: the other rows
+    keep their stable expert order, the dropped ones get row_pos -1, are counted
+    in the plan header, and add nothing in the combine.  Expected values: the
+    oracle's plan with every such id moved to an extra expert E sorted last."""
+    rng = np.random.default_rng(T * k + E)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[0, k - 1] = -1
+    ids[T - 1, 0] = E
+    ids[T // 2, k // 2] = E + 7
+    R = T * k
+    valid = (ids >= 0) & (ids < E)
+    n_valid = int(valid.sum())
+    plan, _, _ = mq.moe_permute(torch.from_numpy(ids).to(_dev()), E)
+    torch.cuda.synchronize()
+    ref = L.permute_plan(np.where(valid, ids, E), E + 1)
+    pf = {name: to_np(v) for name, v in mq.plan_fields(plan, E, R).items()}
+    assert int(pf["header"][6]) == R - n_valid                  # dropped rows
+    np.testing.assert_array_equal(pf["offsets"], ref["offsets"][:E + 1])
+    flat_valid = valid.reshape(-1)
+    np.testing.assert_array_equal(pf["row_pos"][flat_valid], ref["row_pos"][flat_valid])
+    assert np.all(pf["row_pos"][~flat_valid] == -1)
+    np.testing.assert_array_equal(pf["sorted_rows"][:n_valid], ref["sorted_rows"][:n_valid])
+    np.testing.assert_array_equal(pf["active"][:len(ref["active"]) - 1], ref["active"][:-1])
+
+    o = F.bf16_round(rng.standard_normal((R, H)))
+    w = rng.random((T, k)).astype(np.float32)
+    sh = F.bf16_round(rng.standard_normal((T, H)))
+    y = mq.moe_combine(torch.from_numpy(o).to(torch.bfloat16).to(_dev()), plan,
+                       torch.from_numpy(w).to(_dev()),
+                       torch.from_numpy(sh).to(torch.bfloat16).to(_dev()))
+    torch.cuda.synchronize()
+    # a dropped slot adds an exact zero: its weight is 0, its row any valid one
+    rp = np.where(flat_valid, ref["row_pos"], 0)
+    w0 = np.where(valid, w, 0.0)
+    y_ref = L.combine(o, rp, w0, k, sh)
+    _assert_combine_close(to_np(y), y_ref, o, rp, w0, k, sh)
 
 
 # ------------------------------------------------------------- shared GEMM ----
