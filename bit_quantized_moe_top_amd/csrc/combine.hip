@@ -21,31 +21,30 @@ __global__ void __launch_bounds__(256)
 combine_kernel(const uint16_t* __restrict__ o, const int32_t* __restrict__ plan,
                const float* __restrict__ w, const uint16_t* __restrict__ shared, int T, int k,
                int H, uint16_t* __restrict__ y) {
-  const int chunks = (H / 8 + 255) / 256;
-  const int t = blockIdx.x / chunks;
-  const int c_raw = ((blockIdx.x - t * chunks) * 256 + threadIdx.x) * 8;
+  // token t = blockIdx.x, 2048-column block blockIdx.y: no division by a
+  // kernel argument, so every argument load goes out in one round
+  const int t = blockIdx.x;
+  const int c_raw = (blockIdx.y * 256 + threadIdx.x) * 8;
   const bool live = c_raw < H;
   const int c = live ? c_raw : 0;
-  // row_pos leads the plan after its header: no dependent read of E.  Every
-  // slot's position and weight are loaded before any is used (slots past k
-  // re-read slot k - 1 and are dropped below), then every slot's row (a row
-  // that is not there reads row 0 and is dropped), so the combine costs two
-  // memory round trips, not 2k: a load under a branch of its own becomes a
-  // round trip of its own.
+  // row_pos leads the plan after its header: no dependent read of E.  Lane j of
+  // each wave loads slot j's position and weight (lanes past k re-read slot
+  // k - 1 and are ignored), which reach every lane by readlane: one round trip
+  // for all the slots, then one for every slot's row of o (a row that is not
+  // there reads row 0 and is dropped).  (As scalar loads, the sixteen values
+  // came back in two rounds or, under per-slot branches, in sixteen.)
   const int32_t* row_pos = plan + kPlanHeader;
+  const int lane = threadIdx.x & 63;
+  const int slot = t * k + min(lane, k - 1);
+  const int pos_l = row_pos[slot];
+  const float w_l = w[slot];
   int pos[MOEQ_MAX_TOPK];
   float wt[MOEQ_MAX_TOPK];
 #pragma unroll
   for (int j = 0; j < MOEQ_MAX_TOPK; ++j) {
-    const int slot = t * k + min(j, k - 1);
-    pos[j] = row_pos[slot];
-    wt[j] = w[slot];
+    pos[j] = readlane(pos_l, j);
+    wt[j] = readlane(w_l, j);
   }
-  // every position and weight consumed here, so that the compiler sinks none
-  // of their loads into the accumulation's branches (the values are uniform
-  // over the workgroup)
-#pragma unroll
-  for (int j = 0; j < MOEQ_MAX_TOPK; ++j) asm volatile("" ::"s"(pos[j]), "s"(wt[j]));
   uint4 raw[MOEQ_MAX_TOPK];
 #pragma unroll
   for (int j = 0; j < MOEQ_MAX_TOPK; ++j)
@@ -81,7 +80,7 @@ hipError_t launch_combine(const uint16_t* o, const void* plan, const float* w,
                           const uint16_t* shared, int T, int k, int H, uint16_t* y,
                           hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  dim3 grid(unsigned((H / 8 + 255) / 256) * unsigned(T));
+  dim3 grid(unsigned(T), unsigned((H / 8 + 255) / 256));
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, o, static_cast<const int32_t*>(plan),
                      w, shared, T, k, H, y);
   return hipGetLastError();
