@@ -165,7 +165,7 @@ gemm_aqlm_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
       for (int j = 0; j < 2; ++j) pin(acc[j]);
     };
     pipeline<kAqDepth<NBOOK>, 0>(G, issue, consume);
-    store_block<kAqlm, EPI>(acc, rb, ti.row0, ti.rows, [a_s](int p) { return a_s[p]; }, srow, col,
+    store_block<kAqlm, EPI>(acc, rb, ti.row0, ti.rows, [a_s](int p, int) { return a_s[p]; }, srow, col,
                             ln, kb, N, out, out_f32);
   }
 }

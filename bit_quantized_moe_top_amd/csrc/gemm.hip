@@ -61,6 +61,17 @@ gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
   for (int rb = 0; rb < nrb; ++rb) {
     v4f acc[NB];
     const int rrows = min(16, ti.rows - 16 * rb);
+    // the activation scales of this lane's four rows of the block, loaded ahead
+    // of the sweep so that the epilogue does not wait a memory round trip for
+    // them (rows past the tile re-read its first row; they are not stored)
+    float sa[4] = {0.f, 0.f, 0.f, 0.f};
+    if (q == 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r_in = 16 * rb + 4 * kb + v;
+        sa[v] = a_s[ti.row0 + (r_in < ti.rows ? r_in : 0)];
+      }
+    }
     if (rrows <= kStageRows && kq <= kStageK) {
       // the block's activation quarter through LDS: one 16-byte load per lane
       // and row, issued ahead of the weight loads
@@ -94,7 +105,7 @@ gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
     }
     quarter_reduce<NB>(acc, red, q, lane, rb + 1 < nrb);
     if (q == 0)
-      store_block<WFMT, EPI, NB>(acc, rb, ti.row0, ti.rows, [a_s](int p) { return a_s[p]; },
+      store_block<WFMT, EPI, NB>(acc, rb, ti.row0, ti.rows, [&sa](int, int v) { return sa[v]; },
                                  srow, col, ln, kb, N, out, out_f32);
   }
 }
@@ -269,7 +280,7 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
       v4f blk[CB];
 #pragma unroll
       for (int j = 0; j < CB; ++j) blk[j] = acc[i][j];
-      store_block<WFMT, EPI, CB>(blk, i, ti.row0, ti.rows, [a_s](int p) { return a_s[p]; }, srow,
+      store_block<WFMT, EPI, CB>(blk, i, ti.row0, ti.rows, [a_s](int p, int) { return a_s[p]; }, srow,
                                  col, ln, kb, N, out, out_f32);
     }
   }

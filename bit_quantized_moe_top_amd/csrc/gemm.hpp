@@ -35,11 +35,12 @@
 //
 // Two GEMM kernels share this arithmetic (the fused expert MLP runs the wave
 // kernel's units):
-//  * wave kernel (few rows per expert, e.g. decode): every wave is independent.
-//    Its unit is (plan tile, 32 weight rows); it reads its own activation
-//    fragment straight from global memory (tiny, cache-resident), so there is
-//    no LDS and no barrier in the K loop.  Tiles with more than 16 rows are swept
-//    once per 16-row block.
+//  * wave kernel (few rows per expert, e.g. decode): a 256-thread workgroup per
+//    unit (plan tile, 32 weight rows); wave q sweeps K quarter q, with the
+//    block's activation quarter staged in LDS when it has at most 4 rows (read
+//    from global memory otherwise), and the four partial sums meet in LDS at
+//    one barrier after the sweep.  Tiles with more than 16 rows are swept once
+//    per 16-row block.
 //  * tile kernel (prefill): a 256-thread workgroup owns one plan tile (<= 64
 //    rows) x 128 or 256 weight rows.  The 64 x 128 B activation slice of each
 //    group is staged once in LDS (double-buffered, one barrier per group) and
@@ -281,7 +282,8 @@ __device__ __forceinline__ void weight_rows(const uint8_t* w, const ScaleT<WFMT>
 }
 
 // epilogue for one 16-row block: lane holds rows 4 kb + v, column col[j] + ln;
-// row_scale(p) is the activation scale of sorted row p
+// row_scale(p, v) is the activation scale of sorted row p (v: its slot 0..3
+// among this lane's four rows of the block, for scales held in registers)
 // the weight-row scales applied at the end (row-scaled FP8 only)
 template <int WFMT, int NB = 2>
 __device__ __forceinline__ void row_scales(const ScaleT<WFMT>* const (&srow)[NB], float (&rs)[NB]) {
@@ -314,7 +316,7 @@ __device__ __forceinline__ void store_block(const v4f (&acc)[NB], int rb, int ro
     const int r_in = 16 * rb + 4 * kb + v;
     if (r_in >= rows) continue;
     const int p = row0 + r_in;
-    const float sa = row_scale(p);
+    const float sa = row_scale(p, v);
     if constexpr (EPI == MOEQ_EPI_SILU_MUL && NB == 2) {
       uint16_t* o = static_cast<uint16_t*>(out) + int64_t(p) * (N >> 1);
       o[col[0] + ln] = silu_mul_bf16(acc, v, sa, rs);

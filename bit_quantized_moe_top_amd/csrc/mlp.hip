@@ -123,7 +123,7 @@ down_hq_kernel(const uint16_t* h, const int32_t* plan, int E, int R, const uint8
     quarter_reduce<2>(acc, red, q, lane, rb + 1 < nrb);
     if (q == 0)
       store_block<WFMT, MOEQ_EPI_NONE>(acc, rb, ti.row0, ti.rows,
-                                       [&](int p) { return s_scale[p - p0]; }, srow, col, ln, kb,
+                                       [&](int p, int) { return s_scale[p - p0]; }, srow, col, ln, kb,
                                        H, o, 0);
     // the next block rewrites s_part after every wave has passed this block's
     // reduction barrier (all reads of s_part precede it); s_scale is written

@@ -155,7 +155,7 @@ gemm_nvfp4_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int
     };
     pipeline<kNvDepth, 0>(G, issue, consume);
     store_block<kNvfp4, EPI>(acc, rb, ti.row0, ti.rows,
-                             [a_s, scale2](int p) { return a_s[p] * scale2; }, srow, col, ln, kb,
+                             [a_s, scale2](int p, int) { return a_s[p] * scale2; }, srow, col, ln, kb,
                              N, out, out_f32);
   }
 }
