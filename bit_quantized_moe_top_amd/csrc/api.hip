@@ -319,7 +319,7 @@ int moe_combine(const uint16_t* o, const void* plan, const float* topk_w, const 
   if (T < 0 || k <= 0 || H <= 0) return MOEQ_ERR_INVALID_ARG;
   if (k > MOEQ_MAX_TOPK) return MOEQ_ERR_UNSUPPORTED;
   if (H % 8 != 0) return MOEQ_ERR_UNSUPPORTED;
-  if (int64_t(T) * ((H / 8 + 255) / 256) > 0x7FFFFFFF) return MOEQ_ERR_UNSUPPORTED;
+  if ((H / 8 + 255) / 256 > 65535) return MOEQ_ERR_UNSUPPORTED;   // grid (T, 2048-column blocks)
   if (T > 0 && (!o || !plan || !topk_w || !y)) return MOEQ_ERR_INVALID_ARG;
   if (T > 0 && (!aligned16(o) || !aligned16(y) || (shared && !aligned16(shared))))
     return MOEQ_ERR_INVALID_ARG;
