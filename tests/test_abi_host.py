@@ -121,6 +121,9 @@ def test_argument_errors_are_reported_without_a_gpu():
     # combine / shared
     assert L.moe_combine(FAKE, FAKE, FAKE, N, 4, 2, 12, FAKE, N) == UNSUPPORTED
     assert L.moe_combine(FAKE, N, FAKE, N, 4, 2, 16, FAKE, N) == INVALID
+    assert L.moe_combine(FAKE, FAKE, FAKE, N, 4, 9, 16, FAKE, N) == UNSUPPORTED   # k > 8
+    # more 2048-column blocks than the grid's second dimension holds
+    assert L.moe_combine(FAKE, FAKE, FAKE, N, 0, 2, 1 << 28, FAKE, N) == UNSUPPORTED
     assert L.moe_shared_gemm_bf16(FAKE, FAKE, 4, 100, 64, 0, FAKE, N) == UNSUPPORTED
     assert L.moe_shared_gemm_bf16(FAKE, FAKE, 4, 128, 48, 0, FAKE, N) == UNSUPPORTED
 
