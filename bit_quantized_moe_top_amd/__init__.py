@@ -55,19 +55,21 @@ _SIGNATURES = {
     "pack_int4_g128": (_I, [_P, _I64, _I, _P, _P, _P]),
     "pack_int4_g128_bf16s": (_I, [_P, _I64, _I, _P, _P, _P]),
     "moe_requant_fp8_fnuz": (_I, [_P, _P, _I64, _I, _P, _P, _P]),
-    "moe_grouped_gemm_w4a8": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
-    "moe_grouped_gemm_fp8row": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
-    "moe_grouped_gemm_w4a8_bf16s": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
-    "moe_grouped_gemm_nvfp4": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P]),
-    "moe_grouped_gemm_aqlm": (_I, [_P, _P, _P, _I, _I, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _I,
-                                   _P]),
+    "moe_grouped_gemm_w4a8": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
+    "moe_grouped_gemm_fp8row": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
+    "moe_grouped_gemm_w4a8_bf16s": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _I, _I, _I, _P, _I,
+                                         _P]),
+    "moe_grouped_gemm_nvfp4": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _I, _P, _P, _P, _I, _I, _I, _P,
+                                    _I, _P]),
+    "moe_grouped_gemm_aqlm": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _I, _I, _P, _P, _P, _P, _I, _I,
+                                   _I, _P, _I, _P]),
     "moe_expert_mlp_w4a8": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P,
                                  _P]),
     "moe_expert_mlp_w4a8_bf16s": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P,
                                        _P, _P]),
     "moe_expert_mlp_fp8row": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P,
                                    _P, _P]),
-    "moe_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
+    "moe_combine": (_I, [_P, _P, _SZ, _I, _P, _P, _I, _I, _I, _P, _P]),
     "moe_shared_gemm_bf16": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
@@ -117,6 +119,33 @@ def _req(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None):
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _weight_bytes(t: torch.Tensor, name: str) -> torch.Tensor:
+    """Packed INT4 weights as bytes: uint8 [..., K/2] as they are, or the checkpoint's
+    int32 [..., K/8] .weight_packed words viewed as their little-endian bytes."""
+    if isinstance(t, torch.Tensor) and t.dtype == torch.int32:
+        _req(t, name, torch.int32)
+        return t.view(torch.uint8)
+    _req(t, name, torch.uint8)
+    return t
+
+
+def _mark_plan(plan: torch.Tensor, E: int, R: int) -> None:
+    # the (E, R) a plan tensor was last built for, so that later calls can check
+    # theirs without reading device memory
+    plan._moeq_shape = (E, R)
+
+
+def _plan_shape_ok(plan: torch.Tensor, E: int, R: int) -> None:
+    built = getattr(plan, "_moeq_shape", None)
+    if built is not None and built != (E, R):
+        raise ValueError(f"plan was built for (E, R) = {built}, the call has ({E}, {R})")
+
+
+def _check_plan(plan: torch.Tensor, E: int, R: int) -> None:
+    _req(plan, "plan", torch.int32, 1)
+    _plan_shape_ok(plan, E, R)
 
 
 def moe_abi_version() -> int:
@@ -222,6 +251,7 @@ def moe_permute(topk_ids: torch.Tensor, E: int, x_q: Optional[torch.Tensor] = No
     _check("moe_permute", lib.moe_permute(_ptr(topk_ids), T, k, E, _ptr(x_q), _ptr(x_s), H,
                                           _ptr(xp_q), _ptr(xp_s), _ptr(plan), plan.numel() * 4,
                                           _stream(dev)))
+    _mark_plan(plan, E, R)
     return plan, xp_q, xp_s
 
 
@@ -253,6 +283,7 @@ def moe_route_quant_permute(logits: torch.Tensor, x: torch.Tensor, k: int,
         _ptr(logits), _ptr(bias), T, E, k, 1 if renormalize else 0, _ptr(x), dt, H, _ptr(o["ids"]),
         _ptr(o["w"]), _ptr(o["x_q"]), _ptr(o["x_s"]), _ptr(o["xp_q"]), _ptr(o["xp_s"]),
         _ptr(o["plan"]), o["plan"].numel() * 4, _stream(dev)))
+    _mark_plan(o["plan"], E, R)
     return o
 
 
@@ -308,8 +339,8 @@ def moe_requant_fp8_fnuz(w_fnuz: torch.Tensor, s_fnuz: torch.Tensor,
 def _gemm(fn_name: str, a_q, a_s, plan, E, w, w_scale, N, K, epilogue, out_dtype, out):
     _req(a_q, "a_q", torch.uint8, 2)
     _req(a_s, "a_s", torch.float32, 1)
-    _req(plan, "plan", torch.int32, 1)
     R = a_q.shape[0]
+    _check_plan(plan, E, R)
     if a_q.shape[1] != K:
         raise ValueError("a_q has the wrong K")
     n_out = N // 2 if epilogue == EPI_SILU_MUL else N
@@ -317,8 +348,8 @@ def _gemm(fn_name: str, a_q, a_s, plan, E, w, w_scale, N, K, epilogue, out_dtype
         out = torch.empty(R, n_out, dtype=out_dtype, device=a_q.device)
     odt = MOEQ_BF16 if out.dtype == torch.bfloat16 else MOEQ_F32
     fn = getattr(lib, fn_name)
-    _check(fn_name, fn(_ptr(a_q), _ptr(a_s), _ptr(plan), E, R, _ptr(w), _ptr(w_scale), N, K,
-                       epilogue, _ptr(out), odt, _stream(a_q.device)))
+    _check(fn_name, fn(_ptr(a_q), _ptr(a_s), _ptr(plan), plan.numel() * 4, E, R, _ptr(w),
+                       _ptr(w_scale), N, K, epilogue, _ptr(out), odt, _stream(a_q.device)))
     return out
 
 
@@ -326,8 +357,9 @@ def moe_grouped_gemm_w4a8(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Tens
                           w_packed: torch.Tensor, w_scales: torch.Tensor,
                           epilogue: int = EPI_NONE, out_dtype=torch.bfloat16,
                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """w_packed [E, N, K/2] uint8, w_scales [E, N, K/128] fp32 (or bfloat16: then
-    moe_grouped_gemm_w4a8_bf16s)."""
+    """w_packed [E, N, K/2] uint8 (or the checkpoint's int32 [E, N, K/8] words),
+    w_scales [E, N, K/128] fp32 (or bfloat16: then moe_grouped_gemm_w4a8_bf16s)."""
+    w_packed = _weight_bytes(w_packed, "w_packed")
     _req(w_packed, "w_packed", torch.uint8, 3)
     bf16 = w_scales.dtype == torch.bfloat16
     _req(w_scales, "w_scales", torch.bfloat16 if bf16 else torch.float32, 3)
@@ -353,10 +385,10 @@ def moe_grouped_gemm_nvfp4(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Ten
                            ) -> torch.Tensor:
     """w_fp4 [S, N, K/2] uint8 (E2M1 pairs), w_block_scale [S, N, K/16] uint8 (E4M3),
     w_scale2 [S] fp32; slab_of [E] int32 (-1: expert not NVFP4; rows left as they are)
-    or None (slab e = expert e, E = S)."""
+    or None (slab e = expert e, E = S).  slab_of values outside [0, S) mark experts of
+    another format."""
     _req(a_q, "a_q", torch.uint8, 2)
     _req(a_s, "a_s", torch.float32, 1)
-    _req(plan, "plan", torch.int32, 1)
     _req(w_fp4, "w_fp4", torch.uint8, 3)
     _req(w_block_scale, "w_block_scale", torch.uint8, 3)
     _req(w_scale2, "w_scale2", torch.float32, 1)
@@ -370,6 +402,7 @@ def moe_grouped_gemm_nvfp4(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Ten
     elif E is None:
         E = S
     R = a_q.shape[0]
+    _check_plan(plan, E, R)
     if a_q.shape[1] != K:
         raise ValueError("a_q has the wrong K")
     n_out = N // 2 if epilogue == EPI_SILU_MUL else N
@@ -377,9 +410,8 @@ def moe_grouped_gemm_nvfp4(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Ten
         out = torch.empty(R, n_out, dtype=out_dtype, device=a_q.device)
     odt = MOEQ_BF16 if out.dtype == torch.bfloat16 else MOEQ_F32
     _check("moe_grouped_gemm_nvfp4", lib.moe_grouped_gemm_nvfp4(
-        _ptr(a_q), _ptr(a_s), _ptr(plan), E, R, _ptr(slab_of), _ptr(w_fp4), _ptr(w_block_scale),
-        _ptr(w_scale2),
-        N, K, epilogue, _ptr(out), odt, _stream(a_q.device)))
+        _ptr(a_q), _ptr(a_s), _ptr(plan), plan.numel() * 4, E, R, _ptr(slab_of), S, _ptr(w_fp4),
+        _ptr(w_block_scale), _ptr(w_scale2), N, K, epilogue, _ptr(out), odt, _stream(a_q.device)))
     return out
 
 
@@ -394,7 +426,6 @@ def moe_grouped_gemm_aqlm(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Tens
     moe_grouped_gemm_nvfp4."""
     _req(a_q, "a_q", torch.uint8, 2)
     _req(a_s, "a_s", torch.float32, 1)
-    _req(plan, "plan", torch.int32, 1)
     _req(row_scale, "row_scale", torch.float16, 2)
     nb = len(codes)
     if nb != len(codebooks) or nb not in (1, 2):
@@ -411,6 +442,7 @@ def moe_grouped_gemm_aqlm(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Tens
         E = slab_of.shape[0]
     elif E is None:
         E = S
+    _check_plan(plan, E, R)
     n_out = N // 2 if epilogue == EPI_SILU_MUL else N
     if out is None:
         out = torch.empty(R, n_out, dtype=out_dtype, device=a_q.device)
@@ -419,8 +451,8 @@ def moe_grouped_gemm_aqlm(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Tens
     bptr = (ctypes.c_void_p * nb)(*[b.data_ptr() for b in codebooks])
     ents = (ctypes.c_int * nb)(*[b.shape[0] for b in codebooks])
     _check("moe_grouped_gemm_aqlm", lib.moe_grouped_gemm_aqlm(
-        _ptr(a_q), _ptr(a_s), _ptr(plan), E, R, _ptr(slab_of), nb, cptr, ents, bptr,
-        _ptr(row_scale), N, K, epilogue, _ptr(out), odt, _stream(a_q.device)))
+        _ptr(a_q), _ptr(a_s), _ptr(plan), plan.numel() * 4, E, R, _ptr(slab_of), S, nb, cptr,
+        ents, bptr, _ptr(row_scale), N, K, epilogue, _ptr(out), odt, _stream(a_q.device)))
     return out
 
 
@@ -441,8 +473,8 @@ def moe_grouped_gemm_fp8row(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Te
 def _expert_mlp(fn_name: str, xp_q, xp_s, plan, E, w13, s13, w2, s2, H, I, out):
     _req(xp_q, "xp_q", torch.uint8, 2)
     _req(xp_s, "xp_s", torch.float32, 1)
-    _req(plan, "plan", torch.int32, 1)
     R = xp_q.shape[0]
+    _check_plan(plan, E, R)
     if xp_q.shape[1] != H:
         raise ValueError("xp_q has the wrong H")
     dev = xp_q.device
@@ -464,8 +496,10 @@ def moe_expert_mlp_w4a8(xp_q: torch.Tensor, xp_s: torch.Tensor, plan: torch.Tens
     """gate/up GEMM + SiLU, FP8 quantization of h, down GEMM (two launches for R <= 192
     and I <= 2048, else three).
     w13 [E, 2I, H/2], w13_scales [E, 2I, H/128], w2 [E, H, I/2], w2_scales [E, H, I/128].
-    Scales fp32, or both bfloat16 (then moe_expert_mlp_w4a8_bf16s).
+    Scales fp32, or both bfloat16 (then moe_expert_mlp_w4a8_bf16s).  w13 / w2 may also be
+    the checkpoint's int32 [.., K/8] words.
     Returns a dict with h, h_q, h_s, o (reusing `out`'s tensors)."""
+    w13, w2 = _weight_bytes(w13, "w13"), _weight_bytes(w2, "w2")
     for t, name in ((w13, "w13"), (w2, "w2")):
         _req(t, name, torch.uint8, 3)
     sdt = torch.bfloat16 if w13_scales.dtype == torch.bfloat16 else torch.float32
@@ -505,18 +539,28 @@ def moe_expert_mlp_fp8row(xp_q: torch.Tensor, xp_s: torch.Tensor, plan: torch.Te
 
 
 def moe_combine(o: torch.Tensor, plan: torch.Tensor, topk_w: torch.Tensor,
-                shared: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None):
+                shared: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                E: Optional[int] = None):
+    """y [T, H] bf16 = sum_j topk_w[t, j] * o[row_pos[t*k + j]] (+ shared).  The plan was
+    built for E experts and R = T*k rows; E=None takes it from a plan this binding built."""
     _req(o, "o", torch.bfloat16, 2)
-    _req(plan, "plan", torch.int32, 1)
     _req(topk_w, "topk_w", torch.float32, 2)
     T, k = topk_w.shape
+    if E is None:
+        built = getattr(plan, "_moeq_shape", None)
+        if built is None:
+            raise ValueError("moe_combine needs E for a plan not built by this binding")
+        E = built[0]
+    _check_plan(plan, E, T * k)
+    if o.shape[0] != T * k:
+        raise ValueError("o must have T*k rows")
     H = o.shape[1]
     if shared is not None:
         _req(shared, "shared", torch.bfloat16, 2)
     if y is None:
         y = torch.empty(T, H, dtype=torch.bfloat16, device=o.device)
-    _check("moe_combine", lib.moe_combine(_ptr(o), _ptr(plan), _ptr(topk_w), _ptr(shared), T, k, H,
-                                          _ptr(y), _stream(o.device)))
+    _check("moe_combine", lib.moe_combine(_ptr(o), _ptr(plan), plan.numel() * 4, E, _ptr(topk_w),
+                                          _ptr(shared), T, k, H, _ptr(y), _stream(o.device)))
     return y
 
 

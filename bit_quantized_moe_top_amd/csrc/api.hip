@@ -30,6 +30,13 @@ int launch_status(hipError_t err) { return err == hipSuccess ? MOEQ_OK : MOEQ_ER
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// a plan read by a kernel: 4-byte aligned and at least moe_plan_size(E, R) bytes
+int check_plan(const void* plan, size_t plan_bytes, int E, int R) {
+  if (reinterpret_cast<uintptr_t>(plan) & 3u) return MOEQ_ERR_INVALID_ARG;
+  if (plan_bytes < moeq::plan_words(E, R) * sizeof(int32_t)) return MOEQ_ERR_WORKSPACE;
+  return MOEQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,9 +176,9 @@ int pack_int4_g128_bf16s(const float* w, int64_t rows, int K, uint8_t* packed, u
   return pack_common(w, rows, K, packed, scales, 1, stream);
 }
 
-static int gemm_common(int wfmt, const uint8_t* a_q, const float* a_s, const void* plan, int E,
-                       int R, const uint8_t* w, const void* w_scale, int N, int K, int epilogue,
-                       void* out, int out_dtype, void* stream) {
+static int gemm_common(int wfmt, const uint8_t* a_q, const float* a_s, const void* plan,
+                       size_t plan_bytes, int E, int R, const uint8_t* w, const void* w_scale, int N,
+                       int K, int epilogue, void* out, int out_dtype, void* stream) {
   if (R < 0 || E <= 0 || N <= 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;
   if (epilogue != MOEQ_EPI_NONE && epilogue != MOEQ_EPI_SILU_MUL) return MOEQ_ERR_INVALID_ARG;
   if (out_dtype != MOEQ_F32 && out_dtype != MOEQ_BF16) return MOEQ_ERR_INVALID_ARG;
@@ -182,87 +189,98 @@ static int gemm_common(int wfmt, const uint8_t* a_q, const float* a_s, const voi
   if (R > 0 && (!a_q || !a_s || !plan || !w || !w_scale || !out)) return MOEQ_ERR_INVALID_ARG;
   if (R > 0 && (!aligned16(a_q) || !aligned16(w) || !aligned16(w_scale))) return MOEQ_ERR_INVALID_ARG;
   if (R == 0) return MOEQ_OK;
+  if (int rc = check_plan(plan, plan_bytes, E, R)) return rc;
   if (int rc = check_device()) return rc;
   return launch_status(moeq::launch_grouped_gemm(wfmt, a_q, a_s, plan, E, R, w, w_scale, N, K,
                                                  epilogue, out, out_dtype, as_stream(stream)));
 }
 
-int moe_grouped_gemm_w4a8(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
-                          const uint8_t* w_packed, const float* w_scales, int N, int K,
-                          int epilogue, void* out, int out_dtype, void* stream) {
-  return gemm_common(moeq::kW4G128, a_q, a_s, plan, E, R, w_packed, w_scales, N, K, epilogue, out,
-                     out_dtype, stream);
+int moe_grouped_gemm_w4a8(const uint8_t* a_q, const float* a_s, const void* plan,
+                          size_t plan_bytes, int E, int R, const uint8_t* w_packed,
+                          const float* w_scales, int N, int K, int epilogue, void* out,
+                          int out_dtype, void* stream) {
+  return gemm_common(moeq::kW4G128, a_q, a_s, plan, plan_bytes, E, R, w_packed, w_scales, N, K,
+                     epilogue, out, out_dtype, stream);
 }
 
-int moe_grouped_gemm_w4a8_bf16s(const uint8_t* a_q, const float* a_s, const void* plan, int E,
-                                int R, const uint8_t* w_packed, const uint16_t* w_scales, int N,
-                                int K, int epilogue, void* out, int out_dtype, void* stream) {
-  return gemm_common(moeq::kW4G128Bf16, a_q, a_s, plan, E, R, w_packed, w_scales, N, K, epilogue,
-                     out, out_dtype, stream);
+int moe_grouped_gemm_w4a8_bf16s(const uint8_t* a_q, const float* a_s, const void* plan,
+                                size_t plan_bytes, int E, int R, const uint8_t* w_packed,
+                                const uint16_t* w_scales, int N, int K, int epilogue, void* out,
+                                int out_dtype, void* stream) {
+  return gemm_common(moeq::kW4G128Bf16, a_q, a_s, plan, plan_bytes, E, R, w_packed, w_scales, N,
+                     K, epilogue, out, out_dtype, stream);
 }
 
-int moe_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
-                           const int32_t* slab_of, const uint8_t* w_fp4,
-                           const uint8_t* w_block_scale,
-                           const float* w_scale2, int N, int K, int epilogue, void* out,
-                           int out_dtype, void* stream) {
-  if (R < 0 || E <= 0 || N <= 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;
+// checks shared by the NVFP4 and AQLM grouped GEMMs
+static int hybrid_common(const uint8_t* a_q, const float* a_s, const void* plan,
+                         size_t plan_bytes, int E, int R, const int32_t* slab_of, int S, int N,
+                         int K, int epilogue, void* out, int out_dtype) {
+  if (R < 0 || E <= 0 || N <= 0 || K <= 0 || S < 0) return MOEQ_ERR_INVALID_ARG;
   if (epilogue != MOEQ_EPI_NONE && epilogue != MOEQ_EPI_SILU_MUL) return MOEQ_ERR_INVALID_ARG;
   if (out_dtype != MOEQ_F32 && out_dtype != MOEQ_BF16) return MOEQ_ERR_INVALID_ARG;
   if (epilogue == MOEQ_EPI_SILU_MUL && out_dtype != MOEQ_BF16) return MOEQ_ERR_INVALID_ARG;
+  if (!slab_of && E > S) return MOEQ_ERR_INVALID_ARG;     // identity map needs a slab per expert
   if (E > MOEQ_MAX_EXPERTS) return MOEQ_ERR_UNSUPPORTED;
   if (K % 128 != 0 || N % 128 != 0) return MOEQ_ERR_UNSUPPORTED;
   if (int64_t(N / 32) * moeq::plan_max_tiles(E, R) > 0x7FFFFFF0) return MOEQ_ERR_UNSUPPORTED;
-  if (R > 0 && (!a_q || !a_s || !plan || !w_fp4 || !w_block_scale || !w_scale2 || !out))
-    return MOEQ_ERR_INVALID_ARG;
-  if (R > 0 && (!aligned16(a_q) || !aligned16(w_fp4) || !aligned16(w_block_scale)))
-    return MOEQ_ERR_INVALID_ARG;
-  if (R == 0) return MOEQ_OK;
-  if (int rc = check_device()) return rc;
-  return launch_status(moeq::launch_grouped_gemm_nvfp4(a_q, a_s, plan, E, R, slab_of, w_fp4,
-                                                       w_block_scale,
-                                                       w_scale2, N, K, epilogue, out, out_dtype,
-                                                       as_stream(stream)));
+  if (R > 0 && (!a_q || !a_s || !plan || !out)) return MOEQ_ERR_INVALID_ARG;
+  if (R > 0 && !aligned16(a_q)) return MOEQ_ERR_INVALID_ARG;
+  if (R > 0) return check_plan(plan, plan_bytes, E, R);
+  return MOEQ_OK;
 }
 
-int moe_grouped_gemm_aqlm(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
-                          const int32_t* slab_of, int n_books, const void* const* codes,
-                          const int* book_entries, const uint16_t* const* codebooks,
-                          const uint16_t* row_scale, int N, int K, int epilogue, void* out,
-                          int out_dtype, void* stream) {
-  if (R < 0 || E <= 0 || N <= 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;
-  if (epilogue != MOEQ_EPI_NONE && epilogue != MOEQ_EPI_SILU_MUL) return MOEQ_ERR_INVALID_ARG;
-  if (out_dtype != MOEQ_F32 && out_dtype != MOEQ_BF16) return MOEQ_ERR_INVALID_ARG;
-  if (epilogue == MOEQ_EPI_SILU_MUL && out_dtype != MOEQ_BF16) return MOEQ_ERR_INVALID_ARG;
+int moe_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* plan,
+                           size_t plan_bytes, int E, int R, const int32_t* slab_of, int S,
+                           const uint8_t* w_fp4, const uint8_t* w_block_scale,
+                           const float* w_scale2, int N, int K, int epilogue, void* out,
+                           int out_dtype, void* stream) {
+  if (int rc = hybrid_common(a_q, a_s, plan, plan_bytes, E, R, slab_of, S, N, K, epilogue, out,
+                             out_dtype))
+    return rc;
+  if (R > 0 && S > 0 && (!w_fp4 || !w_block_scale || !w_scale2)) return MOEQ_ERR_INVALID_ARG;
+  if (R > 0 && S > 0 && (!aligned16(w_fp4) || !aligned16(w_block_scale)))
+    return MOEQ_ERR_INVALID_ARG;
+  if (R == 0 || S == 0) return MOEQ_OK;               // no expert is stored in this format
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_grouped_gemm_nvfp4(a_q, a_s, plan, E, R, slab_of, S, w_fp4,
+                                                       w_block_scale, w_scale2, N, K, epilogue,
+                                                       out, out_dtype, as_stream(stream)));
+}
+
+int moe_grouped_gemm_aqlm(const uint8_t* a_q, const float* a_s, const void* plan,
+                          size_t plan_bytes, int E, int R, const int32_t* slab_of, int S,
+                          int n_books, const void* const* codes, const int* book_entries,
+                          const uint16_t* const* codebooks, const uint16_t* row_scale, int N, int K,
+                          int epilogue, void* out, int out_dtype, void* stream) {
+  if (int rc = hybrid_common(a_q, a_s, plan, plan_bytes, E, R, slab_of, S, N, K, epilogue, out,
+                             out_dtype))
+    return rc;
   if (n_books < 1 || n_books > moeq::kAqlmMaxBooks) return MOEQ_ERR_UNSUPPORTED;
   if (!codes || !book_entries || !codebooks) return MOEQ_ERR_INVALID_ARG;
   for (int b = 0; b < n_books; ++b)
     if (book_entries[b] < 1 || book_entries[b] > 65536) return MOEQ_ERR_UNSUPPORTED;
-  if (E > MOEQ_MAX_EXPERTS) return MOEQ_ERR_UNSUPPORTED;
-  if (K % 128 != 0 || N % 128 != 0) return MOEQ_ERR_UNSUPPORTED;
-  if (int64_t(N / 32) * moeq::plan_max_tiles(E, R) > 0x7FFFFFF0) return MOEQ_ERR_UNSUPPORTED;
-  if (R > 0 && (!a_q || !a_s || !plan || !row_scale || !out)) return MOEQ_ERR_INVALID_ARG;
-  for (int b = 0; R > 0 && b < n_books; ++b) {
+  if (R > 0 && S > 0 && !row_scale) return MOEQ_ERR_INVALID_ARG;
+  for (int b = 0; R > 0 && S > 0 && b < n_books; ++b) {
     if (!codes[b] || !codebooks[b]) return MOEQ_ERR_INVALID_ARG;
     const uintptr_t align = book_entries[b] > 256 ? 7u : 3u;      // 8- or 4-byte code loads
     if ((reinterpret_cast<uintptr_t>(codes[b]) & align) || !aligned16(codebooks[b]))
       return MOEQ_ERR_INVALID_ARG;
   }
-  if (R > 0 && (!aligned16(a_q) || (reinterpret_cast<uintptr_t>(row_scale) & 1u)))
-    return MOEQ_ERR_INVALID_ARG;
-  if (R == 0) return MOEQ_OK;
+  if (R > 0 && S > 0 && (reinterpret_cast<uintptr_t>(row_scale) & 1u)) return MOEQ_ERR_INVALID_ARG;
+  if (R == 0 || S == 0) return MOEQ_OK;               // no expert is stored in this format
   if (int rc = check_device()) return rc;
-  return launch_status(moeq::launch_grouped_gemm_aqlm(a_q, a_s, plan, E, R, slab_of, n_books,
+  return launch_status(moeq::launch_grouped_gemm_aqlm(a_q, a_s, plan, E, R, slab_of, S, n_books,
                                                       codes, book_entries, codebooks, row_scale,
                                                       N, K, epilogue, out, out_dtype,
                                                       as_stream(stream)));
 }
 
-int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
-                            const uint8_t* w_fp8, const float* w_row_scale, int N, int K,
-                            int epilogue, void* out, int out_dtype, void* stream) {
-  return gemm_common(moeq::kFp8Row, a_q, a_s, plan, E, R, w_fp8, w_row_scale, N, K, epilogue, out,
-                     out_dtype, stream);
+int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* plan,
+                            size_t plan_bytes, int E, int R, const uint8_t* w_fp8,
+                            const float* w_row_scale, int N, int K, int epilogue, void* out,
+                            int out_dtype, void* stream) {
+  return gemm_common(moeq::kFp8Row, a_q, a_s, plan, plan_bytes, E, R, w_fp8, w_row_scale, N, K,
+                     epilogue, out, out_dtype, stream);
 }
 
 static int mlp_common(int wfmt, const uint8_t* xp_q, const float* xp_s, const void* plan,
@@ -281,8 +299,7 @@ static int mlp_common(int wfmt, const uint8_t* xp_q, const float* xp_s, const vo
                 !aligned16(s13) || !aligned16(w2) || !aligned16(s2)))
     return MOEQ_ERR_INVALID_ARG;
   if (R == 0) return MOEQ_OK;
-  if (reinterpret_cast<uintptr_t>(plan) & 3u) return MOEQ_ERR_INVALID_ARG;
-  if (plan_bytes < moe_plan_size(E, R)) return MOEQ_ERR_WORKSPACE;
+  if (int rc = check_plan(plan, plan_bytes, E, R)) return rc;
   if (int rc = check_device()) return rc;
   return launch_status(moeq::launch_expert_mlp(wfmt, xp_q, xp_s, plan, E, R, w13, s13, w2, s2, H,
                                                I, h, h_q, h_s, o, as_stream(stream)));
@@ -314,16 +331,19 @@ int moe_expert_mlp_fp8row(const uint8_t* xp_q, const float* xp_s, const void* pl
                     w2_scales, H, I, h, h_q, h_s, o, stream);
 }
 
-int moe_combine(const uint16_t* o, const void* plan, const float* topk_w, const uint16_t* shared,
-                int T, int k, int H, uint16_t* y, void* stream) {
-  if (T < 0 || k <= 0 || H <= 0) return MOEQ_ERR_INVALID_ARG;
-  if (k > MOEQ_MAX_TOPK) return MOEQ_ERR_UNSUPPORTED;
+int moe_combine(const uint16_t* o, const void* plan, size_t plan_bytes, int E,
+                const float* topk_w, const uint16_t* shared, int T, int k, int H, uint16_t* y,
+                void* stream) {
+  if (T < 0 || k <= 0 || H <= 0 || E <= 0) return MOEQ_ERR_INVALID_ARG;
+  if (k > MOEQ_MAX_TOPK || E > MOEQ_MAX_EXPERTS) return MOEQ_ERR_UNSUPPORTED;
+  if (int64_t(T) * k > 0x3FFFFFFF) return MOEQ_ERR_UNSUPPORTED;
   if (H % 8 != 0) return MOEQ_ERR_UNSUPPORTED;
   if ((H / 8 + 255) / 256 > 65535) return MOEQ_ERR_UNSUPPORTED;   // grid (T, 2048-column blocks)
   if (T > 0 && (!o || !plan || !topk_w || !y)) return MOEQ_ERR_INVALID_ARG;
   if (T > 0 && (!aligned16(o) || !aligned16(y) || (shared && !aligned16(shared))))
     return MOEQ_ERR_INVALID_ARG;
   if (T == 0) return MOEQ_OK;
+  if (int rc = check_plan(plan, plan_bytes, E, T * k)) return rc;
   if (int rc = check_device()) return rc;
   return launch_status(moeq::launch_combine(o, plan, topk_w, shared, T, k, H, y, as_stream(stream)));
 }

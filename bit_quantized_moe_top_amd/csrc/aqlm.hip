@@ -80,7 +80,7 @@ struct AqStage {
 template <int EPI, int NBOOK, bool W16_0, bool W16_1>
 __global__ void __launch_bounds__(kThreads, 3)
 gemm_aqlm_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int E, int R,
-                 const int32_t* slab_of, const uint8_t* codes0, const uint8_t* codes1,
+                 const int32_t* slab_of, int S, const uint8_t* codes0, const uint8_t* codes1,
                  const uint16_t* book0, const uint16_t* book1, int last0, int last1,
                  const _Float16* row_scale, int N, int K, void* out, int out_f32) {
   const int lane = threadIdx.x & 63;
@@ -92,7 +92,7 @@ gemm_aqlm_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
   TileInfo ti;
   if (!tile_info(plan, E, R, tile, ti)) return;   // wave-uniform
   const int slab = slab_of ? slab_of[ti.e] : ti.e;
-  if (slab < 0) return;                                 // wave-uniform
+  if (slab < 0 || slab >= S) return;                    // wave-uniform
   const int G = K >> 7;
   const int64_t code_row0 = int64_t(K >> 3) * (W16_0 ? 2 : 1);   // bytes per row of codes
   const int64_t code_row1 = int64_t(K >> 3) * (W16_1 ? 2 : 1);
@@ -172,12 +172,12 @@ gemm_aqlm_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
 
 template <int EPI, int NBOOK, bool W16_0, bool W16_1>
 void launch_aqlm_kernel(dim3 grid, hipStream_t stream, const uint8_t* a_q, const float* a_s,
-                        const int32_t* plan, int E, int R, const int32_t* slab_of,
+                        const int32_t* plan, int E, int R, const int32_t* slab_of, int S,
                         const void* const* codes, const int* entries,
                         const uint16_t* const* books, const uint16_t* row_scale, int N, int K,
                         void* out, int out_f32) {
   hipLaunchKernelGGL((gemm_aqlm_kernel<EPI, NBOOK, W16_0, W16_1>), grid, dim3(kThreads), 0, stream,
-                     a_q, a_s, plan, E, R, slab_of, static_cast<const uint8_t*>(codes[0]),
+                     a_q, a_s, plan, E, R, slab_of, S, static_cast<const uint8_t*>(codes[0]),
                      NBOOK > 1 ? static_cast<const uint8_t*>(codes[1]) : nullptr, books[0],
                      NBOOK > 1 ? books[1] : nullptr, entries[0] - 1,
                      NBOOK > 1 ? entries[1] - 1 : 0, reinterpret_cast<const _Float16*>(row_scale), N,
@@ -186,38 +186,39 @@ void launch_aqlm_kernel(dim3 grid, hipStream_t stream, const uint8_t* a_q, const
 
 template <int EPI>
 void launch_aqlm_epi(dim3 grid, hipStream_t stream, const uint8_t* a_q, const float* a_s,
-                     const int32_t* plan, int E, int R, const int32_t* slab_of, int n_books,
+                     const int32_t* plan, int E, int R, const int32_t* slab_of, int S,
+                     int n_books,
                      const void* const* codes, const int* entries, const uint16_t* const* books,
                      const uint16_t* row_scale, int N, int K, void* out, int out_f32) {
   const bool w0 = entries[0] > 256;
   if (n_books == 1) {
     if (w0)
-      launch_aqlm_kernel<EPI, 1, true, false>(grid, stream, a_q, a_s, plan, E, R, slab_of, codes,
+      launch_aqlm_kernel<EPI, 1, true, false>(grid, stream, a_q, a_s, plan, E, R, slab_of, S, codes,
                                               entries, books, row_scale, N, K, out, out_f32);
     else
-      launch_aqlm_kernel<EPI, 1, false, false>(grid, stream, a_q, a_s, plan, E, R, slab_of, codes,
+      launch_aqlm_kernel<EPI, 1, false, false>(grid, stream, a_q, a_s, plan, E, R, slab_of, S, codes,
                                                entries, books, row_scale, N, K, out, out_f32);
     return;
   }
   const bool w1 = entries[1] > 256;
   if (w0 && w1)
-    launch_aqlm_kernel<EPI, 2, true, true>(grid, stream, a_q, a_s, plan, E, R, slab_of, codes,
+    launch_aqlm_kernel<EPI, 2, true, true>(grid, stream, a_q, a_s, plan, E, R, slab_of, S, codes,
                                            entries, books, row_scale, N, K, out, out_f32);
   else if (w0)
-    launch_aqlm_kernel<EPI, 2, true, false>(grid, stream, a_q, a_s, plan, E, R, slab_of, codes,
+    launch_aqlm_kernel<EPI, 2, true, false>(grid, stream, a_q, a_s, plan, E, R, slab_of, S, codes,
                                             entries, books, row_scale, N, K, out, out_f32);
   else if (w1)
-    launch_aqlm_kernel<EPI, 2, false, true>(grid, stream, a_q, a_s, plan, E, R, slab_of, codes,
+    launch_aqlm_kernel<EPI, 2, false, true>(grid, stream, a_q, a_s, plan, E, R, slab_of, S, codes,
                                             entries, books, row_scale, N, K, out, out_f32);
   else
-    launch_aqlm_kernel<EPI, 2, false, false>(grid, stream, a_q, a_s, plan, E, R, slab_of, codes,
+    launch_aqlm_kernel<EPI, 2, false, false>(grid, stream, a_q, a_s, plan, E, R, slab_of, S, codes,
                                              entries, books, row_scale, N, K, out, out_f32);
 }
 
 }  // namespace
 
 hipError_t launch_grouped_gemm_aqlm(const uint8_t* a_q, const float* a_s, const void* plan, int E,
-                                    int R, const int32_t* slab_of, int n_books,
+                                    int R, const int32_t* slab_of, int S, int n_books,
                                     const void* const* codes, const int* book_entries,
                                     const uint16_t* const* codebooks, const uint16_t* row_scale,
                                     int N, int K, int epilogue, void* out, int out_dtype,
@@ -228,10 +229,10 @@ hipError_t launch_grouped_gemm_aqlm(const uint8_t* a_q, const float* a_s, const 
   const dim3 grid(unsigned((units + 3) / 4));
   const int32_t* p = static_cast<const int32_t*>(plan);
   if (epilogue == MOEQ_EPI_SILU_MUL)
-    launch_aqlm_epi<MOEQ_EPI_SILU_MUL>(grid, stream, a_q, a_s, p, E, R, slab_of, n_books, codes,
+    launch_aqlm_epi<MOEQ_EPI_SILU_MUL>(grid, stream, a_q, a_s, p, E, R, slab_of, S, n_books, codes,
                                        book_entries, codebooks, row_scale, N, K, out, out_f32);
   else
-    launch_aqlm_epi<MOEQ_EPI_NONE>(grid, stream, a_q, a_s, p, E, R, slab_of, n_books, codes,
+    launch_aqlm_epi<MOEQ_EPI_NONE>(grid, stream, a_q, a_s, p, E, R, slab_of, S, n_books, codes,
                                    book_entries, codebooks, row_scale, N, K, out, out_f32);
   return hipGetLastError();
 }

@@ -24,6 +24,7 @@ combine_kernel(const uint16_t* __restrict__ o, const int32_t* __restrict__ plan,
   // token t = blockIdx.x, 2048-column block blockIdx.y: no division by a
   // kernel argument, so every argument load goes out in one round
   const int t = blockIdx.x;
+  const int R = T * k;
   const int c_raw = (blockIdx.y * 256 + threadIdx.x) * 8;
   const bool live = c_raw < H;
   const int c = live ? c_raw : 0;
@@ -48,13 +49,15 @@ combine_kernel(const uint16_t* __restrict__ o, const int32_t* __restrict__ plan,
   uint4 raw[MOEQ_MAX_TOPK];
 #pragma unroll
   for (int j = 0; j < MOEQ_MAX_TOPK; ++j)
-    raw[j] = *reinterpret_cast<const uint4*>(o + int64_t(max(pos[j], 0)) * H + c);
+    raw[j] = *reinterpret_cast<const uint4*>(o + int64_t(min(max(pos[j], 0), R - 1)) * H + c);
   uint4 sh = {};
   if (shared) sh = *reinterpret_cast<const uint4*>(shared + int64_t(t) * H + c);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < MOEQ_MAX_TOPK; ++j) {
-    if (j >= k || pos[j] < 0) continue;       // slots past k, or rows dropped by the permute
+    // slots past k, rows dropped by the permute (and positions outside o, which
+    // only a plan built for other sizes holds)
+    if (j >= k || pos[j] < 0 || pos[j] >= R) continue;
     float v[8];
     bf16x8_to_f32(raw[j], v);
 #pragma unroll

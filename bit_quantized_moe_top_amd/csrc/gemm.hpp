@@ -260,9 +260,11 @@ __device__ __forceinline__ bool tile_info(const int32_t* plan, int E, int R, int
   // scalar memory round trips in a row instead of one.  The values are uniform
   // over the caller's wave.
   asm volatile("" ::"s"(n), "s"(e), "s"(row0), "s"(next), "s"(end_all));
-  ti.e = e;
-  ti.row0 = row0;
-  ti.rows = min(MOEQ_TILE_M, (tile + 1 < n ? next : end_all) - row0);
+  // clamped to the caller's E and R: a plan built for other sizes then yields
+  // wrong rows, never an access outside the weight or activation buffers
+  ti.e = min(max(e, 0), E - 1);
+  ti.row0 = min(max(row0, 0), R);
+  ti.rows = max(0, min(min(MOEQ_TILE_M, (tile + 1 < n ? next : end_all) - ti.row0), R - ti.row0));
   return tile < n;
 }
 

@@ -90,10 +90,10 @@ hipError_t launch_grouped_gemm(int wfmt, const uint8_t* a_q, const float* a_s, c
                                int epilogue, void* out, int out_dtype, hipStream_t stream);
 
 // NVFP4 weights: E2M1 codes [S, N, K/2], E4M3 block-16 scales [S, N, K/16], fp32
-// per-slab scale2 [S]; slab_of [E] maps experts to slabs (-1: not NVFP4), NULL
-// for the identity
+// per-slab scale2 [S]; slab_of [E] maps experts to slabs (values outside
+// [0, S): not NVFP4), NULL for the identity
 hipError_t launch_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* plan, int E,
-                                     int R, const int32_t* slab_of, const uint8_t* w,
+                                     int R, const int32_t* slab_of, int S, const uint8_t* w,
                                      const uint8_t* w_block_scale,
                                      const float* w_scale2, int N, int K, int epilogue, void* out,
                                      int out_dtype, hipStream_t stream);
@@ -103,7 +103,7 @@ hipError_t launch_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const
 // fp16, row_scale [S, N] fp16; slab_of as for NVFP4
 constexpr int kAqlmMaxBooks = 2;
 hipError_t launch_grouped_gemm_aqlm(const uint8_t* a_q, const float* a_s, const void* plan, int E,
-                                    int R, const int32_t* slab_of, int n_books,
+                                    int R, const int32_t* slab_of, int S, int n_books,
                                     const void* const* codes, const int* book_entries,
                                     const uint16_t* const* codebooks, const uint16_t* row_scale,
                                     int N, int K, int epilogue, void* out, int out_dtype,

@@ -78,7 +78,7 @@ struct NvStage {
 template <int EPI>
 __global__ void __launch_bounds__(kThreads, 3)
 gemm_nvfp4_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int E, int R,
-                  const int32_t* slab_of, const uint8_t* w, const uint8_t* w_bs,
+                  const int32_t* slab_of, int S, const uint8_t* w, const uint8_t* w_bs,
                   const float* w_scale2, int N, int K, void* out, int out_f32) {
   const int lane = threadIdx.x & 63;
   const int ln = lane & 15, kb = lane >> 4;
@@ -90,7 +90,7 @@ gemm_nvfp4_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int
   if (!tile_info(plan, E, R, tile, ti)) return;   // wave-uniform
   // weight slab of the tile's expert; experts stored in another format are skipped
   const int slab = slab_of ? slab_of[ti.e] : ti.e;
-  if (slab < 0) return;                                 // wave-uniform
+  if (slab < 0 || slab >= S) return;                    // wave-uniform
   const float scale2 = w_scale2[slab];
   const int G = K >> 7;
 
@@ -163,7 +163,7 @@ gemm_nvfp4_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int
 }  // namespace
 
 hipError_t launch_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* plan, int E,
-                                     int R, const int32_t* slab_of, const uint8_t* w,
+                                     int R, const int32_t* slab_of, int S, const uint8_t* w,
                                      const uint8_t* w_block_scale,
                                      const float* w_scale2, int N, int K, int epilogue, void* out,
                                      int out_dtype, hipStream_t stream) {
@@ -174,10 +174,10 @@ hipError_t launch_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const
   const int32_t* p = static_cast<const int32_t*>(plan);
   if (epilogue == MOEQ_EPI_SILU_MUL)
     hipLaunchKernelGGL(gemm_nvfp4_kernel<MOEQ_EPI_SILU_MUL>, grid, dim3(kThreads), 0, stream, a_q,
-                       a_s, p, E, R, slab_of, w, w_block_scale, w_scale2, N, K, out, out_f32);
+                       a_s, p, E, R, slab_of, S, w, w_block_scale, w_scale2, N, K, out, out_f32);
   else
     hipLaunchKernelGGL(gemm_nvfp4_kernel<MOEQ_EPI_NONE>, grid, dim3(kThreads), 0, stream, a_q, a_s,
-                       p, E, R, slab_of, w, w_block_scale, w_scale2, N, K, out, out_f32);
+                       p, E, R, slab_of, S, w, w_block_scale, w_scale2, N, K, out, out_f32);
   return hipGetLastError();
 }
 

@@ -145,11 +145,13 @@ class MoELayer:
                  self.s2, out=b)
         shared = None
         if self.ws13 is not None:
-            xb = x if x.dtype == torch.bfloat16 else x.to(torch.bfloat16)
-            step("shared_gate_up", moe_shared_gemm_bf16, xb, self.ws13, EPI_SILU_MUL, out=b["sh_h"])
+            # the shared experts are bf16 MLPs of the bf16 model: their input is x itself
+            if x.dtype != torch.bfloat16:
+                raise TypeError("shared experts take bfloat16 x")
+            step("shared_gate_up", moe_shared_gemm_bf16, x, self.ws13, EPI_SILU_MUL, out=b["sh_h"])
             shared = step("shared_down", moe_shared_gemm_bf16, b["sh_h"], self.ws2, EPI_NONE,
                           out=b["shared"])
-        step("combine", moe_combine, b["o"], b["plan"], b["w"], shared, y=b["y"])
+        step("combine", moe_combine, b["o"], b["plan"], b["w"], shared, y=b["y"], E=self.E)
         return b if return_all else b["y"]
 
     __call__ = forward
@@ -225,7 +227,7 @@ class HybridMoELayer(MoELayer):
              EPI_SILU_MUL, b["h"])
         step("quant_h", quant_fp8_per_token, b["h"], q=b["h_q"], scale=b["h_s"])
         step("gemm_down", self._gemm_both, b["h_q"], b["h_s"], b["plan"], "w2", EPI_NONE, b["o"])
-        step("combine", moe_combine, b["o"], b["plan"], b["w"], None, y=b["y"])
+        step("combine", moe_combine, b["o"], b["plan"], b["w"], None, y=b["y"], E=self.E)
         return b if return_all else b["y"]
 
     __call__ = forward

@@ -44,13 +44,13 @@
 extern "C" {
 #endif
 
-#define MOEQ_ABI_VERSION 1
+#define MOEQ_ABI_VERSION 2
 
 /* status codes */
 #define MOEQ_OK               0
 #define MOEQ_ERR_INVALID_ARG  1  /* null pointer, non-positive size, misalignment, inconsistent sizes */
 #define MOEQ_ERR_UNSUPPORTED  2  /* a size outside what the kernels implement (see each call) */
-#define MOEQ_ERR_WORKSPACE    3  /* plan buffer too small */
+#define MOEQ_ERR_WORKSPACE    3  /* plan buffer smaller than moe_plan_size(E, R) */
 #define MOEQ_ERR_DEVICE       4  /* no device, or the current device is not gfx950 */
 #define MOEQ_ERR_LAUNCH       5  /* a kernel launch failed (hipGetLastError) */
 
@@ -88,6 +88,15 @@ const char* moe_status_string(int status);
  *   scratch     [chunks * E] per-chunk counts used while the plan is built
  * with max_tiles = ceil(R / MOEQ_TILE_M) + min(E, R) and chunks = max(1, ceil(R / 1024)).
  * Returns 0 for E <= 0 or R < 0.
+ *
+ * Every call that reads a plan takes its byte count (plan_bytes) and the E and
+ * R it was built for, and returns MOEQ_ERR_WORKSPACE when plan_bytes <
+ * moe_plan_size(E, R): every device read of the plan then stays inside the
+ * buffer.  A plan built by moe_permute for other E or R (the header words 0
+ * and 1 record them) is a caller error the library cannot see without reading
+ * device memory; the kernels clamp every expert id and row index they take
+ * from a plan to [0, E) and [0, R], so such a plan gives wrong values, never an
+ * access outside the caller's buffers.
  */
 size_t moe_plan_size(int E, int R);
 
@@ -260,14 +269,17 @@ int moe_requant_fp8_fnuz(const uint8_t* w_fnuz, const float* s_fnuz, int64_t row
  * ([R, N/2], out_dtype must be bf16).
  *
  *   a_q [R, K] E4M3, a_s [R] fp32 -- rows in plan order
- *   plan from moe_permute with the same E and R
- *   w_packed [E, N, K/2] (pack_int4_g128 layout), w_scales [E, N, K/128] fp32
+ *   plan, plan_bytes -- from moe_permute with the same E and R (read only)
+ *   w_packed [E, N, K/2] (pack_int4_g128 layout; the little-endian byte view of
+ *     the checkpoint's int32 [E, N, K/8] .weight_packed words, passed through
+ *     as they are), w_scales [E, N, K/128] fp32
  * Limits: K % 128 == 0, N % 128 == 0, R >= 0, 1 <= E <= MOEQ_MAX_EXPERTS;
  * a_q, w_packed and w_scales 16-byte aligned.
  */
-int moe_grouped_gemm_w4a8(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
-                          const uint8_t* w_packed, const float* w_scales, int N, int K,
-                          int epilogue, void* out, int out_dtype, void* stream);
+int moe_grouped_gemm_w4a8(const uint8_t* a_q, const float* a_s, const void* plan,
+                          size_t plan_bytes, int E, int R, const uint8_t* w_packed,
+                          const float* w_scales, int N, int K, int epilogue, void* out,
+                          int out_dtype, void* stream);
 
 /*
  * moe_grouped_gemm_w4a8_bf16s -- moe_grouped_gemm_w4a8 with bfloat16 group
@@ -276,9 +288,10 @@ int moe_grouped_gemm_w4a8(const uint8_t* a_q, const float* a_s, const void* plan
  * scale is widened exactly to fp32 and applied as in moe_grouped_gemm_w4a8.
  * Limits and errors: as moe_grouped_gemm_w4a8.
  */
-int moe_grouped_gemm_w4a8_bf16s(const uint8_t* a_q, const float* a_s, const void* plan, int E,
-                                int R, const uint8_t* w_packed, const uint16_t* w_scales, int N,
-                                int K, int epilogue, void* out, int out_dtype, void* stream);
+int moe_grouped_gemm_w4a8_bf16s(const uint8_t* a_q, const float* a_s, const void* plan,
+                                size_t plan_bytes, int E, int R, const uint8_t* w_packed,
+                                const uint16_t* w_scales, int N, int K, int epilogue, void* out,
+                                int out_dtype, void* stream);
 
 /*
  * moe_grouped_gemm_nvfp4 -- grouped GEMM over NVFP4 expert weights (the hot
@@ -295,16 +308,19 @@ int moe_grouped_gemm_w4a8_bf16s(const uint8_t* a_q, const float* a_s, const void
  * FP8 (the card quantizes only the weights; the reading used here keeps the
  * layer's activation path).
  *
- *   slab_of [E] int32 or NULL: weight slab of each routed expert, -1 for experts
- *     stored in another format, whose rows this call leaves untouched (the hybrid
- *     card's hot_ids list the routed expert of each NVFP4 slab; slab_of is its
- *     inverse).  NULL: slab e is expert e.
+ *   slab_of [E] int32 or NULL: weight slab of each routed expert; a value
+ *     outside [0, S) (-1 by convention) marks an expert stored in another
+ *     format, whose rows this call leaves untouched (the hybrid card's hot_ids
+ *     list the routed expert of each NVFP4 slab; slab_of is its inverse).
+ *     NULL: slab e is expert e (then E <= S).
+ *   S -- number of slabs in the weight tensors
  *   w_fp4 [S, N, K/2] bytes, w_block_scale [S, N, K/16] E4M3 bytes, w_scale2 [S] fp32
  * Limits: K % 128 == 0, N % 128 == 0, 1 <= E <= MOEQ_MAX_EXPERTS; a_q, w_fp4 and
  * w_block_scale 16-byte aligned.
  */
-int moe_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
-                           const int32_t* slab_of, const uint8_t* w_fp4,
+int moe_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* plan,
+                           size_t plan_bytes, int E, int R, const int32_t* slab_of, int S,
+                           const uint8_t* w_fp4,
                            const uint8_t* w_block_scale,
                            const float* w_scale2, int N, int K, int epilogue, void* out,
                            int out_dtype, void* stream);
@@ -324,7 +340,7 @@ int moe_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* pla
  * separately, never added to each other in fp16); epilogue and out as in
  * moe_grouped_gemm_w4a8.
  *
- *   slab_of [E] int32 or NULL -- as in moe_grouped_gemm_nvfp4 (cold_ids inverse)
+ *   slab_of [E] int32 or NULL, S -- as in moe_grouped_gemm_nvfp4 (cold_ids inverse)
  *   n_books 1 or 2; codes, book_entries, codebooks: HOST arrays of n_books
  *     entries: device pointers to codes_b [S, N, K/8], the entry counts
  *     (1 .. 65536), device pointers to codebook_b [entries_b, 8] fp16
@@ -334,8 +350,9 @@ int moe_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const void* pla
  * Limits: K % 128 == 0, N % 128 == 0, 1 <= E <= MOEQ_MAX_EXPERTS; a_q and the
  * codebooks 16-byte aligned, int16 codes 8-byte and uint8 codes 4-byte aligned.
  */
-int moe_grouped_gemm_aqlm(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
-                          const int32_t* slab_of, int n_books, const void* const* codes,
+int moe_grouped_gemm_aqlm(const uint8_t* a_q, const float* a_s, const void* plan,
+                          size_t plan_bytes, int E, int R, const int32_t* slab_of, int S,
+                          int n_books, const void* const* codes,
                           const int* book_entries, const uint16_t* const* codebooks,
                           const uint16_t* row_scale, int N, int K, int epilogue, void* out,
                           int out_dtype, void* stream);
@@ -352,9 +369,10 @@ int moe_grouped_gemm_aqlm(const uint8_t* a_q, const float* a_s, const void* plan
  *   w_fp8 [E, N, K] E4M3, w_row_scale [E, N] fp32
  * Limits: K % 128 == 0, N % 128 == 0; a_q, w_fp8 and w_row_scale 16-byte aligned.
  */
-int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* plan, int E, int R,
-                            const uint8_t* w_fp8, const float* w_row_scale, int N, int K,
-                            int epilogue, void* out, int out_dtype, void* stream);
+int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* plan,
+                            size_t plan_bytes, int E, int R, const uint8_t* w_fp8,
+                            const float* w_row_scale, int N, int K, int epilogue, void* out,
+                            int out_dtype, void* stream);
 
 /*
  * moe_expert_mlp_w4a8 -- the routed experts' MLP: gate/up GEMM with the
@@ -383,11 +401,6 @@ int moe_expert_mlp_w4a8(const uint8_t* xp_q, const float* xp_s, const void* plan
                         uint8_t* h_q, float* h_s, uint16_t* o, void* stream);
 
 /*
- * moe_expert_mlp_fp8row -- moe_expert_mlp_w4a8 with row-scaled FP8 expert
- * weights (the moe_grouped_gemm_fp8row arithmetic):
- *   w13 [E, 2I, H] E4M3, w13_scales [E, 2I] fp32; w2 [E, H, I] E4M3, w2_scales [E, H] fp32.
- */
-/*
  * moe_expert_mlp_w4a8_bf16s -- moe_expert_mlp_w4a8 with bfloat16 group scales
  * (w13_scales [E, 2I, H/128], w2_scales [E, H, I/128]): exactly the three calls
  * with moe_grouped_gemm_w4a8_bf16s, bit-identical.  Limits: as
@@ -399,6 +412,11 @@ int moe_expert_mlp_w4a8_bf16s(const uint8_t* xp_q, const float* xp_s, const void
                               const uint16_t* w2_scales, int H, int I, uint16_t* h, uint8_t* h_q,
                               float* h_s, uint16_t* o, void* stream);
 
+/*
+ * moe_expert_mlp_fp8row -- moe_expert_mlp_w4a8 with row-scaled FP8 expert
+ * weights (the moe_grouped_gemm_fp8row arithmetic):
+ *   w13 [E, 2I, H] E4M3, w13_scales [E, 2I] fp32; w2 [E, H, I] E4M3, w2_scales [E, H] fp32.
+ */
 int moe_expert_mlp_fp8row(const uint8_t* xp_q, const float* xp_s, const void* plan,
                           size_t plan_bytes,
                           int E, int R, const uint8_t* w13, const float* w13_scales,
@@ -412,20 +430,23 @@ int moe_expert_mlp_fp8row(const uint8_t* xp_q, const float* xp_s, const void* pl
  *   y[t, c] = bf16( sum_{j=0}^{k-1} w[t, j] * o[row_pos[t*k + j], c] + shared[t, c] )
  * Rows dropped by moe_permute contribute nothing.
  *
- *   o [R, H] bf16 in plan order;  topk_w [T, k] fp32;  shared [T, H] bf16 or NULL
- *   y [T, H] bf16 (out)
- * Limits: H % 8 == 0; o, shared and y 16-byte aligned.
+ *   o [R, H] bf16 in plan order (R = T*k)
+ *   plan, plan_bytes -- from moe_permute with E and R = T*k (read only)
+ *   topk_w [T, k] fp32;  shared [T, H] bf16 or NULL;  y [T, H] bf16 (out)
+ * Limits: H % 8 == 0, 1 <= k <= MOEQ_MAX_TOPK, 1 <= E <= MOEQ_MAX_EXPERTS;
+ * o, shared and y 16-byte aligned.
  */
-int moe_combine(const uint16_t* o, const void* plan, const float* topk_w, const uint16_t* shared,
-                int T, int k, int H, uint16_t* y, void* stream);
+int moe_combine(const uint16_t* o, const void* plan, size_t plan_bytes, int E,
+                const float* topk_w, const uint16_t* shared, int T, int k, int H, uint16_t* y,
+                void* stream);
 
 /*
  * moe_shared_gemm_bf16 -- dense bf16 GEMM for the shared experts.
  *
- * Inkling-Small keeps its 2 shared experts per sparse layer in BF16
- * ("wstewart3/Inkling-Small-W4A8-G128", section 1: "retained ... shared-expert
- * parameters" stay BF16; section 7 dry-run table: unquantized shared gate/up
- * pairs).  out = epilogue(a @ w^T) with fp32 accumulation:
+ * Inkling-Small keeps its 2 shared experts per sparse layer in BF16: the W4A8
+ * conversion quantizes only the routed experts' weights
+ * ("wstewart3/Inkling-Small-W4A8-G128", section 1 table; section 7 dry-run
+ * table lists the shared gate/up pairs among the unquantized tensors).  out = epilogue(a @ w^T) with fp32 accumulation:
  *   NONE:     out[m, n] = bf16(acc[m, n])                       [M, N]
  *   SILU_MUL: out[m, i] = bf16(silu(acc[m, i]) * acc[m, N/2+i])  [M, N/2]
  *

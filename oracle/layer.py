@@ -286,13 +286,20 @@ def fp8row_rows(a_q, a_s, experts, wq_of, srow_of):
 
 
 def nvfp4_dequant(packed, block_scale, scale2):
-    """NVFP4 hot-expert weights ("Inkling-512k-NVFP4-AQLM-hybrid", "Dequant math",
-    hot): W = LUT[code] * scale[block of 16 along K] * scale2, with packed
-    [N, K/2] codes (low nibble first), block_scale [N, K/16] E4M3 bytes and the
-    per-expert fp32 scale2.  Exact in float64."""
-    codes = unpack_fp4(packed)
-    bs = e4m3_decode(block_scale)
-    return e2m1_decode(codes) * np.repeat(bs, 16, axis=-1) * float(np.float32(scale2))
+    """NVFP4 hot-expert weights ("Inkling-512k-NVFP4-AQLM-hybrid", "On-disk tensor
+    format" and "Dequant math", hot experts), element by element:
+
+      code(n, k) = (packed[n, k // 2] >> (4 * (k % 2))) & 0xF   (earlier weight in bits 0-3)
+      W[n, k]    = e2m1(code(n, k)) * e4m3(block_scale[n, k // 16]) * scale2
+
+    packed [N, K/2] bytes, block_scale [N, K/16] E4M3 bytes, scale2 the expert's
+    fp32 scale.  Every factor is exact in float64, and so is the product."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    N, K = packed.shape[0], 2 * packed.shape[1]
+    k = np.arange(K)
+    code = (packed[:, k // 2] >> (4 * (k % 2)).astype(np.uint8)) & 0xF      # [N, K]
+    bscale = e4m3_decode(np.asarray(block_scale, dtype=np.uint8)[:, k // 16])  # [N, K]
+    return e2m1_decode(code) * bscale * float(np.float32(scale2))
 
 
 def nvfp4_rows(a_q, a_s, experts, packed_of, bscale_of, scale2_of):
@@ -312,20 +319,23 @@ def nvfp4_rows(a_q, a_s, experts, packed_of, bscale_of, scale2_of):
 
 
 def aqlm_dequant(codes, books, row_scale):
-    """AQLM cold-expert weights ("Inkling-512k-NVFP4-AQLM-hybrid", "Dequant math",
-    cold): for output row r and group g of 8 input channels,
-    W[r, 8g:8g+8] = (sum over books b of book_b[codes_b[r, g]]) * row_scale[r].
-    codes: list of [N, K/8] arrays (uint8, or int16 whose negative values wrap to
-    the unsigned row, idx & 0xFFFF); books: list of fp16 [entries_b, 8];
-    row_scale: fp16 [N].  Exact in float64."""
-    acc = None
+    """AQLM cold-expert weights ("Inkling-512k-NVFP4-AQLM-hybrid", "On-disk tensor
+    format" and "Dequant math", cold experts), element by element: input channel k
+    of output row n lies in group k // 8 at position k % 8, and
+
+      W[n, k] = row_scale[n] * sum over books b of book_b[codes_b[n, k // 8] & 0xFFFF, k % 8]
+
+    codes: list of [N, K/8] arrays (uint8, or int16 whose negative values stand
+    for the unsigned index, hence & 0xFFFF); books: list of fp16 [entries_b, 8];
+    row_scale: fp16 [N].  The sum over books and the scaling are exact in float64."""
+    N, G = np.asarray(codes[0]).shape
+    k = np.arange(8 * G)
+    w = np.zeros((N, 8 * G), dtype=np.float64)
     for c, bk in zip(codes, books):
-        idx = np.asarray(c).astype(np.int64) & 0xFFFF
-        rows = np.asarray(bk, dtype=np.float16).astype(np.float64)[idx]     # [N, K/8, 8]
-        acc = rows if acc is None else acc + rows
-    N, G, _ = acc.shape
-    w = acc.reshape(N, G * 8)
-    return w * np.asarray(row_scale, dtype=np.float16).astype(np.float64)[:, None]
+        idx = np.asarray(c).astype(np.int64) & 0xFFFF                      # [N, G]
+        book = np.asarray(bk, dtype=np.float16).astype(np.float64)         # [entries, 8]
+        w += book[idx[:, k // 8], k % 8]                                   # [N, K]
+    return np.asarray(row_scale, dtype=np.float16).astype(np.float64)[:, None] * w
 
 
 def aqlm_rows(a_q, a_s, experts, codes_of, books, scale_of):

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert mq.moe_abi_version() == 1
+    assert mq.moe_abi_version() == 2
     assert mq.moe_status_string(0) == "ok"
     for s in range(1, 6):
         assert mq.moe_status_string(s) not in ("ok", "unknown status")
@@ -99,14 +99,41 @@ def test_argument_errors_are_reported_without_a_gpu():
     # pack
     assert L.pack_int4_g128(FAKE, 4, 100, FAKE, FAKE, N) == UNSUPPORTED
     assert L.pack_int4_g128(N, 4, 128, FAKE, FAKE, N) == INVALID
-    # grouped GEMMs
-    for fn in (L.moe_grouped_gemm_w4a8, L.moe_grouped_gemm_fp8row):
-        assert fn(FAKE, FAKE, FAKE, 8, 32, FAKE, FAKE, 100, 256, 0, FAKE, 1, N) == UNSUPPORTED
-        assert fn(FAKE, FAKE, FAKE, 8, 32, FAKE, FAKE, 256, 200, 0, FAKE, 1, N) == UNSUPPORTED
-        assert fn(FAKE, FAKE, FAKE, 8, 32, FAKE, FAKE, 256, 256, 1, FAKE, 0, N) == INVALID
-        assert fn(FAKE, FAKE, FAKE, 8, 32, FAKE, FAKE, 256, 256, 5, FAKE, 1, N) == INVALID
-        assert fn(N, FAKE, FAKE, 8, 32, FAKE, FAKE, 256, 256, 0, FAKE, 1, N) == INVALID
-        assert fn(N, N, N, 8, 0, N, N, 256, 256, 0, N, 1, N) == OK
+    # grouped GEMMs (plan_bytes after the plan)
+    pb = mq.moe_plan_size(8, 32)
+    for fn in (L.moe_grouped_gemm_w4a8, L.moe_grouped_gemm_fp8row, L.moe_grouped_gemm_w4a8_bf16s):
+        assert fn(FAKE, FAKE, FAKE, pb, 8, 32, FAKE, FAKE, 100, 256, 0, FAKE, 1, N) == UNSUPPORTED
+        assert fn(FAKE, FAKE, FAKE, pb, 8, 32, FAKE, FAKE, 256, 200, 0, FAKE, 1, N) == UNSUPPORTED
+        assert fn(FAKE, FAKE, FAKE, pb, 8, 32, FAKE, FAKE, 256, 256, 1, FAKE, 0, N) == INVALID
+        assert fn(FAKE, FAKE, FAKE, pb, 8, 32, FAKE, FAKE, 256, 256, 5, FAKE, 1, N) == INVALID
+        assert fn(N, FAKE, FAKE, pb, 8, 32, FAKE, FAKE, 256, 256, 0, FAKE, 1, N) == INVALID
+        assert fn(N, N, N, 0, 8, 0, N, N, 256, 256, 0, N, 1, N) == OK
+        # a plan buffer smaller than moe_plan_size(E, R): too few bytes, or built for a smaller R
+        assert fn(FAKE, FAKE, FAKE, pb - 4, 8, 32, FAKE, FAKE, 256, 256, 0, FAKE, 1, N) == WORKSPACE
+        assert fn(FAKE, FAKE, FAKE, mq.moe_plan_size(8, 16), 8, 32, FAKE, FAKE, 256, 256, 0, FAKE,
+                  1, N) == WORKSPACE
+        assert fn(FAKE, FAKE, FAKE, mq.moe_plan_size(4, 32), 8, 32, FAKE, FAKE, 256, 256, 0, FAKE,
+                  1, N) == WORKSPACE
+        assert fn(FAKE, FAKE, ctypes.c_void_p(4098), pb, 8, 32, FAKE, FAKE, 256, 256, 0, FAKE, 1,
+                  N) == INVALID                                                   # plan misaligned
+    # NVFP4 / AQLM: plan bytes and the slab count S
+    nv = lambda pbytes, E, slab, S: L.moe_grouped_gemm_nvfp4(  # noqa: E731
+        FAKE, FAKE, FAKE, pbytes, E, 32, slab, S, FAKE, FAKE, FAKE, 256, 256, 0, FAKE, 1, N)
+    assert nv(pb - 4, 8, FAKE, 3) == WORKSPACE
+    assert nv(pb, 8, N, 3) == INVALID                 # identity slab map with fewer slabs than E
+    assert nv(pb, 8, FAKE, -1) == INVALID
+    assert nv(pb, 8, FAKE, 0) == OK                   # no expert in this format: nothing to do
+    books = (ctypes.c_void_p * 1)(FAKE)
+    ents = (ctypes.c_int * 1)(65536)
+    aq = lambda pbytes, E, slab, S: L.moe_grouped_gemm_aqlm(  # noqa: E731
+        FAKE, FAKE, FAKE, pbytes, E, 32, slab, S, 1, books, ents, books, FAKE, 256, 256, 0, FAKE,
+        1, N)
+    assert aq(pb - 4, 8, FAKE, 3) == WORKSPACE
+    assert aq(pb, 8, N, 3) == INVALID
+    assert aq(pb, 8, FAKE, 0) == OK
+    bad_ents = (ctypes.c_int * 1)(65537)
+    assert L.moe_grouped_gemm_aqlm(FAKE, FAKE, FAKE, pb, 8, 32, FAKE, 3, 1, books, bad_ents, books,
+                                   FAKE, 256, 256, 0, FAKE, 1, N) == UNSUPPORTED
     # fused expert MLP
     for fn in (L.moe_expert_mlp_w4a8, L.moe_expert_mlp_fp8row):
         ok = (FAKE, FAKE, FAKE, big, 8, 24, FAKE, FAKE, FAKE, FAKE, 4096, 2048, FAKE, FAKE, FAKE,
@@ -118,12 +145,16 @@ def test_argument_errors_are_reported_without_a_gpu():
         assert fn(*ok[:3], 64, *ok[4:]) == WORKSPACE                        # plan too small
         assert fn(ctypes.c_void_p(4100), *ok[1:]) == INVALID                # xp_q misaligned
         assert fn(N, N, N, 0, 8, 0, N, N, N, N, 4096, 2048, N, N, N, N, N) == OK   # R = 0
-    # combine / shared
-    assert L.moe_combine(FAKE, FAKE, FAKE, N, 4, 2, 12, FAKE, N) == UNSUPPORTED
-    assert L.moe_combine(FAKE, N, FAKE, N, 4, 2, 16, FAKE, N) == INVALID
-    assert L.moe_combine(FAKE, FAKE, FAKE, N, 4, 9, 16, FAKE, N) == UNSUPPORTED   # k > 8
+    # combine / shared (plan_bytes and E after the plan)
+    cb = mq.moe_plan_size(8, 8)
+    assert L.moe_combine(FAKE, FAKE, cb, 8, FAKE, N, 4, 2, 12, FAKE, N) == UNSUPPORTED
+    assert L.moe_combine(FAKE, N, cb, 8, FAKE, N, 4, 2, 16, FAKE, N) == INVALID
+    assert L.moe_combine(FAKE, FAKE, cb, 8, FAKE, N, 4, 9, 16, FAKE, N) == UNSUPPORTED   # k > 8
+    assert L.moe_combine(FAKE, FAKE, cb, 0, FAKE, N, 4, 2, 16, FAKE, N) == INVALID       # E = 0
+    assert L.moe_combine(FAKE, FAKE, cb - 4, 8, FAKE, N, 4, 2, 16, FAKE, N) == WORKSPACE
+    assert L.moe_combine(FAKE, FAKE, cb, 8, FAKE, N, 8, 2, 16, FAKE, N) == WORKSPACE      # R = 16
     # more 2048-column blocks than the grid's second dimension holds
-    assert L.moe_combine(FAKE, FAKE, FAKE, N, 0, 2, 1 << 28, FAKE, N) == UNSUPPORTED
+    assert L.moe_combine(FAKE, FAKE, cb, 8, FAKE, N, 0, 2, 1 << 28, FAKE, N) == UNSUPPORTED
     assert L.moe_shared_gemm_bf16(FAKE, FAKE, 4, 100, 64, 0, FAKE, N) == UNSUPPORTED
     assert L.moe_shared_gemm_bf16(FAKE, FAKE, 4, 128, 48, 0, FAKE, N) == UNSUPPORTED
 
@@ -132,7 +163,10 @@ def test_argument_errors_are_reported_without_a_gpu():
 def test_valid_call_without_gpu_reports_device_error():
     L = mq.lib
     assert L.moe_route_topk(FAKE, None, 4, 8, 2, 1, FAKE, FAKE, None) == DEVICE
-    assert L.moe_combine(FAKE, FAKE, FAKE, None, 4, 2, 16, FAKE, None) == DEVICE
+    assert L.moe_combine(FAKE, FAKE, mq.moe_plan_size(8, 8), 8, FAKE, None, 4, 2, 16, FAKE,
+                         None) == DEVICE
+    assert L.moe_grouped_gemm_w4a8(FAKE, FAKE, FAKE, mq.moe_plan_size(8, 32), 8, 32, FAKE, FAKE,
+                                   256, 256, 0, FAKE, 1, None) == DEVICE
     assert L.moe_expert_mlp_w4a8(FAKE, FAKE, FAKE, 1 << 20, 8, 24, FAKE, FAKE, FAKE, FAKE, 256,
                                  128, FAKE, FAKE, FAKE, FAKE, None) == DEVICE
 
@@ -142,3 +176,25 @@ def test_python_binding_raises_on_bad_input():
         mq.moe_route_topk(torch.zeros(2, 8, dtype=torch.float64), 2)
     with pytest.raises(ValueError):
         mq.moe_route_topk(torch.zeros(2, 8), 2)        # host tensor
+
+
+def test_binding_plan_shape_check():
+    # a plan tensor remembers the (E, R) it was built for; calls with other sizes
+    # are rejected in Python, before the C ABI (no device memory is read)
+    plan = torch.zeros(mq.moe_plan_size(8, 32) // 4, dtype=torch.int32)
+    mq._mark_plan(plan, 8, 32)
+    with pytest.raises(ValueError, match="built for"):
+        mq._plan_shape_ok(plan, 8, 16)
+    with pytest.raises(ValueError, match="built for"):
+        mq._plan_shape_ok(plan, 4, 32)
+    mq._plan_shape_ok(plan, 8, 32)
+    unmarked = torch.zeros(4, dtype=torch.int32)
+    mq._plan_shape_ok(unmarked, 8, 32)                 # no record: nothing to compare
+
+
+def test_binding_views_int32_packed_weights():
+    # the checkpoint's int32 [N, K/8] .weight_packed words are the GEMM's [N, K/2] bytes
+    words = torch.tensor([[0x76543210, -0x1234568]], dtype=torch.int32)
+    b = words.view(torch.uint8)
+    assert b.shape == (1, 8)
+    assert b.tolist() == [[0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]]

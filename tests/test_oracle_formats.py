@@ -76,7 +76,7 @@ def test_e2m1_table_matches_the_format_definition():
 
 
 def test_fp4_packing_low_nibble_first():
-    # the card: "low nibble is the first weight of each pair"
+    # the hybrid card's packing puts the earlier weight of each byte's pair in bits 0-3
     assert F.unpack_fp4(np.array([[0x21, 0xF8]], dtype=np.uint8)).tolist() == [[1, 2, 8, 15]]
     rng = np.random.default_rng(31)
     c = rng.integers(0, 16, (5, 64)).astype(np.uint8)
