@@ -283,23 +283,37 @@ int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* pl
                      epilogue, out, out_dtype, stream);
 }
 
-static int mlp_common(int wfmt, const uint8_t* xp_q, const float* xp_s, const void* plan,
-                      size_t plan_bytes, int E, int R, const uint8_t* w13, const void* s13,
-                      const uint8_t* w2, const void* s2, int H, int I, uint16_t* h, uint8_t* h_q,
-                      float* h_s, uint16_t* o, void* stream) {
+// the checks of the expert MLP calls; with_intermediates: h, h_q, h_s are
+// caller buffers (else the library's scratch array holds them)
+static int mlp_checks(const uint8_t* xp_q, const float* xp_s, const void* plan, size_t plan_bytes,
+                      int E, int R, const uint8_t* w13, const void* s13, const uint8_t* w2,
+                      const void* s2, int H, int I, bool with_intermediates, const uint16_t* h,
+                      const uint8_t* h_q, const float* h_s, const uint16_t* o) {
   if (R < 0 || E <= 0 || H <= 0 || I <= 0) return MOEQ_ERR_INVALID_ARG;
   if (E > MOEQ_MAX_EXPERTS) return MOEQ_ERR_UNSUPPORTED;
   if (H % 128 != 0 || I % 128 != 0) return MOEQ_ERR_UNSUPPORTED;
   if (int64_t(2 * int64_t(I) / 128) * moeq::plan_max_tiles(E, R) > 0x7FFFFFF0 ||
       int64_t(H / 128) * moeq::plan_max_tiles(E, R) > 0x7FFFFFF0)
     return MOEQ_ERR_UNSUPPORTED;
-  if (R > 0 && (!xp_q || !xp_s || !plan || !w13 || !s13 || !w2 || !s2 || !h || !h_q || !h_s || !o))
+  if (R > 0 && (!xp_q || !xp_s || !plan || !w13 || !s13 || !w2 || !s2 || !o))
     return MOEQ_ERR_INVALID_ARG;
-  if (R > 0 && (!aligned16(xp_q) || !aligned16(h_q) || !aligned16(h) || !aligned16(w13) ||
-                !aligned16(s13) || !aligned16(w2) || !aligned16(s2)))
+  if (R > 0 && with_intermediates && (!h || !h_q || !h_s)) return MOEQ_ERR_INVALID_ARG;
+  if (R > 0 && (!aligned16(xp_q) || !aligned16(w13) || !aligned16(s13) || !aligned16(w2) ||
+                !aligned16(s2)))
     return MOEQ_ERR_INVALID_ARG;
+  if (R > 0 && with_intermediates && (!aligned16(h_q) || !aligned16(h))) return MOEQ_ERR_INVALID_ARG;
   if (R == 0) return MOEQ_OK;
-  if (int rc = check_plan(plan, plan_bytes, E, R)) return rc;
+  return check_plan(plan, plan_bytes, E, R);
+}
+
+static int mlp_common(int wfmt, const uint8_t* xp_q, const float* xp_s, const void* plan,
+                      size_t plan_bytes, int E, int R, const uint8_t* w13, const void* s13,
+                      const uint8_t* w2, const void* s2, int H, int I, uint16_t* h, uint8_t* h_q,
+                      float* h_s, uint16_t* o, void* stream) {
+  if (int rc = mlp_checks(xp_q, xp_s, plan, plan_bytes, E, R, w13, s13, w2, s2, H, I, true, h,
+                          h_q, h_s, o))
+    return rc;
+  if (R == 0) return MOEQ_OK;
   if (int rc = check_device()) return rc;
   return launch_status(moeq::launch_expert_mlp(wfmt, xp_q, xp_s, plan, E, R, w13, s13, w2, s2, H,
                                                I, h, h_q, h_s, o, as_stream(stream)));

@@ -29,24 +29,9 @@ namespace moeq {
 
 namespace {
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-
 // chunks of codes in flight per wave (two books hold twice the gathered rows)
 template <int NBOOK>
 constexpr int kAqDepth = (NBOOK > 1) ? 2 : 3;
-
-__device__ __forceinline__ v4f mfma_f16(const h8& a, const h8& b, const v4f& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ h8 fp8x8_to_f16(uint32_t d0, uint32_t d1) {
-  const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
-  const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
-  const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
-  const h2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
-  return h8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
 
 // the 4 codes of a lane for one chunk: 16-bit (int16, entry = code & 0xFFFF) or 8-bit
 template <bool W16>

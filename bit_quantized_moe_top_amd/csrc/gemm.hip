@@ -247,7 +247,7 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
     // the next group's slice (its slot is not the one refilled below)
     const int next = (slot + 1 == kDepth) ? 0 : slot + 1;
     const uint4 x0 = st[next].a0, x1 = st[next].a1;
-    v8i bop[CB];
+    OperandT<WFMT> bop[CB];
     float sg[CB];
 #pragma unroll
     for (int j = 0; j < CB; ++j) bop[j] = st[slot].b[j].operand();
@@ -264,7 +264,7 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
     for (int i = 0; i < 4; ++i) {
       if (i < nrb) {
         const uint4* ap = reinterpret_cast<const uint4*>(&As[buf][(16 * i + ln) * kRowDw + kb * 8]);
-        const v8i aop = as_v8i(ap[0], ap[1]);
+        const OperandT<WFMT> aop = a_operand_staged<WFMT>(ap[0], ap[1]);
 #pragma unroll
         for (int j = 0; j < CB; ++j) accumulate<WFMT>(acc[i][j], aop, bop[j], sg[j]);
       }

@@ -13,8 +13,9 @@
 //              accumulate).  One MFMA covers exactly one 128-wide group: its fp32
 //              result is the group's partial sum, which is scaled by the group
 //              scale and added to the running fp32 accumulator.
-//   kFp8Row -- E4M3 weights with one fp32 scale per output row: the MFMA
-//              accumulates over all of K and the row scale is applied at the end.
+//   kFp8Row -- E4M3 weights with one fp32 scale per output row: each MFMA's
+//              128-wide partial sum is added to the fp32 accumulator and the row
+//              scale is applied at the end.
 //
 // MFMA operand layout (16x16x128, 8 VGPRs per operand): lane (r = l % 16,
 // kb = l / 16) supplies 32 K-values of row r; the result lane l holds column
@@ -62,6 +63,8 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
 constexpr int kRowDw = 36;         // LDS row stride in dwords (128 B + 16 B pad)
@@ -193,6 +196,35 @@ __device__ __forceinline__ v8i as_v8i(const uint4& x0, const uint4& x1) {
   return r;
 }
 
+__device__ __forceinline__ v4f mfma_f16(const h8& a, const h8& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 8 E4M3 bytes (two dwords) -> 8 f16, exact (every E4M3 value is an f16 value)
+__device__ __forceinline__ h8 fp8x8_to_f16(uint32_t d0, uint32_t d1) {
+  const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
+  const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
+  const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
+  const h2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
+  return h8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// A lane's 32 K-values of one row as four f16 operands of v_mfma_f32_16x16x32_f16:
+// m[j] holds the lane's bytes 8 j .. 8 j + 7, so MFMA j of a 128-K group sums
+// K 32 kb + 8 j + (0..7) over the lanes kb -- each K once, the same mapping for
+// both operands.
+struct F16x32 {
+  h8 m[4];
+};
+__device__ __forceinline__ F16x32 fp8x32_to_f16(const uint4& x0, const uint4& x1) {
+  F16x32 r;
+  r.m[0] = fp8x8_to_f16(x0.x, x0.y);
+  r.m[1] = fp8x8_to_f16(x0.z, x0.w);
+  r.m[2] = fp8x8_to_f16(x1.x, x1.y);
+  r.m[3] = fp8x8_to_f16(x1.z, x1.w);
+  return r;
+}
+
 // One group scale.  A relaxed atomic load: the compiler may neither merge the
 // scale loads of different groups into wide loads hoisted ahead of the K sweep
 // (which costs registers and spills in the unrolled sweep) nor move them.
@@ -227,12 +259,43 @@ struct BFrag<kFp8Row> {
     raw0 = p[0];
     raw1 = p[1];
   }
-  __device__ __forceinline__ v8i operand() const { return as_v8i(raw0, raw1); }
+  __device__ __forceinline__ F16x32 operand() const { return fp8x32_to_f16(raw0, raw1); }
 };
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
   // cbsz = blgp = 0: both operands FP8 E4M3; no block scales.
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// MFMA operand of each weight format: INT4 codes become E4M3 bytes for the FP8
+// MFMA.  Row-scaled FP8 weights and their activations become f16 for the f16
+// MFMA: the FP8 MFMAs sum their products in a narrower internal format (for
+// products of two full-range E4M3 values the result was measured up to 2e-5 of
+// the sum of the products' magnitudes away from the exact sum, against 3e-8 --
+// fp32 rounding -- for the same products through v_mfma_f32_16x16x32_f16), which
+// would leave the row-FP8 layer's h about 4x further from the exact values than
+// the INT4 layer's (whose integer-valued weights keep the products' exponents
+// close).  The f16 MFMA has half the FP8 rate; the row-FP8 layer streams 64
+// weight bytes per 128 flops of each row and stays HBM-bound.
+template <int WFMT>
+struct OperandOf { using type = v8i; };
+template <>
+struct OperandOf<kFp8Row> { using type = F16x32; };
+template <int WFMT>
+using OperandT = typename OperandOf<WFMT>::type;
+
+// a lane's 32 activation bytes as the format's operand (INT4: reordered to the
+// order the nibble unpack produces; FP8-row: as f16)
+template <int WFMT>
+__device__ __forceinline__ OperandT<WFMT> a_operand(const uint4& x0, const uint4& x1) {
+  if constexpr (WFMT == kFp8Row) return fp8x32_to_f16(x0, x1);
+  else return shuffle_a(x0, x1);
+}
+// the same from bytes staged in LDS, where INT4 activations are kept reordered
+template <int WFMT>
+__device__ __forceinline__ OperandT<WFMT> a_operand_staged(const uint4& x0, const uint4& x1) {
+  if constexpr (WFMT == kFp8Row) return fp8x32_to_f16(x0, x1);
+  else return as_v8i(x0, x1);
 }
 
 struct TileInfo {
@@ -351,15 +414,22 @@ __device__ __forceinline__ void pin(v4f& a) {
   asm volatile("" : "+v"(a));
 }
 
-template <int WFMT>
-__device__ __forceinline__ void accumulate(v4f& acc, const v8i& a, const v8i& b, float s) {
-  if (kIsW4<WFMT>) {
-    const v4f part = mfma_fp8(a, b, v4f{0.f, 0.f, 0.f, 0.f});
+// INT4: one FP8 MFMA per 128-K group from zero, its partial sum scaled by the
+// group scale into the fp32 accumulator.  FP8-row: four f16 MFMAs accumulating
+// into it directly (the row scale is applied at the end).
+__device__ __forceinline__ void accumulate_op(v4f& acc, const v8i& a, const v8i& b, float s) {
+  const v4f part = mfma_fp8(a, b, v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] = fmaf(s, part[v], acc[v]);
-  } else {
-    acc = mfma_fp8(a, b, acc);
-  }
+  for (int v = 0; v < 4; ++v) acc[v] = fmaf(s, part[v], acc[v]);
+}
+__device__ __forceinline__ void accumulate_op(v4f& acc, const F16x32& a, const F16x32& b, float) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = mfma_f16(a.m[j], b.m[j], acc);
+}
+template <int WFMT>
+__device__ __forceinline__ void accumulate(v4f& acc, const OperandT<WFMT>& a,
+                                           const OperandT<WFMT>& b, float s) {
+  accumulate_op(acc, a, b, s);
 }
 
 // Runs consume(slot, g, refill) for g = 0 .. G-1 over a ring of kDepth slots
@@ -512,8 +582,8 @@ __device__ __forceinline__ void wave_sweep(v4f (&acc)[NB], const uint8_t* a_q, i
   };
   auto consume = [&](int slot, int g, bool refill) {
     const WaveStage<WFMT, NB>& s = st[slot];
-    const v8i aop = kIsW4<WFMT> ? shuffle_a(s.a0, s.a1) : as_v8i(s.a0, s.a1);
-    v8i b[NB];
+    const OperandT<WFMT> aop = a_operand<WFMT>(s.a0, s.a1);
+    OperandT<WFMT> b[NB];
     float sg[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {

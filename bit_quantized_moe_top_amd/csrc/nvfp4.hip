@@ -35,23 +35,7 @@ namespace moeq {
 
 namespace {
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-
 constexpr int kNvDepth = 3;   // 128-K chunks in flight per wave (4 spills)
-
-__device__ __forceinline__ v4f mfma_f16(const h8& a, const h8& b, const v4f& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// 8 E4M3 bytes (two dwords) -> 8 f16, exact
-__device__ __forceinline__ h8 fp8x8_to_f16(uint32_t d0, uint32_t d1) {
-  const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
-  const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
-  const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
-  const h2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
-  return h8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
 
 // 8 E2M1 codes (one dword, low nibble first) times their block scale -> 8 f16, exact
 __device__ __forceinline__ h8 fp4x8_to_f16(uint32_t w, h2 s) {

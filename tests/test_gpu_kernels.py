@@ -142,6 +142,57 @@ def test_e4m3_encoder_boundary_sweep():
     np.testing.assert_array_equal(q.cpu().numpy()[:, 1:], F.e4m3_encode(x[:, 1:]))
 
 
+def _rounding_window_rows(n_rows, K, seed):
+    """fp32 rows with random non-unit scales whose quotients x / s land within
+    +-12 fp32 ulp of every E4M3 rounding midpoint (both signs), so that both the
+    reciprocal fast path and the IEEE-division fallback of the encoder, and the
+    edge between them (8 ulp), meet values that round differently one ulp apart."""
+    rng = np.random.default_rng(seed)
+    pos = F.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)          # 126 midpoints
+    offs = np.arange(-12, 13)
+    targets = []
+    for j in offs:                                               # m + j ulp(m), exact in fp32
+        t = mids.copy()
+        step = np.float32(np.inf) if j > 0 else np.float32(0)
+        for _ in range(abs(int(j))):
+            t = np.nextafter(t, step)
+        targets.append(t)
+    targets = np.concatenate(targets)
+    targets = np.concatenate([targets, -targets])
+    x = np.zeros((n_rows, K), np.float32)
+    amax = np.exp(rng.uniform(np.log(1e-3), np.log(1e3), n_rows)).astype(np.float32)
+    # scales below 2^-120 (reciprocal inaccurate: division path), one of them
+    # an fp32 subnormal, and a scale of exactly 1/64
+    amax[:4] = [1e-35, 2e-34, 2.5e-38, 7.0]
+    for r in range(n_rows):
+        s = np.float32(amax[r] / np.float32(448.0))
+        q = rng.choice(targets, K - 1)
+        v = (q * s).astype(np.float32)                           # quotient fl32(v / s) ~ q
+        v = np.clip(v, -amax[r], amax[r])                        # the row max stays amax
+        x[r, 0] = amax[r] if r % 2 else -amax[r]
+        x[r, 1:] = v
+    return x
+
+
+def test_e4m3_encoder_rounding_window_random_scales():
+    x = _rounding_window_rows(160, 4096, 5)
+    q, s = mq.quant_fp8_per_token(torch.from_numpy(x).to(_dev()))
+    torch.cuda.synchronize()
+    rq, rs = L.quant_fp8_per_token(x)
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    assert (rs != 1.0).all()
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+    # the fused decode front end quantizes x with the same encoder
+    T, E, k = 8, 64, 6
+    logits = torch.randn(T, E, generator=torch.Generator().manual_seed(3))
+    xs = torch.from_numpy(x[:T].copy())
+    fused = mq.moe_route_quant_permute(logits.to(_dev()), xs.to(_dev()), k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(fused["x_q"].cpu().numpy(), rq[:T])
+    np.testing.assert_array_equal(fused["x_s"].cpu().numpy(), rs[:T])
+
+
 # ------------------------------------------------- E4M3FNUZ -> OCP requantization ----
 @pytest.mark.parametrize("rows,K", [(37, 4096), (50, 2048), (9, 24), (5, 8192), (3, 520),
                                     (4096, 4096)])
@@ -302,7 +353,12 @@ def _plan_and_experts(ids, E):
 @pytest.mark.parametrize("T,k,E,N,K,hot", [(40, 2, 8, 256, 256, None),     # R=80 -> 64-row tiles
                                            (4, 6, 16, 256, 512, None),     # R=24 -> decode path
                                            (100, 3, 5, 128, 384, 2),       # expert with >64 rows
-                                           (9, 1, 4, 384, 128, None)])
+                                           (9, 1, 4, 384, 128, None),
+                                           # the prefill tile kernels: K = 4096 (gate/up) and
+                                           # 2048 (down) with 256-row weight tiles, one expert
+                                           # holding 5 row tiles (the last one ragged)
+                                           (300, 2, 6, 512, 4096, 1),
+                                           (300, 2, 6, 256, 2048, 4)])
 def test_w4a8_integer_exact(T, k, E, N, K, hot):
     # unit scales and activations that decode to small integers: every output is
     # an exact integer (|.| < 2^24), so the GPU result must be bit-exact.
@@ -334,7 +390,10 @@ def test_w4a8_integer_exact(T, k, E, N, K, hot):
 @pytest.mark.parametrize("T,k,E,N,K,hot", [(40, 2, 8, 256, 256, None), (4, 6, 16, 256, 512, None),
                                            (100, 3, 5, 256, 384, 2), (50, 6, 64, 128, 256, None),
                                            (70, 2, 4, 384, 4096, 1), (100, 3, 6, 512, 2048, 2),
-                                           (4, 6, 24, 512, 4096, None)])
+                                           (4, 6, 24, 512, 4096, None),
+                                           # prefill tile kernels (R > 192): K = 4096 and 2048,
+                                           # N a multiple of 256, an expert with 5 row tiles
+                                           (300, 2, 6, 512, 4096, 1), (260, 3, 7, 256, 2048, 3)])
 def test_grouped_gemm_random(fmt, T, k, E, N, K, hot):
     rng = np.random.default_rng(E + N + K + T)
     ids = _case_ids(T, k, E, rng, hot)
