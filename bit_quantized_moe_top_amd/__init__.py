@@ -23,7 +23,7 @@ __all__ = [
     "moe_route_quant_permute", "pack_int4_g128", "moe_requant_fp8_fnuz",
     "moe_grouped_gemm_w4a8", "moe_grouped_gemm_w4a8_bf16s", "moe_grouped_gemm_nvfp4",
     "moe_grouped_gemm_aqlm",
-    "moe_expert_mlp_w4a8",
+    "moe_expert_mlp_w4a8", "moe_expert_mlp_w4a8_noalloc", "NOALLOC_SCRATCH_BYTES",
     "moe_expert_mlp_w4a8_bf16s", "moe_expert_mlp_fp8row", "pack_int4_g128_bf16s", "moe_grouped_gemm_fp8row", "moe_combine", "moe_shared_gemm_bf16",
     "plan_fields", "EXPORTED_SYMBOLS",
 ]
@@ -35,6 +35,7 @@ EPI_NONE, EPI_SILU_MUL = 0, 1
 TILE_M = 64
 MAX_EXPERTS, MAX_TOPK = 1024, 8
 PLAN_HEADER = 16
+NOALLOC_SCRATCH_BYTES = 32 << 20     # MOEQ_NOALLOC_SCRATCH_BYTES
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -69,6 +70,8 @@ _SIGNATURES = {
                                        _P, _P]),
     "moe_expert_mlp_fp8row": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P,
                                    _P, _P]),
+    "moe_expert_mlp_w4a8_noalloc": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _I, _I, _P,
+                                         _P]),
     "moe_combine": (_I, [_P, _P, _SZ, _I, _P, _P, _I, _I, _I, _P, _P]),
     "moe_shared_gemm_bf16": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
 }
@@ -512,6 +515,38 @@ def moe_expert_mlp_w4a8(xp_q: torch.Tensor, xp_s: torch.Tensor, plan: torch.Tens
         raise ValueError("w13 / w2 / scale shapes do not match")
     name = "moe_expert_mlp_w4a8_bf16s" if sdt == torch.bfloat16 else "moe_expert_mlp_w4a8"
     return _expert_mlp(name, xp_q, xp_s, plan, E, w13, w13_scales, w2, w2_scales, H, I, out)
+
+
+def moe_expert_mlp_w4a8_noalloc(xp_q: torch.Tensor, xp_s: torch.Tensor, plan: torch.Tensor,
+                                w13: torch.Tensor, w13_scales: torch.Tensor, w2: torch.Tensor,
+                                w2_scales: torch.Tensor,
+                                o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_expert_mlp_w4a8 (fp32 group scales) with h, h_q, h_s in the library's own
+    per-GPU scratch array: the C call allocates nothing.  Returns o [R, H] bf16 (a
+    new tensor unless `o` is given).  Calls overlapping on one GPU race on the array."""
+    w13, w2 = _weight_bytes(w13, "w13"), _weight_bytes(w2, "w2")
+    for t, name in ((w13, "w13"), (w2, "w2")):
+        _req(t, name, torch.uint8, 3)
+    for t, name in ((w13_scales, "w13_scales"), (w2_scales, "w2_scales")):
+        _req(t, name, torch.float32, 3)
+    _req(xp_q, "xp_q", torch.uint8, 2)
+    _req(xp_s, "xp_s", torch.float32, 1)
+    E, N13, H2 = w13.shape
+    H, I = 2 * H2, N13 // 2
+    if tuple(w2.shape) != (E, H, I // 2) or tuple(w13_scales.shape) != (E, N13, H // 128) or \
+            tuple(w2_scales.shape) != (E, H, I // 128):
+        raise ValueError("w13 / w2 / scale shapes do not match")
+    R = xp_q.shape[0]
+    _check_plan(plan, E, R)
+    if xp_q.shape[1] != H:
+        raise ValueError("xp_q has the wrong H")
+    if o is None:
+        o = torch.empty(R, H, dtype=torch.bfloat16, device=xp_q.device)
+    _req(o, "o", torch.bfloat16, 2)
+    _check("moe_expert_mlp_w4a8_noalloc", lib.moe_expert_mlp_w4a8_noalloc(
+        _ptr(xp_q), _ptr(xp_s), _ptr(plan), plan.numel() * 4, E, R, _ptr(w13), _ptr(w13_scales),
+        _ptr(w2), _ptr(w2_scales), H, I, _ptr(o), _stream(xp_q.device)))
+    return o
 
 
 def moe_expert_mlp_w4a8_bf16s(xp_q, xp_s, plan, w13, w13_scales, w2, w2_scales, out=None) -> dict:

@@ -51,6 +51,7 @@ const char* moe_status_string(int status) {
     case MOEQ_ERR_WORKSPACE: return "plan buffer too small";
     case MOEQ_ERR_DEVICE: return "no gfx950 device";
     case MOEQ_ERR_LAUNCH: return "kernel launch failed";
+    case MOEQ_ERR_SCRATCH: return "sizes exceed the library's scratch array";
     default: return "unknown status";
   }
 }
@@ -343,6 +344,21 @@ int moe_expert_mlp_fp8row(const uint8_t* xp_q, const float* xp_s, const void* pl
                           uint8_t* h_q, float* h_s, uint16_t* o, void* stream) {
   return mlp_common(moeq::kFp8Row, xp_q, xp_s, plan, plan_bytes, E, R, w13, w13_scales, w2,
                     w2_scales, H, I, h, h_q, h_s, o, stream);
+}
+
+int moe_expert_mlp_w4a8_noalloc(const uint8_t* xp_q, const float* xp_s, const void* plan,
+                                size_t plan_bytes, int E, int R, const uint8_t* w13,
+                                const float* w13_scales, const uint8_t* w2,
+                                const float* w2_scales, int H, int I, uint16_t* o, void* stream) {
+  if (int rc = mlp_checks(xp_q, xp_s, plan, plan_bytes, E, R, w13, w13_scales, w2, w2_scales, H,
+                          I, false, nullptr, nullptr, nullptr, o))
+    return rc;
+  if (R == 0) return MOEQ_OK;
+  if (moeq::noalloc_mlp_bytes(R, I) > MOEQ_NOALLOC_SCRATCH_BYTES) return MOEQ_ERR_SCRATCH;
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_expert_mlp_noalloc(moeq::kW4G128, xp_q, xp_s, plan, E, R, w13,
+                                                       w13_scales, w2, w2_scales, H, I, o,
+                                                       as_stream(stream)));
 }
 
 int moe_combine(const uint16_t* o, const void* plan, size_t plan_bytes, int E,

@@ -130,6 +130,14 @@ hipError_t launch_expert_mlp(int wfmt, const uint8_t* xp_q, const float* xp_s, c
                              const void* s2, int H, int I, uint16_t* h, uint8_t* h_q, float* h_s,
                              uint16_t* o, hipStream_t stream);
 
+// bytes of the scratch array the allocation-free expert MLP needs for R rows of
+// width I (h, h_q, h_s, each 256-byte aligned), and that MLP itself
+size_t noalloc_mlp_bytes(int R, int I);
+hipError_t launch_expert_mlp_noalloc(int wfmt, const uint8_t* xp_q, const float* xp_s,
+                                     const void* plan, int E, int R, const uint8_t* w13,
+                                     const void* s13, const uint8_t* w2, const void* s2, int H,
+                                     int I, uint16_t* o, hipStream_t stream);
+
 hipError_t launch_shared_gemm_bf16(const uint16_t* a, const uint16_t* w, int M, int N, int K,
                                    int epilogue, uint16_t* out, hipStream_t stream);
 

@@ -53,6 +53,7 @@ extern "C" {
 #define MOEQ_ERR_WORKSPACE    3  /* plan buffer smaller than moe_plan_size(E, R) */
 #define MOEQ_ERR_DEVICE       4  /* no device, or the current device is not gfx950 */
 #define MOEQ_ERR_LAUNCH       5  /* a kernel launch failed (hipGetLastError) */
+#define MOEQ_ERR_SCRATCH      6  /* sizes beyond the library's scratch array (no-allocation call) */
 
 /* element types */
 #define MOEQ_F32   0
@@ -411,6 +412,28 @@ int moe_expert_mlp_w4a8_bf16s(const uint8_t* xp_q, const float* xp_s, const void
                               const uint16_t* w13_scales, const uint8_t* w2,
                               const uint16_t* w2_scales, int H, int I, uint16_t* h, uint8_t* h_q,
                               float* h_s, uint16_t* o, void* stream);
+
+/*
+ * moe_expert_mlp_w4a8_noalloc -- moe_expert_mlp_w4a8 for callers that cannot
+ * allocate device memory (code under graph capture, serving loops, harnesses
+ * that forbid allocation): the caller passes only the inputs and o; the
+ * intermediates h, h_q and h_s live in a device array inside the library of
+ * MOEQ_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on that GPU
+ * until the process ends.  o equals moe_expert_mlp_w4a8's o bit for bit.
+ *
+ * Size limit: 256-byte-aligned h (R*I*2), h_q (R*I) and h_s (R*4) together
+ * within MOEQ_NOALLOC_SCRATCH_BYTES (R <= 5457 at I = 2048), else
+ * MOEQ_ERR_SCRATCH.  Every call on one GPU uses the same array: calls that
+ * overlap on a GPU (other streams, other host threads) race and must be
+ * serialized by the caller; calls on one stream are ordered.  The call
+ * allocates nothing, on the host or the device.
+ * Arguments, other limits and errors: as moe_expert_mlp_w4a8.
+ */
+#define MOEQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int moe_expert_mlp_w4a8_noalloc(const uint8_t* xp_q, const float* xp_s, const void* plan,
+                                size_t plan_bytes, int E, int R, const uint8_t* w13,
+                                const float* w13_scales, const uint8_t* w2,
+                                const float* w2_scales, int H, int I, uint16_t* o, void* stream);
 
 /*
  * moe_expert_mlp_fp8row -- moe_expert_mlp_w4a8 with row-scaled FP8 expert
