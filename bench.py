@@ -9,7 +9,12 @@ fused expert-MLP launch).  The headline workload is the Inkling-Small
 sparse layer at decode, T = 4 tokens (256 experts of width 2048, hidden 4096,
 top-6, INT4 g128 weights, per-token FP8 activations); its metric is the weight
 stream: bytes of the distinct experts' packed weights and scales / step time.
-The same run also times the T = 2048 prefill layer and reports its FP8 TFLOP/s.
+The same run also times the T = 2048 prefill layer (FP8 TFLOP/s and the
+fraction of its attainable roofline), the skewed prefill layer with two bf16
+shared experts, the row-FP8 layer (384 experts), a supplementary token sweep of
+the prefill layer (T = 4096 .. 16384), decode with bf16 group scales and the
+NVFP4 + AQLM hybrid decode layer, plus measured copy / read ceilings and the
+shader clock before and after.
 
 Weights rotate over several independently generated weight sets so that no
 step finds its experts in the 256 MB last-level cache.  Prints one JSON line.
@@ -30,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer FP8 TFLOP/s at T=2048 prefill; weight-stream GB/s at T=4 decode"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 
 def parse():
@@ -38,10 +44,11 @@ def parse():
     # 200 decode steps take ~16 ms: enough that the host-to-device latency of
     # the first launch (paid once per timed region) is a small share of a step
     ap.add_argument("--steps", type=int, default=200)
-    # the first ~200 decode steps after the weight sets are built run ~5% slower
-    # than the steady state (first touches of the weight pages), so the default
-    # warm-up covers them; the timed steps are the same with any warm-up
-    ap.add_argument("--warmup", type=int, default=200)
+    # every weight set is read once right after it is built (the first reads of
+    # fresh pages are slow); the timed region itself carries a fixed ~50 us (the
+    # first launch's host latency and the final synchronize), i.e. ~2.5 us per
+    # step at 20 steps and ~0.25 us at 200
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="weight sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -54,6 +61,10 @@ def parse():
                          "size, to scale the memory-traffic counters), then exit")
     ap.add_argument("--no-graph", action="store_true",
                     help="time only eager launches (default: also replay captured graphs)")
+    ap.add_argument("--no-skewed", action="store_true", help="skip the skewed prefill layer")
+    ap.add_argument("--no-fp8row", action="store_true", help="skip the row-FP8 prefill layer")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the supplementary prefill token sweep (T = 4096 .. 16384)")
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed", "fp8row"])
     return ap.parse_args()
 
@@ -103,18 +114,31 @@ def build_sets(cfg, n_sets, dev):
             layer.set_shared(*W.make_shared_weights(c, dev))
         inp = W.make_layer_inputs(c, device=dev, weights=False)
         layers.append((layer, inp))
+        touch(layer.w13, layer.s13, layer.w2, layer.s2, layer.ws13, layer.ws2)
         torch.cuda.synchronize()
         log(f"{cfg.name}: weight set {s + 1}/{n_sets} ready")
     return layers
 
 
-def time_layer(cfg, n_sets, steps, warmup, dev, graph=False, split_events=False):
+def touch(*tensors):
+    """Reads every byte of the given tensors once (untimed): the first reads of
+    freshly written weight pages are slower than later ones."""
+    import torch
+    for t in tensors:
+        if t is not None:
+            torch.sum(t.view(torch.uint8), dtype=torch.int64)
+
+
+def time_layer(cfg, n_sets, steps, warmup, dev, graph=False, split_events=False, layers=None):
     """Times `steps` layer passes; returns timings and the per-call launch times
-    (with split_events the expert MLP's three calls are timed one by one)."""
+    (with split_events the expert MLP's three calls are timed one by one).
+    layers: already built (layer, inputs) pairs to time instead of new weight sets."""
     import torch
 
     import bit_quantized_moe_top_amd as mq
-    layers = build_sets(cfg, n_sets, dev)
+    if layers is None:
+        layers = build_sets(cfg, n_sets, dev)
+    n_sets = len(layers)
     # distinct experts touched per set (bytes the step must stream)
     distinct = []
     for layer, inp in layers:
@@ -223,6 +247,9 @@ def time_hybrid(cfg, n_sets, steps, warmup, dev):
                                  W.make_aqlm_slabs(c, len(cold), dev))
         inp = W.make_layer_inputs(c, device=dev, weights=False)
         layers.append((layer, inp, set(hot.tolist())))
+        for part in (layer.hot, layer.cold):
+            for v in part.values():
+                touch(*(v if isinstance(v, list) else [v]))
         torch.cuda.synchronize()
         log(f"{cfg.name}: weight set {s + 1}/{n_sets} ready")
     # bytes per expert: hot = E2M1 codes + E4M3 block scales (+ scale2); cold = the
@@ -337,6 +364,94 @@ def cpu_baseline(cfg, layers, target_s=10.0):
             "seconds_per_layer": sec}
 
 
+def prefill_summary(pcfg, pres, short=False):
+    """FP8 TFLOP/s of a T-token layer and its fractions of the FP8 peak and of
+    the attainable roofline min(peak FLOP/s, HBM bandwidth x arithmetic intensity)."""
+    pms = pres["ms_per_step"]
+    t = pms * 1e-3
+    fp8_flops = 2.0 * pcfg.R * 3 * pcfg.H * pcfg.I
+    pw13, pw2 = expert_bytes(pcfg)
+    wbytes = pres["distinct_mean"] * (pw13 + pw2)
+    S = pcfg.n_shared * pcfg.I
+    bf16_flops = 2.0 * pcfg.T * 3 * pcfg.H * S
+    shared_bytes = 3 * pcfg.H * S * 2
+    io_bytes = pcfg.T * pcfg.H * 2 * 2 + pcfg.T * pcfg.E * 4       # x in, y out, logits
+    total_bytes = wbytes + shared_bytes + io_bytes
+    t_roof = max(total_bytes / (HBM_PEAK_GBS * 1e9),
+                 fp8_flops / (FP8_PEAK_TFLOPS * 1e12) + bf16_flops / (BF16_PEAK_TFLOPS * 1e12))
+    fmt = {"w4a8": "INT4 g128", "w4a8_bf16s": "INT4 g128 (bf16 scales)", "fp8row": "row FP8"}
+    d = {"workload": f"{pcfg.name}: T={pcfg.T}, hidden {pcfg.H}, {pcfg.E} experts of width "
+                     f"{pcfg.I}, top-{pcfg.k}, {fmt.get(pcfg.weight_format, pcfg.weight_format)}"
+                     + (f", {pcfg.n_shared} bf16 shared experts" if pcfg.n_shared else ""),
+         "T": pcfg.T,
+         "value": round(fp8_flops / t / 1e12, 2), "unit": "TFLOP/s",
+         "ms_per_step": round(pms, 4),
+         "frac_fp8_peak": round(fp8_flops / t / 1e12 / FP8_PEAK_TFLOPS, 4),
+         "roofline_us": round(t_roof * 1e6, 1),
+         "frac_attainable_roofline": round(t_roof / t, 4),
+         "bytes_per_step": round(total_bytes),
+         "hbm_GBps": round(total_bytes / t / 1e9, 1),
+         "gate_up_gemm_us": round(pres["gate_up_back_to_back_us"], 2),
+         "gate_up_gemm_GBps": round(pres["distinct_mean"] * pw13 /
+                                    (pres["gate_up_back_to_back_us"] * 1e-6) / 1e9, 1),
+         "per_call_us": {k: round(v, 2) for k, v in pres["per_call_us"].items()}}
+    pc = pres["per_call_us"]
+    if "gemm_down" in pc:
+        d["down_gemm_GBps"] = round(pres["distinct_mean"] * pw2 / (pc["gemm_down"] * 1e-6) / 1e9, 1)
+    if pcfg.n_shared:
+        sh_us = pc.get("shared_gate_up", 0.0) + pc.get("shared_down", 0.0)
+        d["shared_bf16"] = {"flops": bf16_flops, "us": round(sh_us, 2),
+                            "TFLOPs": round(bf16_flops / (sh_us * 1e-6) / 1e12, 1) if sh_us else None,
+                            "frac_bf16_peak": round(bf16_flops / (sh_us * 1e-6) / 1e12 /
+                                                    BF16_PEAK_TFLOPS, 4) if sh_us else None}
+    if short:
+        for k in ("workload", "per_call_us", "bytes_per_step"):
+            d.pop(k)
+    return d
+
+
+def copy_ceiling(dev, nbytes=2 << 30, reps=5):
+    """Measured streaming ceilings on this machine with torch's own kernels: a
+    device-to-device copy of nbytes (bytes read + written per second) and a
+    reduction over 2 * nbytes (bytes read per second)."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    big = torch.ones(2 * nbytes // 4, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        fn()
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        for _ in range(reps):
+            fn()
+        e_ev.record()
+        torch.cuda.synchronize()
+        return s_ev.elapsed_time(e_ev) * 1e-3 / reps
+    copy_s = timed(lambda: dst.copy_(src))
+    read_s = timed(lambda: torch.sum(big))
+    del src, dst, big
+    torch.cuda.empty_cache()
+    return {"GBps": round(2 * nbytes / copy_s / 1e9, 1), "bytes": nbytes,
+            "kind": "device copy (read + write), torch copy kernel",
+            "read_GBps": round(2 * nbytes / read_s / 1e9, 1),
+            "read_kind": f"torch.sum over {2 * nbytes >> 30} GiB of fp32 (bytes read)"}
+
+
+def sclk_mhz():
+    """Current shader clock (MHz) of the GPU(s) from the driver's DPM table, if readable."""
+    import glob
+    vals = []
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(path):
+                if line.strip().endswith("*"):
+                    vals.append(int(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0]))
+        except (OSError, ValueError, IndexError):
+            pass
+    return vals or None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -358,6 +473,7 @@ def main():
         return
     cfg = W.get_config(args.workload)
     log(f"device {torch.cuda.get_device_name(0)}; workload {cfg}")
+    sclk_before = sclk_mhz()
     res = time_layer(cfg, args.sets, args.steps, args.warmup, dev, graph=not args.no_graph,
                      split_events=cfg.R > 64)
     w13b, w2b = expert_bytes(cfg)
@@ -417,25 +533,35 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_prefill and cfg.name == "decode":
         pcfg = W.get_config("prefill")
-        pres = time_layer(pcfg, 2, max(5, args.steps // 2), 2, dev, split_events=True)
-        pms = pres["ms_per_step"]
-        pflops = 2.0 * pcfg.R * 3 * pcfg.H * pcfg.I
-        ptf = pflops / (pms * 1e-3) / 1e12
-        pw13, pw2 = expert_bytes(pcfg)
-        pbytes = pres["distinct_mean"] * (pw13 + pw2)
-        t_roof = max(pbytes / (HBM_PEAK_GBS * 1e9), pflops / (FP8_PEAK_TFLOPS * 1e12))
-        out["prefill"] = {
-            "workload": f"prefill: T={pcfg.T}, hidden {pcfg.H}, {pcfg.E} experts of width {pcfg.I}, "
-                        f"top-{pcfg.k}, INT4 g128",
-            "value": round(ptf, 2), "unit": "TFLOP/s", "ms_per_step": round(pms, 4),
-            "frac_fp8_peak": round(ptf / FP8_PEAK_TFLOPS, 4),
-            "frac_attainable_roofline": round(t_roof / (pms * 1e-3), 4),
-            "weight_GBps": round(pbytes / (pms * 1e-3) / 1e9, 1),
-            "gate_up_gemm_us": round(pres["gate_up_back_to_back_us"], 2),
-            "gate_up_gemm_GBps": round(pres["distinct_mean"] * pw13 /
-                                       (pres["gate_up_back_to_back_us"] * 1e-6) / 1e9, 1),
-            "per_call_us": {k: round(v, 2) for k, v in pres["per_call_us"].items()},
-        }
+        psteps = max(5, args.steps // 2)
+        pres = time_layer(pcfg, 2, psteps, 2, dev, split_events=True)
+        out["prefill"] = prefill_summary(pcfg, pres)
+        if not args.no_sweep:
+            # supplementary: the same layer (weight set 0) at larger token counts,
+            # where the grouped GEMMs have enough rows per expert to become
+            # MFMA-bound; not one of the named workloads
+            layer = pres["layers"][0][0]
+            sweep = []
+            for T in (4096, 8192, 16384):
+                scfg = W.get_config("prefill", T=T)
+                sres = time_layer(scfg, 1, 5, 2, dev, split_events=True,
+                                  layers=[(layer, W.make_layer_inputs(scfg, dev, weights=False))])
+                sres.pop("layers")
+                sweep.append(prefill_summary(scfg, sres, short=True))
+                layer._bufs.clear()
+                torch.cuda.empty_cache()
+            out["t_sweep"] = {"note": "supplementary prefill token sweep of the prefill layer "
+                                      "(not one of the named workloads)", "points": sweep}
+        pres.pop("layers")
+        torch.cuda.empty_cache()
+    for name, skip in (("skewed", args.no_skewed), ("fp8row", args.no_fp8row)):
+        if skip or cfg.name != "decode" or args.no_prefill:
+            continue
+        scfg = W.get_config(name)
+        sres = time_layer(scfg, 2, max(5, args.steps // 2), 2, dev, split_events=True)
+        sres.pop("layers")
+        out[name] = prefill_summary(scfg, sres)
+        torch.cuda.empty_cache()
     if not args.no_bf16_scales and cfg.name == "decode":
         import dataclasses
         bcfg = dataclasses.replace(cfg, weight_format="w4a8_bf16s")
@@ -470,6 +596,10 @@ def main():
             "per_call_us": {k: round(v, 2) for k, v in hres["per_call_us"].items()},
         }
         torch.cuda.empty_cache()
+    out["copy_ceiling"] = copy_ceiling(dev)
+    out["layer_frac_of_read_ceiling"] = round(gbs / out["copy_ceiling"]["read_GBps"], 4) \
+        if cfg.name == "decode" else None
+    out["sclk_mhz"] = {"before": sclk_before, "after": sclk_mhz()}
     out["host"] = platform.node()
     print(json.dumps(out), flush=True)
 
