@@ -66,7 +66,46 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the supplementary prefill token sweep (T = 4096 .. 16384)")
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed", "fp8row"])
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="only summarise the rocprofv3 CSV output under DIR (kernel stats, or the "
+                         "mean per dispatch of every collected counter per kernel) and exit")
     return ap.parse_args()
+
+
+def summarize(root: str) -> str:
+    """Markdown summary of rocprofv3 CSV output under root: the kernel stats table of
+    a --kernel-trace --stats run, or for --pmc runs the mean per dispatch of each
+    counter per kernel (libmoeq kernels and the device copy)."""
+    import csv
+    import glob
+    import re
+
+    def short(name):
+        name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+        name = re.sub(r"\((?!anon).*$", "", name)
+        return name.replace("moeq::", "")
+    lines = []
+    for f in sorted(glob.glob(os.path.join(root, "**", "*kernel_stats.csv"), recursive=True)):
+        lines += [f"kernel stats ({os.path.relpath(f, root)})", "",
+                  "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+        for r in csv.DictReader(open(f)):
+            lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+        lines.append("")
+    per = {}
+    for f in sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            k = short(r.get("Kernel_Name", ""))
+            if not (k.split("<")[0].endswith("kernel") or "copyBuffer" in k):
+                continue
+            per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if per:
+        lines += ["| kernel | counter | dispatches | mean per dispatch |", "|---|---|---:|---:|"]
+        for k in sorted(per):
+            for c in sorted(per[k]):
+                v = per[k][c]
+                lines.append(f"| `{k}` | {c} | {len(v)} | {sum(v) / len(v):.1f} |")
+    return "\n".join(lines)
 
 
 def log(msg):
@@ -97,14 +136,17 @@ def build_sets(cfg, n_sets, dev):
         c = dataclasses.replace(cfg, seed=cfg.seed + 1000 * s)
         layer = mq.MoELayer(c.H, c.I, c.E, c.k, c.weight_format, device=dev)
         fp8 = c.weight_format == "fp8row"
-        kd13, kd2 = (c.H, c.I) if fp8 else (c.H // 2, c.I // 2)
-        w13 = torch.empty(c.E, 2 * c.I, kd13, dtype=torch.uint8, device=dev)
-        w2 = torch.empty(c.E, c.H, kd2, dtype=torch.uint8, device=dev)
+        # E4M3 rows, or INT4 in the GEMMs' tiled order [E, N/16, K/128, 16, 64]
+        w13 = torch.empty((c.E, 2 * c.I, c.H) if fp8 else (c.E, 2 * c.I // 16, c.H // 128, 16, 64),
+                          dtype=torch.uint8, device=dev)
+        w2 = torch.empty((c.E, c.H, c.I) if fp8 else (c.E, c.H // 16, c.I // 128, 16, 64),
+                         dtype=torch.uint8, device=dev)
         sdt = torch.bfloat16 if c.weight_format == "w4a8_bf16s" else torch.float32
         s13 = torch.empty((c.E, 2 * c.I) if fp8 else (c.E, 2 * c.I, c.H // 128), dtype=sdt,
                           device=dev)
         s2 = torch.empty((c.E, c.H) if fp8 else (c.E, c.H, c.I // 128), dtype=sdt, device=dev)
-        quant = mq.quant_fp8_per_token if fp8 else mq.pack_int4_g128
+        quant = mq.quant_fp8_per_token if fp8 else \
+            (lambda wf, wq, ws: mq.pack_int4_g128(wf, wq, ws, tiled=True))
         for which, wq, ws in (("w13", w13, s13), ("w2", w2, s2)):
             for e0, wf in W.iter_expert_weights(c, which, dev, chunk=32):
                 quant(wf, wq[e0:e0 + wf.shape[0]], ws[e0:e0 + wf.shape[0]])
@@ -454,6 +496,9 @@ def sclk_mhz():
 
 def main():
     args = parse()
+    if args.summarize:
+        print(summarize(args.summarize))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the layer would shard by experts or by width across GPUs; this library "

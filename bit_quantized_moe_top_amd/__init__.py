@@ -20,7 +20,7 @@ __all__ = [
     "LIB_PATH", "lib", "MOEQ_F32", "MOEQ_BF16", "EPI_NONE", "EPI_SILU_MUL", "TILE_M",
     "MAX_EXPERTS", "MAX_TOPK", "MoeqError", "moe_abi_version", "moe_status_string",
     "moe_plan_size", "moe_router_logits", "moe_route_topk", "quant_fp8_per_token", "moe_permute",
-    "moe_route_quant_permute", "pack_int4_g128", "moe_requant_fp8_fnuz",
+    "moe_route_quant_permute", "pack_int4_g128", "tile_int4_weights", "moe_requant_fp8_fnuz",
     "moe_grouped_gemm_w4a8", "moe_grouped_gemm_w4a8_bf16s", "moe_grouped_gemm_nvfp4",
     "moe_grouped_gemm_aqlm",
     "moe_expert_mlp_w4a8", "moe_expert_mlp_w4a8_noalloc", "NOALLOC_SCRATCH_BYTES",
@@ -55,6 +55,7 @@ _SIGNATURES = {
                                      _P, _SZ, _P]),
     "pack_int4_g128": (_I, [_P, _I64, _I, _P, _P, _P]),
     "pack_int4_g128_bf16s": (_I, [_P, _I64, _I, _P, _P, _P]),
+    "moe_tile_int4_weights": (_I, [_P, _I64, _I, _P, _P]),
     "moe_requant_fp8_fnuz": (_I, [_P, _P, _I64, _I, _P, _P, _P]),
     "moe_grouped_gemm_w4a8": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_grouped_gemm_fp8row": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
@@ -132,6 +133,19 @@ def _weight_bytes(t: torch.Tensor, name: str) -> torch.Tensor:
         return t.view(torch.uint8)
     _req(t, name, torch.uint8)
     return t
+
+
+def _tiled_int4(t: torch.Tensor, name: str) -> Tuple[int, int, int]:
+    """(E, N, K) of INT4 weights in the GEMMs' tiled order, uint8
+    [E, N/16, K/128, 16, 64] as tile_int4_weights returns them."""
+    if isinstance(t, torch.Tensor) and t.dim() != 5:
+        raise ValueError(f"{name} must be INT4 weights in the tiled order [E, N/16, K/128, 16, 64] "
+                         f"(pass the packed rows through tile_int4_weights first), got {tuple(t.shape)}")
+    _req(t, name, torch.uint8, 5)
+    E, nb, G, r, c = t.shape
+    if (r, c) != (16, 64):
+        raise ValueError(f"{name}: the last two dims of the tiled order are (16, 64)")
+    return E, 16 * nb, 128 * G
 
 
 def _mark_plan(plan: torch.Tensor, E: int, R: int) -> None:
@@ -290,16 +304,41 @@ def moe_route_quant_permute(logits: torch.Tensor, x: torch.Tensor, k: int,
     return o
 
 
+def tile_int4_weights(w_packed: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed INT4 rows uint8 [..., N, K/2] (or the checkpoint's int32 [..., N, K/8]
+    words) -> the GEMMs' tiled order uint8 [..., N/16, K/128, 16, 64]
+    (moe_tile_int4_weights; a permutation of whole bytes)."""
+    w_packed = _weight_bytes(w_packed, "w_packed")
+    if w_packed.dim() < 2:
+        raise ValueError("w_packed must be [..., N, K/2]")
+    N, K = w_packed.shape[-2], 2 * w_packed.shape[-1]
+    shape = tuple(w_packed.shape[:-2]) + (N // 16, K // 128, 16, 64)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.uint8, device=w_packed.device)
+    _req(out, "out", torch.uint8)
+    if N % 16 or K % 128 or tuple(out.shape) != shape:
+        raise ValueError(f"tiled INT4 weights need N % 16 == 0, K % 128 == 0 and out {shape}")
+    rows = w_packed.numel() // (K // 2) if K else 0
+    _check("moe_tile_int4_weights", lib.moe_tile_int4_weights(
+        _ptr(w_packed), rows, K, _ptr(out), _stream(w_packed.device)))
+    return out
+
+
 def pack_int4_g128(w: torch.Tensor, packed: Optional[torch.Tensor] = None,
                    scales: Optional[torch.Tensor] = None,
-                   scale_dtype=torch.float32) -> Tuple[torch.Tensor, torch.Tensor]:
+                   scale_dtype=torch.float32, tiled: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """w [..., K] fp32 -> packed uint8 [..., K/2], scales [..., K/128] of scale_dtype
-    (fp32: pack_int4_g128; bfloat16: pack_int4_g128_bf16s)."""
+    (fp32: pack_int4_g128; bfloat16: pack_int4_g128_bf16s).
+    tiled=True: the packed rows go through tile_int4_weights (into `packed`, then
+    [..., N/16, K/128, 16, 64]), the order the GEMMs read."""
     _req(w, "w", torch.float32)
     if scales is not None:
         scale_dtype = scales.dtype
     if scale_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("scale_dtype must be float32 or bfloat16")
+    if tiled:
+        rows_packed, scales = pack_int4_g128(w, None, scales, scale_dtype)
+        return tile_int4_weights(rows_packed, packed), scales
     K = w.shape[-1]
     rows = w.numel() // K if K else 0
     if packed is None:
@@ -360,17 +399,17 @@ def moe_grouped_gemm_w4a8(a_q: torch.Tensor, a_s: torch.Tensor, plan: torch.Tens
                           w_packed: torch.Tensor, w_scales: torch.Tensor,
                           epilogue: int = EPI_NONE, out_dtype=torch.bfloat16,
                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """w_packed [E, N, K/2] uint8 (or the checkpoint's int32 [E, N, K/8] words),
-    w_scales [E, N, K/128] fp32 (or bfloat16: then moe_grouped_gemm_w4a8_bf16s)."""
-    w_packed = _weight_bytes(w_packed, "w_packed")
-    _req(w_packed, "w_packed", torch.uint8, 3)
+    """w_packed: INT4 weights in the tiled order, uint8 [E, N/16, K/128, 16, 64]
+    (tile_int4_weights of the packed [E, N, K/2] rows or of the checkpoint's int32
+    [E, N, K/8] words), w_scales [E, N, K/128] fp32 (or bfloat16: then
+    moe_grouped_gemm_w4a8_bf16s)."""
+    E, N, K = _tiled_int4(w_packed, "w_packed")
     bf16 = w_scales.dtype == torch.bfloat16
     _req(w_scales, "w_scales", torch.bfloat16 if bf16 else torch.float32, 3)
-    E, N, K2 = w_packed.shape
-    if tuple(w_scales.shape) != (E, N, 2 * K2 // 128):
+    if tuple(w_scales.shape) != (E, N, K // 128):
         raise ValueError("w_scales shape does not match w_packed")
     name = "moe_grouped_gemm_w4a8_bf16s" if bf16 else "moe_grouped_gemm_w4a8"
-    return _gemm(name, a_q, a_s, plan, E, w_packed, w_scales, N, 2 * K2, epilogue, out_dtype, out)
+    return _gemm(name, a_q, a_s, plan, E, w_packed, w_scales, N, K, epilogue, out_dtype, out)
 
 
 def moe_grouped_gemm_w4a8_bf16s(a_q, a_s, plan, w_packed, w_scales, epilogue: int = EPI_NONE,
@@ -493,26 +532,30 @@ def _expert_mlp(fn_name: str, xp_q, xp_s, plan, E, w13, s13, w2, s2, H, I, out):
     return o
 
 
+def _w4_mlp_shapes(w13, w13_scales, w2, w2_scales, scale_dtype=None) -> Tuple[int, int, int]:
+    """(E, H, I) of tiled INT4 w13 [2I x H] and w2 [H x I] with their group scales."""
+    E, N13, H = _tiled_int4(w13, "w13")
+    E2, H2, I = _tiled_int4(w2, "w2")
+    sdt = scale_dtype or (torch.bfloat16 if w13_scales.dtype == torch.bfloat16 else torch.float32)
+    for t, name in ((w13_scales, "w13_scales"), (w2_scales, "w2_scales")):
+        _req(t, name, sdt, 3)
+    if (E2, H2, N13) != (E, H, 2 * I) or tuple(w13_scales.shape) != (E, N13, H // 128) or \
+            tuple(w2_scales.shape) != (E, H, I // 128):
+        raise ValueError("w13 / w2 / scale shapes do not match")
+    return E, H, I
+
+
 def moe_expert_mlp_w4a8(xp_q: torch.Tensor, xp_s: torch.Tensor, plan: torch.Tensor,
                         w13: torch.Tensor, w13_scales: torch.Tensor, w2: torch.Tensor,
                         w2_scales: torch.Tensor, out: Optional[dict] = None) -> dict:
     """gate/up GEMM + SiLU, FP8 quantization of h, down GEMM (two launches for R <= 192
     and I <= 2048, else three).
-    w13 [E, 2I, H/2], w13_scales [E, 2I, H/128], w2 [E, H, I/2], w2_scales [E, H, I/128].
-    Scales fp32, or both bfloat16 (then moe_expert_mlp_w4a8_bf16s).  w13 / w2 may also be
-    the checkpoint's int32 [.., K/8] words.
+    w13 (2I x H) and w2 (H x I) INT4 weights in the tiled order (tile_int4_weights),
+    w13_scales [E, 2I, H/128], w2_scales [E, H, I/128]; scales fp32, or both
+    bfloat16 (then moe_expert_mlp_w4a8_bf16s).
     Returns a dict with h, h_q, h_s, o (reusing `out`'s tensors)."""
-    w13, w2 = _weight_bytes(w13, "w13"), _weight_bytes(w2, "w2")
-    for t, name in ((w13, "w13"), (w2, "w2")):
-        _req(t, name, torch.uint8, 3)
-    sdt = torch.bfloat16 if w13_scales.dtype == torch.bfloat16 else torch.float32
-    for t, name in ((w13_scales, "w13_scales"), (w2_scales, "w2_scales")):
-        _req(t, name, sdt, 3)
-    E, N13, H2 = w13.shape
-    H, I = 2 * H2, N13 // 2
-    if tuple(w2.shape) != (E, H, I // 2) or tuple(w13_scales.shape) != (E, N13, H // 128) or \
-            tuple(w2_scales.shape) != (E, H, I // 128):
-        raise ValueError("w13 / w2 / scale shapes do not match")
+    E, H, I = _w4_mlp_shapes(w13, w13_scales, w2, w2_scales)
+    sdt = w13_scales.dtype
     name = "moe_expert_mlp_w4a8_bf16s" if sdt == torch.bfloat16 else "moe_expert_mlp_w4a8"
     return _expert_mlp(name, xp_q, xp_s, plan, E, w13, w13_scales, w2, w2_scales, H, I, out)
 
@@ -524,18 +567,9 @@ def moe_expert_mlp_w4a8_noalloc(xp_q: torch.Tensor, xp_s: torch.Tensor, plan: to
     """moe_expert_mlp_w4a8 (fp32 group scales) with h, h_q, h_s in the library's own
     per-GPU scratch array: the C call allocates nothing.  Returns o [R, H] bf16 (a
     new tensor unless `o` is given).  Calls overlapping on one GPU race on the array."""
-    w13, w2 = _weight_bytes(w13, "w13"), _weight_bytes(w2, "w2")
-    for t, name in ((w13, "w13"), (w2, "w2")):
-        _req(t, name, torch.uint8, 3)
-    for t, name in ((w13_scales, "w13_scales"), (w2_scales, "w2_scales")):
-        _req(t, name, torch.float32, 3)
+    E, H, I = _w4_mlp_shapes(w13, w13_scales, w2, w2_scales, torch.float32)
     _req(xp_q, "xp_q", torch.uint8, 2)
     _req(xp_s, "xp_s", torch.float32, 1)
-    E, N13, H2 = w13.shape
-    H, I = 2 * H2, N13 // 2
-    if tuple(w2.shape) != (E, H, I // 2) or tuple(w13_scales.shape) != (E, N13, H // 128) or \
-            tuple(w2_scales.shape) != (E, H, I // 128):
-        raise ValueError("w13 / w2 / scale shapes do not match")
     R = xp_q.shape[0]
     _check_plan(plan, E, R)
     if xp_q.shape[1] != H:

@@ -177,6 +177,21 @@ int pack_int4_g128_bf16s(const float* w, int64_t rows, int K, uint8_t* packed, u
   return pack_common(w, rows, K, packed, scales, 1, stream);
 }
 
+int moe_tile_int4_weights(const uint8_t* w_packed, int64_t rows, int K, uint8_t* w_tiled,
+                          void* stream) {
+  if (rows < 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;
+  if (K % 128 != 0 || rows % 16 != 0) return MOEQ_ERR_UNSUPPORTED;
+  if (rows == 0) return MOEQ_OK;
+  if (!w_packed || !w_tiled || !aligned16(w_packed) || !aligned16(w_tiled))
+    return MOEQ_ERR_INVALID_ARG;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w_packed);
+  const uintptr_t b = reinterpret_cast<uintptr_t>(w_tiled);
+  const uintptr_t n = uintptr_t(rows) * uintptr_t(K / 2);
+  if (a < b + n && b < a + n) return MOEQ_ERR_INVALID_ARG;      // the ranges overlap
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_tile_int4(w_packed, rows, K, w_tiled, as_stream(stream)));
+}
+
 static int gemm_common(int wfmt, const uint8_t* a_q, const float* a_s, const void* plan,
                        size_t plan_bytes, int E, int R, const uint8_t* w, const void* w_scale, int N,
                        int K, int epilogue, void* out, int out_dtype, void* stream) {

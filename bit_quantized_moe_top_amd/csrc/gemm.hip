@@ -34,7 +34,7 @@ gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
   constexpr int kStageRows = 4, kStageK = 1024, kStageStride = kStageK + 16;
   __shared__ __align__(16) uint8_t a_stage[4][kStageRows][kStageStride];
   __shared__ v4f red[3 * NB * kWave];           // quarter sums of waves 1..3
-  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15, kb = lane >> 4;
   const int units_per_tile = N / (16 * NB);
   const int tile = blockIdx.x / units_per_tile;
@@ -49,12 +49,13 @@ gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
 
   int col[NB];
   unit_columns<EPI, NB>(N, u, col);
-  const uint8_t* wrow[NB];
+  const uint8_t* wblk[NB];
   const ScaleT<WFMT>* srow[NB];
-  weight_rows<WFMT, NB>(w, w_scale, ti.e, N, K, col, ln, wrow, srow);
+  uint32_t wlane;
+  weight_rows<WFMT, NB>(w, w_scale, ti.e, N, K, col, ln, kb, wblk, srow, wlane);
   const int G = K >> 7;
   const int g0 = quarter_g0(G, q);
-  quarter_rows<WFMT, NB>(g0, wrow, srow);
+  quarter_rows<WFMT, NB>(g0, wblk, srow);
   const int kq = (GS > 0 ? GQ : quarter_groups(G, q)) * 128;   // K of this wave's quarter
 
   const int nrb = (ti.rows + 15) >> 4;
@@ -88,7 +89,7 @@ gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
         if (rrows > 3) v3 = *reinterpret_cast<const uint4*>(src + 3 * int64_t(K));
       }
       wave_sweep<WFMT, NB, GQ, true, kALds>(
-          acc, stage, kq, 0, rrows, 0, wrow, srow, ln, kb,
+          acc, stage, kq, 0, rrows, 0, wblk, srow, wlane, ln, kb,
           [&] {
             if (on) {
               uint8_t* d = stage + lane * 16;
@@ -100,8 +101,8 @@ gemm_wave_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int 
           },
           kStageStride);
     } else {
-      wave_sweep<WFMT, NB, GQ, false>(acc, a_q + g0 * 128, kq, ti.row0, ti.rows, rb, wrow, srow,
-                                      ln, kb, [] {}, K);
+      wave_sweep<WFMT, NB, GQ, false>(acc, a_q + g0 * 128, kq, ti.row0, ti.rows, rb, wblk, srow,
+                                      wlane, ln, kb, [] {}, K);
     }
     quarter_reduce<NB>(acc, red, q, lane, rb + 1 < nrb);
     if (q == 0)
@@ -162,7 +163,9 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
   if (!tile_info(plan, E, R, tile, ti)) return;   // workgroup-uniform
   const int nrb = (ti.rows + 15) >> 4;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (the wave index as a scalar: the weight block bases derived from it stay in
+  // scalar registers)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15, kb = lane >> 4;
   const int G = K >> 7;
 
@@ -177,9 +180,10 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
     else
       col[j] = nt * BN + 16 * (wave + 4 * j);
   }
-  const uint8_t* wrow[CB];
+  const uint8_t* wblk[CB];
   const ScaleT<WFMT>* srow[CB];
-  weight_rows<WFMT, CB>(w, w_scale, ti.e, N, K, col, ln, wrow, srow);
+  uint32_t wlane;
+  weight_rows<WFMT, CB>(w, w_scale, ti.e, N, K, col, ln, kb, wblk, srow, wlane);
 
   // A staging: wave w stages rows 16 w .. 16 w + 15 of the 64 x 128 B slice;
   // load j of lane l takes segment l % 8 (16 bytes) of row 16 w + 8 j + l / 8,
@@ -233,7 +237,7 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
     }
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
-      st[slot].b[j].load(wrow[j], g, kb);
+      st[slot].b[j].load(wblk[j], g * kGroupStride<WFMT>, wlane);
       if constexpr (!Shape::kLdsScales) st[slot].s[j] = sc.load(j, g);
     }
   };

@@ -30,7 +30,10 @@
 // consecutive output columns, for EPI_SILU_MUL 16 gate rows and the matching 16
 // up rows (N/2 further), so the SiLU-gated product forms in registers.  A lane
 // streams 16 B of packed weights (32 codes) per block per group: lane (n, kb)
-// reads bytes [16 kb, 16 kb + 16) of its row's 64-byte group.  Weight loads run
+// reads bytes [16 kb, 16 kb + 16) of its row's 64-byte group.  INT4 weights are
+// read in the library's tiled order (16-row blocks stored group after group), so
+// the 16 rows x 64 B that one load instruction of a wave takes are 1024
+// contiguous bytes rather than 16 pieces 2 KB apart.  Weight loads run
 // kDepth groups ahead of their use (a register ring, unrolled so every ring
 // index is static) to keep enough bytes in flight to cover HBM latency.
 //
@@ -239,11 +242,36 @@ __device__ __forceinline__ float load_scale(const uint16_t* p) {
 template <int WFMT>
 struct BFrag;
 
+// Bytes between consecutive 128-K groups of a weight block: INT4 in the tiled
+// order (a group of a 16-row block is 16 x 64 contiguous bytes), FP8-row in
+// rows (the next 128 bytes of each row).
+template <int WFMT>
+constexpr int kGroupStride = kIsW4<WFMT> ? 16 * 64 : 128;
+
+// 16 bytes at base + off + lane by a buffer load: base (the weight block's first
+// byte) goes into a buffer resource and off (the group's group_offset) into the
+// scalar offset, both wave-uniform; only the lane's 32-bit offset lane is a
+// vector register, shared by every load of a sweep.  (A flat global load would
+// need a 64-bit vector address per load once off is not a compile-time
+// constant, and the unrolled sweep would run out of registers.)  Word 3 of the
+// resource: 32-bit data format, the setting for untyped buffer access on gfx9;
+// the record count is the largest the 32-bit offsets can reach.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_weight16(const uint8_t* base, int off, uint32_t lane) {
+  const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(base), static_cast<short>(0), 0x7FFFFFFF, 0x00020000);
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(res, int(lane), off, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// BFrag::load(base, off, lane): base the weight block's first byte, off the
+// group's offset g kGroupStride (both wave-uniform), lane this lane's offset
+// (weight_rows).
 template <>
 struct BFrag<kW4G128> {
   uint4 raw;
-  __device__ __forceinline__ void load(const uint8_t* row, int g, int kb) {
-    raw = *reinterpret_cast<const uint4*>(row + g * 64 + kb * 16);
+  __device__ __forceinline__ void load(const uint8_t* base, int off, uint32_t lane) {
+    raw = load_weight16(base, off, lane);
   }
   __device__ __forceinline__ v8i operand() const { return unpack_w4(raw); }
 };
@@ -254,10 +282,9 @@ struct BFrag<kW4G128Bf16> : BFrag<kW4G128> {};
 template <>
 struct BFrag<kFp8Row> {
   uint4 raw0, raw1;
-  __device__ __forceinline__ void load(const uint8_t* row, int g, int kb) {
-    const uint4* p = reinterpret_cast<const uint4*>(row + g * 128 + kb * 32);
-    raw0 = p[0];
-    raw1 = p[1];
+  __device__ __forceinline__ void load(const uint8_t* base, int off, uint32_t lane) {
+    raw0 = load_weight16(base, off, lane);
+    raw1 = load_weight16(base, off, lane + 16);
   }
   __device__ __forceinline__ F16x32 operand() const { return fp8x32_to_f16(raw0, raw1); }
 };
@@ -331,17 +358,22 @@ __device__ __forceinline__ bool tile_info(const int32_t* plan, int E, int R, int
   return tile < n;
 }
 
-// weight-row bases (16-row block j of this wave) and their scale rows
+// Weights of the 16-row blocks j of this wave (rows col[j] .. col[j] + 15 of
+// expert e, col[j] a multiple of 16 and wave-uniform): wblk[j] the block's first
+// byte (16 rows x K/2 bytes per INT4 block, K bytes per FP8 row), srow[j] the
+// scales of this lane's row col[j] + ln, and lane the lane's byte offset inside
+// a block's group (INT4 tiled order: row ln at 64 ln, bytes 16 kb; FP8 rows:
+// row ln at ln K, bytes 32 kb).
 template <int WFMT, int NB = 2>
 __device__ __forceinline__ void weight_rows(const uint8_t* w, const ScaleT<WFMT>* w_scale, int e,
-                                            int N, int K, const int (&col)[NB], int ln,
-                                            const uint8_t* (&wrow)[NB],
-                                            const ScaleT<WFMT>* (&srow)[NB]) {
-  const int64_t row_bytes = kIsW4<WFMT> ? (K >> 1) : K;
+                                            int N, int K, const int (&col)[NB], int ln, int kb,
+                                            const uint8_t* (&wblk)[NB],
+                                            const ScaleT<WFMT>* (&srow)[NB], uint32_t& lane) {
+  lane = kIsW4<WFMT> ? uint32_t(ln * 64 + kb * 16) : uint32_t(ln * K + kb * 32);
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int64_t n_glob = int64_t(e) * N + col[j] + ln;
-    wrow[j] = w + n_glob * row_bytes;
+    wblk[j] = w + (int64_t(e) * N + col[j]) * (kIsW4<WFMT> ? (K >> 1) : K);
     srow[j] = kIsW4<WFMT> ? (w_scale + n_glob * (K >> 7)) : (w_scale + n_glob);
   }
 }
@@ -540,11 +572,13 @@ enum ASource { kAGlobal = 0, kALds = 1 };
 // With kSplit the first kDepth groups' weights are issued, then before_a()
 // runs (e.g. producing the activations), then their activations; otherwise
 // each group's activations and weights are issued together.
+// The weights: block bases wblk and scales srow (as quarter_rows leaves them),
+// lane offset wlane (weight_rows).
 template <int WFMT, int NB, int GS, bool kSplit, int ASRC = kAGlobal, typename HookF>
 __device__ __forceinline__ void wave_sweep(v4f (&acc)[NB], const uint8_t* a_q, int K, int row0,
-                                           int rows, int rb, const uint8_t* const (&wrow)[NB],
-                                           const ScaleT<WFMT>* const (&srow)[NB], int ln, int kb,
-                                           HookF&& before_a, int a_stride = 0) {
+                                           int rows, int rb, const uint8_t* const (&wblk)[NB],
+                                           const ScaleT<WFMT>* const (&srow)[NB], uint32_t wlane,
+                                           int ln, int kb, HookF&& before_a, int a_stride = 0) {
   const int G = K >> 7;
   const bool a_ok = 16 * rb + ln < rows;
   const int a_row = a_ok ? 16 * rb + ln : 0;
@@ -572,7 +606,7 @@ __device__ __forceinline__ void wave_sweep(v4f (&acc)[NB], const uint8_t* a_q, i
   auto issue_b = [&](int slot, int g) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      st[slot].b[j].load(wrow[j], g, kb);
+      st[slot].b[j].load(wblk[j], g * kGroupStride<WFMT>, wlane);
       st[slot].s[j] = sc.load(j, g);
     }
   };
@@ -627,15 +661,14 @@ __device__ __forceinline__ void wave_sweep(v4f (&acc)[NB], const uint8_t* a_q, i
 __device__ __forceinline__ int quarter_g0(int G, int q) { return (q * G) >> 2; }
 __device__ __forceinline__ int quarter_groups(int G, int q) { return (((q + 1) * G) >> 2) - ((q * G) >> 2); }
 
-// Moves this wave's weight-row and scale pointers to the first group g0 of
+// Moves this wave's weight blocks and scale pointers to the first group g0 of
 // its quarter.
 template <int WFMT, int NB>
-__device__ __forceinline__ void quarter_rows(int g0, const uint8_t* (&wrow)[NB],
+__device__ __forceinline__ void quarter_rows(int g0, const uint8_t* (&wblk)[NB],
                                              const ScaleT<WFMT>* (&srow)[NB]) {
-  constexpr int kGroupBytes = kIsW4<WFMT> ? 64 : 128;   // bytes of one row's 128-K group
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    wrow[j] += g0 * kGroupBytes;
+    wblk[j] += g0 * kGroupStride<WFMT>;
     if constexpr (kIsW4<WFMT>) srow[j] += g0;             // per-group scales; FP8-row: per row
   }
 }

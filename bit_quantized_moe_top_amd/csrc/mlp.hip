@@ -38,7 +38,7 @@ down_hq_kernel(const uint16_t* h, const int32_t* plan, int E, int R, const uint8
   __shared__ float s_part[4][kHqRows];          // per-quarter max |h| of each row
   __shared__ float s_scale[kHqRows];
   __shared__ v4f red[3 * 2 * kWave];           // quarter sums of waves 1..3
-  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15, kb = lane >> 4;
   const int upt = H >> 5;                       // units per tile
   const int tile = blockIdx.x / upt;
@@ -54,12 +54,13 @@ down_hq_kernel(const uint16_t* h, const int32_t* plan, int E, int R, const uint8
 
   int col[2];
   unit_columns<MOEQ_EPI_NONE>(H, u, col);
-  const uint8_t* wrow[2];
+  const uint8_t* wblk[2];
   const ScaleT<WFMT>* srow[2];
-  weight_rows<WFMT>(w2, s2, ti.e, H, I, col, ln, wrow, srow);
+  uint32_t wlane;
+  weight_rows<WFMT>(w2, s2, ti.e, H, I, col, ln, kb, wblk, srow, wlane);
   const int G = I >> 7;
   const int g0 = quarter_g0(G, q);
-  quarter_rows<WFMT, 2>(g0, wrow, srow);
+  quarter_rows<WFMT, 2>(g0, wblk, srow);
   const int kq = (GS > 0 ? GQ : quarter_groups(G, q)) * 128;   // <= kHqMaxQuarter
   const int c0 = g0 * 128 + lane * 8;           // this lane's 8 elements of the quarter
   const bool on = lane * 8 < kq;
@@ -118,7 +119,7 @@ down_hq_kernel(const uint16_t* h, const int32_t* plan, int E, int R, const uint8
       for (int r = 4; r < rrows; ++r) encode(r, on ? load_h8(hb + r * int64_t(I)) : zero);
     };
     v4f acc[2];
-    wave_sweep<WFMT, 2, GQ, true, kALds>(acc, stage, kq, 0, rrows, 0, wrow, srow, ln, kb,
+    wave_sweep<WFMT, 2, GQ, true, kALds>(acc, stage, kq, 0, rrows, 0, wblk, srow, wlane, ln, kb,
                                          quantize, kHqStride);
     quarter_reduce<2>(acc, red, q, lane, rb + 1 < nrb);
     if (q == 0)

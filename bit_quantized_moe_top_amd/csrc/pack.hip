@@ -4,7 +4,8 @@
 // each lane stores its 8 codes as one little-endian 32-bit word of nibbles
 // (code + 8, first code in the least significant nibble).  With bfloat16
 // scales the stored scale is bf16(max/7) (RNE) and the codes are taken
-// against that stored value.
+// against that stored value.  tile_int4_kernel moves packed rows into the
+// GEMMs' tiled order.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -56,7 +57,36 @@ pack_int4_kernel(const float* __restrict__ w, int64_t n_groups, int groups_per_r
   (void)groups_per_row;
 }
 
+// Packed rows [rows][K/2] -> the tiled order [rows/16][K/128][16][64] (16-row
+// blocks stored group after group).  One thread per 16 output bytes, numbered in
+// output order u: piece c = u % 4 of row r = (u / 4) % 16 of group
+// g = (u / 64) % G of block b = u / (64 G), read from row 16 b + r, bytes
+// 64 g + 16 c.  Grid-stride over u.
+__global__ void __launch_bounds__(256)
+tile_int4_kernel(const uint4* __restrict__ in, int64_t units, int G, uint4* __restrict__ out) {
+  const int64_t row_units = int64_t(G) * 4;                 // 16-byte pieces per row
+  for (int64_t u = int64_t(blockIdx.x) * 256 + threadIdx.x; u < units;
+       u += int64_t(gridDim.x) * 256) {
+    const int c = int(u & 3), r = int((u >> 2) & 15);
+    const int64_t bg = u >> 6;                               // block * G + group
+    const int64_t b = bg / G, g = bg - b * G;
+    out[u] = in[(16 * b + r) * row_units + 4 * g + c];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_tile_int4(const uint8_t* packed, int64_t rows, int K, uint8_t* tiled,
+                            hipStream_t stream) {
+  const int64_t units = rows * (K / 32);
+  if (units == 0) return hipSuccess;
+  const int64_t blocks = (units + 255) / 256;
+  const unsigned grid = unsigned(blocks < 65536 * 16 ? blocks : 65536 * 16);
+  hipLaunchKernelGGL(tile_int4_kernel, dim3(grid), dim3(256), 0, stream,
+                     reinterpret_cast<const uint4*>(packed), units, K / 128,
+                     reinterpret_cast<uint4*>(tiled));
+  return hipGetLastError();
+}
 
 template <typename ST>
 hipError_t launch_pack(const float* w, int64_t rows, int K, uint8_t* packed, ST* scales,

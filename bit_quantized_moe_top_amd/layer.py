@@ -45,15 +45,16 @@ class MoELayer:
 
     # --------------------------------------------------------------- weights
     def set_weights(self, w13, s13, w2, s2):
-        """Already-quantized weights (packed INT4 + group scales, or E4M3 + row scales)."""
+        """Already-quantized weights: INT4 in the GEMMs' tiled order (tile_int4_weights)
+        with group scales, or E4M3 with row scales."""
         self.w13, self.s13, self.w2, self.s2 = w13, s13, w2, s2
 
     def quantize_weights(self, w13_f32: torch.Tensor, w2_f32: torch.Tensor):
         """Quantize fp32 weights on the device with the library's own kernels."""
         if self.weight_format in ("w4a8", "w4a8_bf16s"):
             sdt = torch.bfloat16 if self.weight_format == "w4a8_bf16s" else torch.float32
-            self.w13, self.s13 = pack_int4_g128(w13_f32, scale_dtype=sdt)
-            self.w2, self.s2 = pack_int4_g128(w2_f32, scale_dtype=sdt)
+            self.w13, self.s13 = pack_int4_g128(w13_f32, scale_dtype=sdt, tiled=True)
+            self.w2, self.s2 = pack_int4_g128(w2_f32, scale_dtype=sdt, tiled=True)
         else:
             self.w13, self.s13 = quant_fp8_per_token(w13_f32)
             self.w2, self.s2 = quant_fp8_per_token(w2_f32)

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOEQ_ABI_VERSION 2
+#define MOEQ_ABI_VERSION 3
 
 /* status codes */
 #define MOEQ_OK               0
@@ -231,6 +231,32 @@ int pack_int4_g128_bf16s(const float* w, int64_t rows, int K, uint8_t* packed, u
                          void* stream);
 
 /*
+ * moe_tile_int4_weights -- packed INT4 weights (pack_int4_g128's layout, which is
+ * the checkpoint's) into the tiled order every INT4 GEMM and expert-MLP call
+ * reads (offline weight preparation, once per weight tensor).
+ *
+ * The checkpoint stores each output row's packed codes contiguously
+ * ("wstewart3/Inkling-Small-W4A8-G128", section 7: I32 [N, K/8] per projection).
+ * The kernels read a 128-wide K group of 16 consecutive rows per wave load
+ * instruction, which in that order is 16 pieces of 64 bytes 2 KB apart; the
+ * tiled order makes them 1024 contiguous bytes.  Tiled order (a permutation of
+ * whole bytes; no code changes):
+ *   w_tiled[((b * G + g) * 16 + r) * 64 + c] = w_packed[(16 b + r) * K/2 + 64 g + c]
+ * for block b < rows/16, group g < G = K/128, row r < 16, byte c < 64.  With
+ * N % 16 == 0 the blocks of an expert stack [E, N, K/2] never straddle two
+ * experts, so rows = E * N tiles the stack in one call, and tiling it a few
+ * experts at a time gives the same bytes.
+ *
+ *   w_packed [rows, K/2] bytes (the byte view of [rows, K/8] int32 words)
+ *   w_tiled  [rows, K/2] bytes (out), not overlapping w_packed
+ * Limits: rows % 16 == 0, K % 128 == 0, both buffers 16-byte aligned.
+ * Errors: MOEQ_ERR_UNSUPPORTED for rows % 16 != 0 or K % 128 != 0;
+ * MOEQ_ERR_INVALID_ARG for overlapping, null or misaligned buffers.
+ */
+int moe_tile_int4_weights(const uint8_t* w_packed, int64_t rows, int K, uint8_t* w_tiled,
+                          void* stream);
+
+/*
  * moe_requant_fp8_fnuz -- row-scaled E4M3FNUZ expert weights to row-scaled OCP
  * E4M3 (offline weight preparation).
  *
@@ -271,9 +297,10 @@ int moe_requant_fp8_fnuz(const uint8_t* w_fnuz, const float* s_fnuz, int64_t row
  *
  *   a_q [R, K] E4M3, a_s [R] fp32 -- rows in plan order
  *   plan, plan_bytes -- from moe_permute with the same E and R (read only)
- *   w_packed [E, N, K/2] (pack_int4_g128 layout; the little-endian byte view of
- *     the checkpoint's int32 [E, N, K/8] .weight_packed words, passed through
- *     as they are), w_scales [E, N, K/128] fp32
+ *   w_packed [E, N, K/2] bytes in the tiled order of moe_tile_int4_weights
+ *     (from pack_int4_g128's output, or from the checkpoint's int32
+ *     [E, N, K/8] .weight_packed words viewed as bytes), w_scales [E, N, K/128]
+ *     fp32 (row order, as written by pack_int4_g128)
  * Limits: K % 128 == 0, N % 128 == 0, R >= 0, 1 <= E <= MOEQ_MAX_EXPERTS;
  * a_q, w_packed and w_scales 16-byte aligned.
  */
@@ -392,6 +419,7 @@ int moe_grouped_gemm_fp8row(const uint8_t* a_q, const float* a_s, const void* pl
  *   plan, plan_bytes -- from moe_permute / moe_route_quant_permute with E, R (read only)
  *   w13 [E, 2I, H/2] packed INT4 (gate rows then up rows), w13_scales [E, 2I, H/128]
  *   w2  [E, H, I/2] packed INT4, w2_scales [E, H, I/128]
+ *   (both weight tensors in the tiled order of moe_tile_int4_weights)
  *   h [R, I] bf16, h_q [R, I] E4M3, h_s [R] fp32, o [R, H] bf16 (outputs)
  * Limits: H % 128 == 0, I % 128 == 0, 1 <= E <= MOEQ_MAX_EXPERTS; xp_q, h_q,
  * the weights and their scales 16-byte aligned.

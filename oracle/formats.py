@@ -18,7 +18,8 @@
   codes per little-endian 32-bit word with the first code in the least
   significant nibble ("wstewart3/Inkling-Small-W4A8-G128", §7 "Recover and
   physically pack INT4", packing bullets).  Viewed as bytes this is two codes
-  per byte, first code in the low nibble.
+  per byte, first code in the low nibble.  The kernels read these bytes in a
+  tiled order of their own (tile_int4), a permutation of whole bytes.
 
 Rounding is round-to-nearest-even everywhere (the pages do not name a rounding
 mode; RNE is the IEEE default).
@@ -184,6 +185,27 @@ def unpack_int4(packed) -> np.ndarray:
     out[..., 0::2] = lo
     out[..., 1::2] = hi
     return out
+
+
+TILE_ROWS = 16
+
+
+def tile_int4(packed) -> np.ndarray:
+    """Packed INT4 bytes [..., N, K/2] -> the kernels' tiled order
+    [..., N/16, K/128, 16, 64]: 16-row blocks, each stored group after group, so
+    the 64 bytes (128 codes) of one 128-wide K group of 16 consecutive rows are
+    1024 contiguous bytes.  Element [..., b, g, r, c] is byte c of group g of row
+    16 b + r, i.e. packed[..., 16 b + r, 64 g + c].  This storage order is the
+    library's own (the pages' checkpoints keep rows contiguous); it changes where
+    bytes sit, never a byte.
+    """
+    p = np.asarray(packed, dtype=np.uint8)
+    N, K2 = p.shape[-2], p.shape[-1]
+    if N % TILE_ROWS or (2 * K2) % GROUP:
+        raise ValueError("tile_int4: N must be a multiple of 16 and K of 128")
+    lead = p.shape[:-2]
+    blocks = p.reshape(lead + (N // TILE_ROWS, TILE_ROWS, (2 * K2) // GROUP, GROUP // 2))
+    return np.ascontiguousarray(np.swapaxes(blocks, -3, -2))
 
 
 def int32_words(packed) -> np.ndarray:

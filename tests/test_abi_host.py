@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     assert set(names) == set(mq.EXPORTED_SYMBOLS)
 
 
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert mq.moe_abi_version() == 2
+    assert mq.moe_abi_version() == 3
     assert mq.moe_status_string(0) == "ok"
     for s in range(1, 7):
         assert mq.moe_status_string(s) not in ("ok", "unknown status")
@@ -99,6 +99,15 @@ def test_argument_errors_are_reported_without_a_gpu():
     # pack
     assert L.pack_int4_g128(FAKE, 4, 100, FAKE, FAKE, N) == UNSUPPORTED
     assert L.pack_int4_g128(N, 4, 128, FAKE, FAKE, N) == INVALID
+    # tiled order: rows % 16, K % 128, null, misaligned and overlapping buffers
+    other = ctypes.c_void_p(FAKE.value + (1 << 20))
+    assert L.moe_tile_int4_weights(FAKE, 8, 128, other, N) == UNSUPPORTED
+    assert L.moe_tile_int4_weights(FAKE, 16, 100, other, N) == UNSUPPORTED
+    assert L.moe_tile_int4_weights(FAKE, -16, 128, other, N) == INVALID
+    assert L.moe_tile_int4_weights(N, 16, 128, other, N) == INVALID
+    assert L.moe_tile_int4_weights(FAKE, 16, 128, ctypes.c_void_p(FAKE.value + 8), N) == INVALID
+    assert L.moe_tile_int4_weights(FAKE, 16, 128, ctypes.c_void_p(FAKE.value + 512), N) == INVALID
+    assert L.moe_tile_int4_weights(FAKE, 0, 128, other, N) == OK
     # grouped GEMMs (plan_bytes after the plan)
     pb = mq.moe_plan_size(8, 32)
     for fn in (L.moe_grouped_gemm_w4a8, L.moe_grouped_gemm_fp8row, L.moe_grouped_gemm_w4a8_bf16s):

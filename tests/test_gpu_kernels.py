@@ -227,6 +227,38 @@ def test_pack_int4_g128(shape, scale_dtype):
     rp, rs = L.pack_int4_g128(w.reshape(rows, shape[2]).numpy(), scale_dtype=scale_dtype)
     np.testing.assert_array_equal(scales.cpu().float().numpy().reshape(rows, -1), rs)
     np.testing.assert_array_equal(packed.cpu().numpy().reshape(rows, -1), rp)
+    # tiled=True: the same bytes in the GEMMs' tiled order
+    tiled, scales_t = mq.pack_int4_g128(
+        w.to(_dev()), scale_dtype=torch.bfloat16 if scale_dtype == "bf16" else torch.float32,
+        tiled=True)
+    torch.cuda.synchronize()
+    assert tuple(tiled.shape) == (shape[0], shape[1] // 16, shape[2] // 128, 16, 64)
+    np.testing.assert_array_equal(tiled.cpu().numpy(), F.tile_int4(rp.reshape(shape[0], shape[1], -1)))
+    np.testing.assert_array_equal(scales_t.cpu().float().numpy().reshape(rows, -1), rs)
+
+
+@pytest.mark.parametrize("shape", [(1, 16, 128), (3, 48, 384), (2, 4096, 2048), (1, 2048, 4096)])
+def test_tile_int4_weights(shape):
+    """moe_tile_int4_weights is the oracle's tile_int4 byte for byte, from uint8 rows
+    and from the checkpoint's int32 words (the same bytes)."""
+    E, N, K = shape
+    rng = np.random.default_rng(N + K)
+    packed = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    ref = F.tile_int4(packed)
+    got = mq.tile_int4_weights(torch.from_numpy(packed).to(_dev()))
+    words = torch.from_numpy(packed.view("<i4").copy()).to(_dev())       # int32 [E, N, K/8]
+    got_w = mq.tile_int4_weights(words)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), ref)
+    np.testing.assert_array_equal(got_w.cpu().numpy(), ref)
+    with pytest.raises(ValueError):                     # N not a multiple of 16
+        mq.tile_int4_weights(torch.from_numpy(packed[:, :N - 8].copy()).to(_dev()))
+    with pytest.raises(ValueError):                     # page-order rows given to a GEMM
+        mq.moe_grouped_gemm_w4a8(torch.zeros(1, K, dtype=torch.uint8, device=_dev()),
+                                 torch.ones(1, device=_dev()), torch.zeros(64, dtype=torch.int32,
+                                                                           device=_dev()),
+                                 torch.from_numpy(packed).to(_dev()),
+                                 torch.ones(E, N, K // 128, device=_dev()))
 
 
 # ---------------------------------------------------------------- permute ----
@@ -375,7 +407,8 @@ def test_w4a8_integer_exact(T, k, E, N, K, hot):
     for epi in (mq.EPI_NONE, mq.EPI_SILU_MUL):
         out = mq.moe_grouped_gemm_w4a8(
             torch.from_numpy(a_q).to(_dev()), torch.ones(R, device=_dev()), plan,
-            torch.from_numpy(packed).to(_dev()), torch.from_numpy(ones_w).to(_dev()),
+            mq.tile_int4_weights(torch.from_numpy(packed).to(_dev())),
+            torch.from_numpy(ones_w).to(_dev()),
             epilogue=epi, out_dtype=torch.float32 if epi == mq.EPI_NONE else torch.bfloat16)
         torch.cuda.synchronize()
         ref = L.w4a8_rows(a_q, np.ones(R, np.float32), experts, lambda e: codes[e],
@@ -420,17 +453,18 @@ def test_grouped_gemm_random(fmt, T, k, E, N, K, hot):
         ref_fn = lambda: L.fp8row_rows(a_q, a_s, experts, lambda e: qs[e][0], lambda e: qs[e][1])  # noqa
     ref = ref_fn()
     dq = lambda a: torch.from_numpy(a).to(_dev())  # noqa
-    out32 = fn(dq(a_q), dq(a_s), plan, dq(wq), ws_t(ws), epilogue=mq.EPI_NONE,
+    wt = dq(wq) if fmt == "fp8row" else mq.tile_int4_weights(dq(wq))
+    out32 = fn(dq(a_q), dq(a_s), plan, wt, ws_t(ws), epilogue=mq.EPI_NONE,
                out_dtype=torch.float32)
-    outbf = fn(dq(a_q), dq(a_s), plan, dq(wq), ws_t(ws), epilogue=mq.EPI_NONE,
+    outbf = fn(dq(a_q), dq(a_s), plan, wt, ws_t(ws), epilogue=mq.EPI_NONE,
                out_dtype=torch.bfloat16)
-    h = fn(dq(a_q), dq(a_s), plan, dq(wq), ws_t(ws), epilogue=mq.EPI_SILU_MUL)
+    h = fn(dq(a_q), dq(a_s), plan, wt, ws_t(ws), epilogue=mq.EPI_SILU_MUL)
     torch.cuda.synchronize()
     assert_close(to_np(out32), ref, rel=1e-4, max_abs_frac=1e-4, what="fp32 out")
     assert_close(to_np(outbf), F.bf16_round(ref), what="bf16 out")
     assert_close(to_np(h), L.silu_mul(ref), what="silu_mul")
     # determinism: a second run is bitwise identical
-    h2 = fn(dq(a_q), dq(a_s), plan, dq(wq), ws_t(ws), epilogue=mq.EPI_SILU_MUL)
+    h2 = fn(dq(a_q), dq(a_s), plan, wt, ws_t(ws), epilogue=mq.EPI_SILU_MUL)
     assert torch.equal(h, h2)
 
 

@@ -37,8 +37,8 @@ def _setup(T, k, E, H, I, fmt, hot, seed):
     w2 = torch.randn(E, H, I, device=_dev(), generator=g) * 0.02
     if fmt in ("w4a8", "w4a8_bf16s"):
         sdt = torch.bfloat16 if fmt == "w4a8_bf16s" else torch.float32
-        q13, s13 = mq.pack_int4_g128(w13, scale_dtype=sdt)
-        q2, s2 = mq.pack_int4_g128(w2, scale_dtype=sdt)
+        q13, s13 = mq.pack_int4_g128(w13, scale_dtype=sdt, tiled=True)
+        q2, s2 = mq.pack_int4_g128(w2, scale_dtype=sdt, tiled=True)
     else:
         q13, s13 = mq.quant_fp8_per_token(w13)
         q2, s2 = mq.quant_fp8_per_token(w2)
@@ -90,11 +90,14 @@ def test_expert_mlp_argument_errors():
     s = torch.zeros(4, device=_dev())
     ids = torch.zeros(1, 4, dtype=torch.int32, device=_dev())
     plan, _, _ = mq.moe_permute(ids, 8)
-    w13 = torch.zeros(8, 256, 64, dtype=torch.uint8, device=_dev())
+    w13 = torch.zeros(8, 16, 1, 16, 64, dtype=torch.uint8, device=_dev())   # tiled, N=256, K=128
     s13 = torch.zeros(8, 256, 1, device=_dev())
-    w2 = torch.zeros(8, 128, 64, dtype=torch.uint8, device=_dev())
+    w2 = torch.zeros(8, 8, 1, 16, 64, dtype=torch.uint8, device=_dev())     # tiled, N=128, K=128
     s2 = torch.zeros(8, 128, 1, device=_dev())
     with pytest.raises(mq.MoeqError):                   # plan too small for R = 4
         mq.moe_expert_mlp_w4a8(z, s, plan[:8], w13, s13, w2, s2)
     with pytest.raises(ValueError):
-        mq.moe_expert_mlp_w4a8(z, s, plan, w13, s13, w2[:, :64], s2)
+        mq.moe_expert_mlp_w4a8(z, s, plan, w13, s13, w2[:, :4], s2)
+    with pytest.raises(ValueError):                     # packed rows not in the tiled order
+        mq.moe_expert_mlp_w4a8(z, s, plan, torch.zeros(8, 256, 64, dtype=torch.uint8,
+                                                       device=_dev()), s13, w2, s2)

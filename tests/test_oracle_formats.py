@@ -189,6 +189,27 @@ def test_int4_pack_brute_force_and_roundtrip():
     np.testing.assert_array_equal(F.unpack_int4(packed), codes)
 
 
+def test_tile_int4_brute_force():
+    """Every byte of the tiled order lands at the offset its definition gives:
+    ((b * G + g) * 16 + r) * 64 + c for byte c of group g of row 16 b + r, per
+    expert; a pure permutation (sorting recovers the input)."""
+    rng = np.random.default_rng(3)
+    E, N, K = 2, 48, 384
+    G = K // 128
+    packed = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    tiled = F.tile_int4(packed)
+    assert tiled.shape == (E, N // 16, G, 16, 64)
+    flat = tiled.reshape(E, -1)
+    for e in range(E):
+        for n in range(N):
+            for kb in range(K // 2):
+                b, r, g, c = n // 16, n % 16, kb // 64, kb % 64
+                assert flat[e, ((b * G + g) * 16 + r) * 64 + c] == packed[e, n, kb]
+    np.testing.assert_array_equal(np.sort(flat, axis=1), np.sort(packed.reshape(E, -1), axis=1))
+    with pytest.raises(ValueError):
+        F.tile_int4(packed[:, :40])
+
+
 def test_int4_pack_rejects_out_of_range():
     with pytest.raises(ValueError):
         F.pack_int4(np.array([[8, 0]]))

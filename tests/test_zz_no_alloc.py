@@ -19,8 +19,9 @@ def _case(T, k, E, H, I, seed, dev):
     x = torch.randn(T, H, generator=g, device=dev).to(torch.bfloat16)
     x_q, x_s = mq.quant_fp8_per_token(x)
     plan, xp_q, xp_s = mq.moe_permute(ids, E, x_q, x_s)
-    w13, s13 = mq.pack_int4_g128(torch.randn(E, 2 * I, H, generator=g, device=dev) * 0.02)
-    w2, s2 = mq.pack_int4_g128(torch.randn(E, H, I, generator=g, device=dev) * 0.02)
+    w13, s13 = mq.pack_int4_g128(torch.randn(E, 2 * I, H, generator=g, device=dev) * 0.02,
+                                 tiled=True)
+    w2, s2 = mq.pack_int4_g128(torch.randn(E, H, I, generator=g, device=dev) * 0.02, tiled=True)
     return plan, xp_q, xp_s, w13, s13, w2, s2
 
 
