@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the supplementary prefill token sweep (T = 4096 .. 16384)")
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed", "fp8row"])
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="token count T of the workload (default: the workload's own); for "
+                         "profiling one point of the prefill token sweep")
     ap.add_argument("--summarize", metavar="DIR",
                     help="only summarise the rocprofv3 CSV output under DIR (kernel stats, or the "
                          "mean per dispatch of every collected counter per kernel) and exit")
@@ -335,9 +338,10 @@ def time_hybrid(cfg, n_sets, steps, warmup, dev):
 
 
 def measured_traffic(kernel_bytes: float, name: str = "gemm_gate_up_decode_T4_traffic"):
-    """HBM bytes per launch of the decode layer's dominant kernel from the
-    committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if the kernel sources
-    are still the ones the counters were taken on (else None)."""
+    """HBM bytes per launch of a layer's gate/up GEMM from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary profiles/<name>.json, if the
+    kernel sources are still the ones the counters were taken on (else None),
+    with the down GEMM's and the summary's matrix-core counters when it has them."""
     import hashlib
     path = os.path.join(ROOT, "profiles", name + ".json")
     try:
@@ -347,9 +351,14 @@ def measured_traffic(kernel_bytes: float, name: str = "gemm_gate_up_decode_T4_tr
             h.update(open(os.path.join(ROOT, "bit_quantized_moe_top_amd", "csrc", f), "rb").read())
         if h.hexdigest() != doc["source_sha256"]:
             return None
-        return {"bytes_per_launch": doc["hbm_bytes_per_launch"],
-                "vs_algorithmic": round(doc["hbm_bytes_per_launch"] / kernel_bytes, 4),
-                "source": f"profiles/{name}.md"}
+        out = {"bytes_per_launch": doc["hbm_bytes_per_launch"],
+               "vs_algorithmic": round(doc["hbm_bytes_per_launch"] / kernel_bytes, 4),
+               "source": f"profiles/{name}.md"}
+        if "down_gemm" in doc:
+            out["down_bytes_per_launch"] = doc["down_gemm"]["hbm_bytes_per_launch"]
+        if "mfma" in doc:
+            out["mfma"] = doc["mfma"]
+        return out
     except (OSError, KeyError, ValueError):
         return None
 
@@ -440,6 +449,11 @@ def prefill_summary(pcfg, pres, short=False):
     pc = pres["per_call_us"]
     if "gemm_down" in pc:
         d["down_gemm_GBps"] = round(pres["distinct_mean"] * pw2 / (pc["gemm_down"] * 1e-6) / 1e9, 1)
+    if not short:
+        tr = measured_traffic(pres["distinct_mean"] * pw13,
+                              f"gemm_gate_up_{pcfg.name}_T{pcfg.T}_traffic")
+        if tr is not None:
+            d["gate_up_traffic"] = tr
     if pcfg.n_shared:
         sh_us = pc.get("shared_gate_up", 0.0) + pc.get("shared_down", 0.0)
         d["shared_bf16"] = {"flops": bf16_flops, "us": round(sh_us, 2),
@@ -453,13 +467,24 @@ def prefill_summary(pcfg, pres, short=False):
 
 
 def copy_ceiling(dev, nbytes=2 << 30, reps=5):
-    """Measured streaming ceilings on this machine with torch's own kernels: a
-    device-to-device copy of nbytes (bytes read + written per second) and a
-    reduction over 2 * nbytes (bytes read per second)."""
+    """Measured streaming ceilings on this machine: a device-to-device copy of nbytes
+    with torch's copy kernel (bytes read + written per second), and the library's
+    streaming-read probe over nbytes at a time, rotating through four such chunks
+    so that no chunk is still in the 256 MB last-level cache (bytes read per
+    second)."""
     import torch
+
+    import bit_quantized_moe_top_amd as mq
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    big = torch.ones(2 * nbytes // 4, dtype=torch.float32, device=dev)
+    big = torch.ones(4 * nbytes // 4, dtype=torch.float32, device=dev)
+    chunks = [big[i * (nbytes // 4):(i + 1) * (nbytes // 4)] for i in range(4)]
+    sink = torch.empty(mq.READ_PROBE_BLOCKS * 4, dtype=torch.int32, device=dev)
+    probe_i = [0]
+
+    def probe():
+        mq.moe_read_bandwidth_probe(chunks[probe_i[0] % 4], sink)
+        probe_i[0] += 1
 
     def timed(fn):
         fn()
@@ -471,13 +496,14 @@ def copy_ceiling(dev, nbytes=2 << 30, reps=5):
         torch.cuda.synchronize()
         return s_ev.elapsed_time(e_ev) * 1e-3 / reps
     copy_s = timed(lambda: dst.copy_(src))
-    read_s = timed(lambda: torch.sum(big))
-    del src, dst, big
+    read_s = timed(probe)
+    del src, dst, big, chunks
     torch.cuda.empty_cache()
     return {"GBps": round(2 * nbytes / copy_s / 1e9, 1), "bytes": nbytes,
             "kind": "device copy (read + write), torch copy kernel",
-            "read_GBps": round(2 * nbytes / read_s / 1e9, 1),
-            "read_kind": f"torch.sum over {2 * nbytes >> 30} GiB of fp32 (bytes read)"}
+            "read_GBps": round(nbytes / read_s / 1e9, 1),
+            "read_kind": f"moe_read_bandwidth_probe over {nbytes >> 30} GiB at a time, four "
+                         f"chunks in rotation (bytes read)"}
 
 
 def sclk_mhz():
@@ -516,7 +542,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 5}))
         return
-    cfg = W.get_config(args.workload)
+    cfg = W.get_config(args.workload, **({"T": args.tokens} if args.tokens else {}))
     log(f"device {torch.cuda.get_device_name(0)}; workload {cfg}")
     sclk_before = sclk_mhz()
     res = time_layer(cfg, args.sets, args.steps, args.warmup, dev, graph=not args.no_graph,
@@ -642,8 +668,18 @@ def main():
         }
         torch.cuda.empty_cache()
     out["copy_ceiling"] = copy_ceiling(dev)
-    out["layer_frac_of_read_ceiling"] = round(gbs / out["copy_ceiling"]["read_GBps"], 4) \
-        if cfg.name == "decode" else None
+    ceil_gbs = out["copy_ceiling"]["read_GBps"]
+    out["layer_frac_of_read_ceiling"] = round(gbs / ceil_gbs, 4) if cfg.name == "decode" else None
+    # the dominant kernel and the prefill GEMMs against the measured read ceiling
+    # (the roofline's peak stays the interface's published 8 TB/s)
+    out["roofline"]["read_ceiling_GBps"] = ceil_gbs
+    out["roofline"]["frac_of_read_ceiling"] = round(dom_gbs / ceil_gbs, 4)
+    for name in ("prefill", "skewed", "fp8row"):
+        if name in out:
+            for key in ("gate_up_gemm_GBps", "down_gemm_GBps"):
+                if key in out[name]:
+                    out[name][key.replace("_GBps", "_frac_of_read_ceiling")] = \
+                        round(out[name][key] / ceil_gbs, 4)
     out["sclk_mhz"] = {"before": sclk_before, "after": sclk_mhz()}
     out["host"] = platform.node()
     print(json.dumps(out), flush=True)

@@ -21,6 +21,7 @@ __all__ = [
     "MAX_EXPERTS", "MAX_TOPK", "MoeqError", "moe_abi_version", "moe_status_string",
     "moe_plan_size", "moe_router_logits", "moe_route_topk", "quant_fp8_per_token", "moe_permute",
     "moe_route_quant_permute", "pack_int4_g128", "tile_int4_weights", "moe_requant_fp8_fnuz",
+    "moe_read_bandwidth_probe", "READ_PROBE_BLOCKS",
     "moe_grouped_gemm_w4a8", "moe_grouped_gemm_w4a8_bf16s", "moe_grouped_gemm_nvfp4",
     "moe_grouped_gemm_aqlm",
     "moe_expert_mlp_w4a8", "moe_expert_mlp_w4a8_noalloc", "NOALLOC_SCRATCH_BYTES",
@@ -36,6 +37,7 @@ TILE_M = 64
 MAX_EXPERTS, MAX_TOPK = 1024, 8
 PLAN_HEADER = 16
 NOALLOC_SCRATCH_BYTES = 32 << 20     # MOEQ_NOALLOC_SCRATCH_BYTES
+READ_PROBE_BLOCKS = 8192             # MOEQ_READ_PROBE_BLOCKS
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -56,6 +58,7 @@ _SIGNATURES = {
     "pack_int4_g128": (_I, [_P, _I64, _I, _P, _P, _P]),
     "pack_int4_g128_bf16s": (_I, [_P, _I64, _I, _P, _P, _P]),
     "moe_tile_int4_weights": (_I, [_P, _I64, _I, _P, _P]),
+    "moe_read_bandwidth_probe": (_I, [_P, _SZ, _P, _P]),
     "moe_requant_fp8_fnuz": (_I, [_P, _P, _I64, _I, _P, _P, _P]),
     "moe_grouped_gemm_w4a8": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_grouped_gemm_fp8row": (_I, [_P, _P, _P, _SZ, _I, _I, _P, _P, _I, _I, _I, _P, _I, _P]),
@@ -302,6 +305,23 @@ def moe_route_quant_permute(logits: torch.Tensor, x: torch.Tensor, k: int,
         _ptr(o["plan"]), o["plan"].numel() * 4, _stream(dev)))
     _mark_plan(o["plan"], E, R)
     return o
+
+
+def moe_read_bandwidth_probe(buf: torch.Tensor, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Streams every byte of the contiguous device tensor buf (a measurement helper,
+    not a layer step); returns sink, READ_PROBE_BLOCKS * 4 uint32 words (as int32)
+    whose XOR is the XOR of buf's 32-bit words."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(READ_PROBE_BLOCKS * 4, dtype=torch.int32, device=buf.device)
+    _req(sink, "sink", torch.int32, 1)
+    if sink.numel() < READ_PROBE_BLOCKS * 4:
+        raise ValueError("sink too small")
+    _check("moe_read_bandwidth_probe", lib.moe_read_bandwidth_probe(
+        _ptr(buf), nbytes, _ptr(sink), _stream(buf.device)))
+    return sink
 
 
 def tile_int4_weights(w_packed: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:

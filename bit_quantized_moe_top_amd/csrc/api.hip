@@ -177,6 +177,14 @@ int pack_int4_g128_bf16s(const float* w, int64_t rows, int K, uint8_t* packed, u
   return pack_common(w, rows, K, packed, scales, 1, stream);
 }
 
+int moe_read_bandwidth_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return MOEQ_OK;
+  if (!buf || !sink || !aligned16(buf) || bytes % 16 != 0 || bytes > (size_t(1) << 40))
+    return MOEQ_ERR_INVALID_ARG;
+  if (int rc = check_device()) return rc;
+  return launch_status(moeq::launch_read_probe(buf, int64_t(bytes), sink, as_stream(stream)));
+}
+
 int moe_tile_int4_weights(const uint8_t* w_packed, int64_t rows, int K, uint8_t* w_tiled,
                           void* stream) {
   if (rows < 0 || K <= 0) return MOEQ_ERR_INVALID_ARG;

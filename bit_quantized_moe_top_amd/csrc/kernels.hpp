@@ -77,6 +77,10 @@ hipError_t launch_permute_quant(const int32_t* ids, int T, int k, int E, const v
                                 float* xp_s, void* plan, hipStream_t stream);
 hipError_t launch_requant_fnuz(const uint8_t* w_fnuz, const float* s_fnuz, int64_t rows, int K,
                                uint8_t* w_ocp, float* s_ocp, hipStream_t stream);
+// streaming read of bytes (a multiple of 16) from buf; one XOR word per wave
+// into sink [MOEQ_READ_PROBE_BLOCKS * 4]
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 // packed INT4 rows [rows][K/2] -> the tiled order [rows/16][K/128][16][64]
 // (rows % 16 == 0, K % 128 == 0, 16-byte aligned, no overlap)
 hipError_t launch_tile_int4(const uint8_t* packed, int64_t rows, int K, uint8_t* tiled,

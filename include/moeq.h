@@ -231,6 +231,26 @@ int pack_int4_g128_bf16s(const float* w, int64_t rows, int K, uint8_t* packed, u
                          void* stream);
 
 /*
+ * moe_read_bandwidth_probe -- a measurement helper, not a step of the layer:
+ * streams `bytes` from device memory the way a well-fed read stream does (16
+ * bytes per lane, consecutive lanes on consecutive addresses, many independent
+ * loads in flight per thread, MOEQ_READ_PROBE_BLOCKS workgroups striding over
+ * the buffer) and stores the XOR of all 32-bit words read, one partial word per
+ * wave, into sink.  Its bytes per second on a buffer much larger than the
+ * device's caches is the practical HBM read ceiling that the weight-streaming
+ * GEMMs are compared against (the 8 TB/s peak is the interface's, not a rate a
+ * kernel reads at).
+ *
+ *   buf  [bytes] device memory, 16-byte aligned, bytes % 16 == 0 (bytes = 0: nothing)
+ *   sink [MOEQ_READ_PROBE_BLOCKS * 4] uint32 (out): the XOR of every sink word
+ *        equals the XOR of every 32-bit word of buf
+ * Errors: MOEQ_ERR_INVALID_ARG for null, misaligned or ragged buffers, or more
+ * than 2^40 bytes.
+ */
+#define MOEQ_READ_PROBE_BLOCKS 8192
+int moe_read_bandwidth_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
+/*
  * moe_tile_int4_weights -- packed INT4 weights (pack_int4_g128's layout, which is
  * the checkpoint's) into the tiled order every INT4 GEMM and expert-MLP call
  * reads (offline weight preparation, once per weight tensor).

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     assert set(names) == set(mq.EXPORTED_SYMBOLS)
 
 
@@ -99,6 +99,12 @@ def test_argument_errors_are_reported_without_a_gpu():
     # pack
     assert L.pack_int4_g128(FAKE, 4, 100, FAKE, FAKE, N) == UNSUPPORTED
     assert L.pack_int4_g128(N, 4, 128, FAKE, FAKE, N) == INVALID
+    # read probe: null, misaligned or ragged buffers; zero bytes is a no-op
+    assert L.moe_read_bandwidth_probe(N, 1024, FAKE, N) == INVALID
+    assert L.moe_read_bandwidth_probe(FAKE, 1000, FAKE, N) == INVALID
+    assert L.moe_read_bandwidth_probe(ctypes.c_void_p(FAKE.value + 4), 1024, FAKE, N) == INVALID
+    assert L.moe_read_bandwidth_probe(FAKE, 1024, N, N) == INVALID
+    assert L.moe_read_bandwidth_probe(N, 0, N, N) == OK
     # tiled order: rows % 16, K % 128, null, misaligned and overlapping buffers
     other = ctypes.c_void_p(FAKE.value + (1 << 20))
     assert L.moe_tile_int4_weights(FAKE, 8, 128, other, N) == UNSUPPORTED

@@ -715,3 +715,18 @@ def test_shared_gemm_bf16(M, N, K):
     acc = a.double().numpy() @ w.double().numpy().T
     assert_close(to_np(none), F.bf16_round(acc), what="none")
     assert_close(to_np(silu), L.silu_mul(acc), what="silu")
+
+
+# ------------------------------------------------------- read-bandwidth probe ----
+@pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 48, 3 << 20, (64 << 20) + 16])
+def test_read_bandwidth_probe_reads_every_word(nbytes):
+    """The probe's sink words XOR to the XOR of every 32-bit word of the buffer
+    (so it really reads all of it, ragged tails included)."""
+    rng = np.random.default_rng(nbytes)
+    words = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32).copy()).to(_dev())
+    sink = mq.moe_read_bandwidth_probe(buf)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert int(got) == int(np.bitwise_xor.reduce(words))
+
