@@ -63,6 +63,8 @@ def parse():
                     help="time only eager launches (default: also replay captured graphs)")
     ap.add_argument("--no-skewed", action="store_true", help="skip the skewed prefill layer")
     ap.add_argument("--no-fp8row", action="store_true", help="skip the row-FP8 prefill layer")
+    ap.add_argument("--no-shares", action="store_true",
+                    help="skip the single-GPU shares of the expert- and width-sharded layer")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the supplementary prefill token sweep (T = 4096 .. 16384)")
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed", "fp8row"])
@@ -633,6 +635,35 @@ def main():
         sres.pop("layers")
         out[name] = prefill_summary(scfg, sres)
         torch.cuda.empty_cache()
+    if not args.no_shares and not args.no_prefill and cfg.name == "decode":
+        import dataclasses
+        # supplementary: what one GPU runs when the layer is sharded over eight
+        # (not one of the named workloads; no collective is timed)
+        shares = {"note": "one GPU's share of the layer sharded over 8 GPUs: EP8 holds 32 of the "
+                          "256 experts and receives 1/8 of the routed rows (T = 2048 -> 1536 rows); "
+                          "TP8 holds 1/8 of every expert's width (w13 512 rows, w2 K = 256)"}
+        for name, base, over in (("ep8_prefill", "prefill", {"E": 32, "T": 256}),
+                                 ("tp8_prefill", "prefill", {"I": 256}),
+                                 ("tp8_decode", "decode", {"I": 256})):
+            scfg = dataclasses.replace(W.get_config(base, **over), name=name)
+            sres = time_layer(scfg, 2 if base == "prefill" else args.sets, max(5, args.steps // 2),
+                              2 if base == "prefill" else args.warmup, dev,
+                              split_events=scfg.R > 64)
+            sres.pop("layers")
+            if base == "prefill":
+                shares[name] = prefill_summary(scfg, sres, short=True)
+            else:
+                sw13, sw2 = expert_bytes(scfg)
+                sms = sres["ms_per_step"]
+                shares[name] = {"ms_per_step": round(sms, 5),
+                                "weight_bytes_per_step": sres["distinct_mean"] * (sw13 + sw2),
+                                "value": round(sres["distinct_mean"] * (sw13 + sw2) / (sms * 1e-3)
+                                               / 1e9, 1), "unit": "GB/s",
+                                "gate_up_gemm_us": round(sres["gate_up_back_to_back_us"], 2),
+                                "per_call_us": {k: round(v, 2)
+                                                for k, v in sres["per_call_us"].items()}}
+            torch.cuda.empty_cache()
+        out["shard_shares"] = shares
     if not args.no_bf16_scales and cfg.name == "decode":
         import dataclasses
         bcfg = dataclasses.replace(cfg, weight_format="w4a8_bf16s")
