@@ -717,6 +717,23 @@ def test_shared_gemm_bf16(M, N, K):
     assert_close(to_np(silu), L.silu_mul(acc), what="silu")
 
 
+@pytest.mark.parametrize("T,H,S", [(64, 256, 128), (300, 512, 384), (1024, 1024, 512)])
+def test_shared_mlp_kernels_vs_oracle(T, H, S):
+    """The shared experts as the layer runs them -- moe_shared_gemm_bf16 with the
+    SiLU-gated epilogue on ws13 [2S, H], then plain on ws2 [H, S] -- against the
+    oracle's shared_mlp (h rounded to bf16 once, fp64 products).  Covers the
+    small-tile (M < 256) and large-tile kernels and a ragged last row tile."""
+    g = torch.Generator().manual_seed(T + H + S)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    ws13 = (torch.randn(2 * S, H, generator=g) * 0.05).to(torch.bfloat16)
+    ws2 = (torch.randn(H, S, generator=g) * 0.05).to(torch.bfloat16)
+    h = mq.moe_shared_gemm_bf16(x.to(_dev()), ws13.to(_dev()), mq.EPI_SILU_MUL)
+    out = mq.moe_shared_gemm_bf16(h, ws2.to(_dev()), mq.EPI_NONE)
+    torch.cuda.synchronize()
+    ref = L.shared_mlp(x.float().numpy(), ws13.float().numpy(), ws2.float().numpy())
+    assert_close(to_np(out), ref, what="shared")
+
+
 # ------------------------------------------------------- read-bandwidth probe ----
 @pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 48, 3 << 20, (64 << 20) + 16])
 def test_read_bandwidth_probe_reads_every_word(nbytes):
