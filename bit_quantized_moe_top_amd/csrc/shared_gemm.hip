@@ -288,9 +288,17 @@ hipError_t launch_big(const uint16_t* a, const uint16_t* w, int M, int N, int K,
 
 }  // namespace
 
+// 256-row tiles (shared_gemm_wide.hip): the tile width for this shape, 0 when
+// they are not taken
+int shared_wide_bn(int M, int N, int K);
+hipError_t launch_shared_gemm_wide(int bn, const uint16_t* a, const uint16_t* w, int M, int N,
+                                   int K, int epilogue, uint16_t* out, hipStream_t stream);
+
 hipError_t launch_shared_gemm_bf16(const uint16_t* a, const uint16_t* w, int M, int N, int K,
                                    int epilogue, uint16_t* out, hipStream_t stream) {
   if (M == 0) return hipSuccess;
+  const int wide_bn = shared_wide_bn(M, N, K);
+  if (wide_bn) return launch_shared_gemm_wide(wide_bn, a, w, M, N, K, epilogue, out, stream);
   if (M >= 256 && K % kBK2 == 0) {
     // 128 x 256 tiles when they give at least two workgroups per CU (512),
     // else 128 x 128

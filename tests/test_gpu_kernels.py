@@ -699,12 +699,18 @@ def test_permute_and_combine_drop_out_of_range_ids(T, k, E, H):
 
 
 # ------------------------------------------------------------- shared GEMM ----
-# M < 256 or K % 32 takes the 128x128 small-tile kernel; the large-tile kernel
-# runs 128x256 tiles when they make >= 512 workgroups, else 128x128 (ragged
-# last row tile, one K step, several column tiles)
+# With K % 64 == 0 and at least 256 tiles of 256 rows: 256x256 tiles (ring of 2
+# slots of 64 K), else 256x128 (ring of 3); ragged last row tile, one slot,
+# fewer slots than the ring holds and more.  Otherwise M < 256 takes the
+# 128x128 small-tile kernel and larger M the 128-row kernel: 128x256 tiles when
+# they make >= 512 workgroups, else 128x128 (ragged last row tile, one K step,
+# several column tiles)
 @pytest.mark.parametrize("M,N,K", [(37, 256, 256), (128, 512, 4096), (200, 128, 96),
                                    (256, 256, 64), (300, 512, 320), (777, 1024, 192),
-                                   (513, 768, 4096), (256, 128, 32), (2000, 8192, 96)])
+                                   (513, 768, 4096), (256, 128, 32), (2000, 8192, 96),
+                                   (2000, 8192, 128), (1000, 8192, 192), (256, 32768, 64),
+                                   (300, 16384, 192), (512, 32768, 64), (2000, 8192, 320),
+                                   (1000, 8192, 448)])
 def test_shared_gemm_bf16(M, N, K):
     g = torch.Generator().manual_seed(M + N + K)
     a = torch.randn(M, K, generator=g).to(torch.bfloat16)
