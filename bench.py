@@ -468,6 +468,32 @@ def prefill_summary(pcfg, pres, short=False):
     return d
 
 
+def torch_shared_gemm_us(cfg, dev, reps=20):
+    """Beside the library's shared-expert GEMMs: torch.matmul (ROCm's BLAS) on
+    the same bf16 shapes, gate/up [T, H] x [H, 2S] and down [T, S] x [S, H]
+    (products only, no SiLU), median microseconds per call."""
+    import torch
+    S = cfg.n_shared * cfg.I
+    g = torch.Generator(device=dev).manual_seed(cfg.seed)
+    out = {}
+    for name, (m, k, n) in (("gate_up", (cfg.T, cfg.H, 2 * S)), ("down", (cfg.T, S, cfg.H))):
+        a = torch.randn(m, k, device=dev, generator=g).to(torch.bfloat16)
+        w = (torch.randn(n, k, device=dev, generator=g) * 0.05).to(torch.bfloat16)
+        wt = w.t()
+        for _ in range(3):
+            torch.matmul(a, wt)
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.matmul(a, wt)
+            e1.record()
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        out[name] = round(sorted(times)[reps // 2], 2)
+    return out
+
+
 def copy_ceiling(dev, nbytes=2 << 30, reps=5):
     """Measured streaming ceilings on this machine: a device-to-device copy of nbytes
     with torch's copy kernel (bytes read + written per second), and the library's
@@ -634,6 +660,8 @@ def main():
         sres = time_layer(scfg, 2, max(5, args.steps // 2), 2, dev, split_events=True)
         sres.pop("layers")
         out[name] = prefill_summary(scfg, sres)
+        if scfg.n_shared:
+            out[name]["shared_bf16"]["torch_matmul_us"] = torch_shared_gemm_us(scfg, dev)
         torch.cuda.empty_cache()
     if not args.no_shares and not args.no_prefill and cfg.name == "decode":
         import dataclasses
