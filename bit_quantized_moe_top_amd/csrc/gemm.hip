@@ -162,132 +162,141 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
   TileInfo ti;
   if (!tile_info(plan, E, R, tile, ti)) return;   // workgroup-uniform
   const int nrb = (ti.rows + 15) >> 4;
+  // Weight loads: an expert with one tile is the only reader of its weight
+  // slice, which is streamed past L2 (kCpStream); the slices of an expert with
+  // several tiles are read once per tile and kept (kCpKeep).  The rest of the
+  // kernel comes in two copies, one per policy: a branch per load would split
+  // the unrolled sweep into basic blocks.
+  const auto body = [&](auto cp) {
+    constexpr int CP = decltype(cp)::value;
+    // (the wave index as a scalar: the weight block bases derived from it stay in
+    // scalar registers)
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ln = lane & 15, kb = lane >> 4;
+    const int G = K >> 7;
 
-  // (the wave index as a scalar: the weight block bases derived from it stay in
-  // scalar registers)
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ln = lane & 15, kb = lane >> 4;
-  const int G = K >> 7;
-
-  // EPI_SILU_MUL: the workgroup takes BN/2 gate rows and the matching up rows;
-  // wave w its 8 CB consecutive gate rows (blocks j < CB/2) and their up rows.
-  // Otherwise wave w takes blocks w, w + 4, ... of the workgroup's BN rows.
-  int col[CB];
-#pragma unroll
-  for (int j = 0; j < CB; ++j) {
-    if (EPI == MOEQ_EPI_SILU_MUL)
-      col[j] = (j < CB / 2 ? 0 : (N >> 1)) + nt * (BN / 2) + wave * (8 * CB) + 16 * (j % (CB / 2));
-    else
-      col[j] = nt * BN + 16 * (wave + 4 * j);
-  }
-  const uint8_t* wblk[CB];
-  const ScaleT<WFMT>* srow[CB];
-  uint32_t wlane;
-  weight_rows<WFMT, CB>(w, w_scale, ti.e, N, K, col, ln, kb, wblk, srow, wlane);
-
-  // A staging: wave w stages rows 16 w .. 16 w + 15 of the 64 x 128 B slice;
-  // load j of lane l takes segment l % 8 (16 bytes) of row 16 w + 8 j + l / 8,
-  // so each load reads 8 whole 128-byte lines.  Waves past the tile's last
-  // 16-row block stage nothing; rows past the tile inside it read the tile's
-  // first row (MFMA rows are independent and those rows are never stored).
-  // The slice of group g is loaded into registers in group g's ring slot,
-  // ahead of its weights in issue order, and written to LDS one group before
-  // its use: waiting for it never waits for the weight loads of later groups.
-  const bool st_on = wave < nrb;                        // wave-uniform
-  const int st_seg = lane & 7;
-  const int st_r0 = 16 * wave + (lane >> 3), st_r1 = st_r0 + 8;
-  const uint8_t* a_src0 = a_q + int64_t(ti.row0 + (st_r0 < ti.rows ? st_r0 : 0)) * K + st_seg * 16;
-  const uint8_t* a_src1 = a_q + int64_t(ti.row0 + (st_r1 < ti.rows ? st_r1 : 0)) * K + st_seg * 16;
-  auto store_a = [&](int buf, const uint4& x0, const uint4& x1) {
-    if (!st_on) return;
-    *reinterpret_cast<uint4*>(&As[buf][st_r0 * kRowDw + st_seg * 4]) =
-        kIsW4<WFMT> ? shuffle_a16(x0) : x0;
-    *reinterpret_cast<uint4*>(&As[buf][st_r1 * kRowDw + st_seg * 4]) =
-        kIsW4<WFMT> ? shuffle_a16(x1) : x1;
-  };
-
-  v4f acc[4][CB];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < CB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  constexpr int kDepth = Shape::kDepth;
-  TileStage<WFMT, CB> st[kDepth];
-  GroupScales<WFMT, Shape::kLdsScales ? 0 : GS, CB> sc;
-  sc.init(srow, kb);
-  if constexpr (Shape::kLdsScales) {
-    // lane (ln, kb) holds groups [kb G/4, (kb+1) G/4) of its rows; made visible
-    // by the barrier before the first group
-    constexpr int kPer = GS / 4;
-#pragma unroll
-    for (int j = 0; j < CB; ++j)
-#pragma unroll
-      for (int i = 0; i < kPer; i += 4) {
-        float fv[4];
-        load_scales<4>(srow[j] + kb * kPer + i, fv);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) Ss[(((kb * kPer + i + t) * 4 + wave) * 16 + ln) * CB + j] = fv[t];
-      }
-  }
-  auto issue = [&](int slot, int g) {
-    if (st_on) {
-      st[slot].a0 = *reinterpret_cast<const uint4*>(a_src0 + g * 128);
-      st[slot].a1 = *reinterpret_cast<const uint4*>(a_src1 + g * 128);
-    }
-#pragma unroll
+    // EPI_SILU_MUL: the workgroup takes BN/2 gate rows and the matching up rows;
+    // wave w its 8 CB consecutive gate rows (blocks j < CB/2) and their up rows.
+    // Otherwise wave w takes blocks w, w + 4, ... of the workgroup's BN rows.
+    int col[CB];
+  #pragma unroll
     for (int j = 0; j < CB; ++j) {
-      st[slot].b[j].load(wblk[j], g * kGroupStride<WFMT>, wlane);
-      if constexpr (!Shape::kLdsScales) st[slot].s[j] = sc.load(j, g);
+      if (EPI == MOEQ_EPI_SILU_MUL)
+        col[j] = (j < CB / 2 ? 0 : (N >> 1)) + nt * (BN / 2) + wave * (8 * CB) + 16 * (j % (CB / 2));
+      else
+        col[j] = nt * BN + 16 * (wave + 4 * j);
     }
-  };
-  auto consume = [&](int slot, int g, bool refill) {
-    const int buf = g & 1;
-    const bool more = g + 1 < G;
-    if (g == 0) {
-      store_a(0, st[slot].a0, st[slot].a1);
-      __syncthreads();
-    }
-    // the next group's slice (its slot is not the one refilled below)
-    const int next = (slot + 1 == kDepth) ? 0 : slot + 1;
-    const uint4 x0 = st[next].a0, x1 = st[next].a1;
-    OperandT<WFMT> bop[CB];
-    float sg[CB];
-#pragma unroll
-    for (int j = 0; j < CB; ++j) bop[j] = st[slot].b[j].operand();
+    const uint8_t* wblk[CB];
+    const ScaleT<WFMT>* srow[CB];
+    uint32_t wlane;
+    weight_rows<WFMT, CB>(w, w_scale, ti.e, N, K, col, ln, kb, wblk, srow, wlane);
+
+    // A staging: wave w stages rows 16 w .. 16 w + 15 of the 64 x 128 B slice;
+    // load j of lane l takes segment l % 8 (16 bytes) of row 16 w + 8 j + l / 8,
+    // so each load reads 8 whole 128-byte lines.  Waves past the tile's last
+    // 16-row block stage nothing; rows past the tile inside it read the tile's
+    // first row (MFMA rows are independent and those rows are never stored).
+    // The slice of group g is loaded into registers in group g's ring slot,
+    // ahead of its weights in issue order, and written to LDS one group before
+    // its use: waiting for it never waits for the weight loads of later groups.
+    const bool st_on = wave < nrb;                        // wave-uniform
+    const int st_seg = lane & 7;
+    const int st_r0 = 16 * wave + (lane >> 3), st_r1 = st_r0 + 8;
+    const uint8_t* a_src0 = a_q + int64_t(ti.row0 + (st_r0 < ti.rows ? st_r0 : 0)) * K + st_seg * 16;
+    const uint8_t* a_src1 = a_q + int64_t(ti.row0 + (st_r1 < ti.rows ? st_r1 : 0)) * K + st_seg * 16;
+    auto store_a = [&](int buf, const uint4& x0, const uint4& x1) {
+      if (!st_on) return;
+      *reinterpret_cast<uint4*>(&As[buf][st_r0 * kRowDw + st_seg * 4]) =
+          kIsW4<WFMT> ? shuffle_a16(x0) : x0;
+      *reinterpret_cast<uint4*>(&As[buf][st_r1 * kRowDw + st_seg * 4]) =
+          kIsW4<WFMT> ? shuffle_a16(x1) : x1;
+    };
+
+    v4f acc[4][CB];
+  #pragma unroll
+    for (int i = 0; i < 4; ++i)
+  #pragma unroll
+      for (int j = 0; j < CB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    constexpr int kDepth = Shape::kDepth;
+    TileStage<WFMT, CB> st[kDepth];
+    GroupScales<WFMT, Shape::kLdsScales ? 0 : GS, CB> sc;
+    sc.init(srow, kb);
     if constexpr (Shape::kLdsScales) {
-      const float4 f = *reinterpret_cast<const float4*>(&Ss[((g * 4 + wave) * 16 + ln) * CB]);
-      sg[0] = f.x; sg[1] = f.y; sg[2] = f.z; sg[3] = f.w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < CB; ++j) sg[j] = sc.get(j, g, ln, st[slot].s[j]);
+      // lane (ln, kb) holds groups [kb G/4, (kb+1) G/4) of its rows; made visible
+      // by the barrier before the first group
+      constexpr int kPer = GS / 4;
+  #pragma unroll
+      for (int j = 0; j < CB; ++j)
+  #pragma unroll
+        for (int i = 0; i < kPer; i += 4) {
+          float fv[4];
+          load_scales<4>(srow[j] + kb * kPer + i, fv);
+  #pragma unroll
+          for (int t = 0; t < 4; ++t) Ss[(((kb * kPer + i + t) * 4 + wave) * 16 + ln) * CB + j] = fv[t];
+        }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (refill) issue(slot, g + kDepth);
-#pragma unroll
+    auto issue = [&](int slot, int g) {
+      if (st_on) {
+        st[slot].a0 = *reinterpret_cast<const uint4*>(a_src0 + g * 128);
+        st[slot].a1 = *reinterpret_cast<const uint4*>(a_src1 + g * 128);
+      }
+  #pragma unroll
+      for (int j = 0; j < CB; ++j) {
+        st[slot].b[j].template load<CP>(wblk[j], g * kGroupStride<WFMT>, wlane);
+        if constexpr (!Shape::kLdsScales) st[slot].s[j] = sc.load(j, g);
+      }
+    };
+    auto consume = [&](int slot, int g, bool refill) {
+      const int buf = g & 1;
+      const bool more = g + 1 < G;
+      if (g == 0) {
+        store_a(0, st[slot].a0, st[slot].a1);
+        __syncthreads();
+      }
+      // the next group's slice (its slot is not the one refilled below)
+      const int next = (slot + 1 == kDepth) ? 0 : slot + 1;
+      const uint4 x0 = st[next].a0, x1 = st[next].a1;
+      OperandT<WFMT> bop[CB];
+      float sg[CB];
+  #pragma unroll
+      for (int j = 0; j < CB; ++j) bop[j] = st[slot].b[j].operand();
+      if constexpr (Shape::kLdsScales) {
+        const float4 f = *reinterpret_cast<const float4*>(&Ss[((g * 4 + wave) * 16 + ln) * CB]);
+        sg[0] = f.x; sg[1] = f.y; sg[2] = f.z; sg[3] = f.w;
+      } else {
+  #pragma unroll
+        for (int j = 0; j < CB; ++j) sg[j] = sc.get(j, g, ln, st[slot].s[j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (refill) issue(slot, g + kDepth);
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < nrb) {
+          const uint4* ap = reinterpret_cast<const uint4*>(&As[buf][(16 * i + ln) * kRowDw + kb * 8]);
+          const OperandT<WFMT> aop = a_operand_staged<WFMT>(ap[0], ap[1]);
+  #pragma unroll
+          for (int j = 0; j < CB; ++j) accumulate<WFMT>(acc[i][j], aop, bop[j], sg[j]);
+        }
+      }
+      if (more) store_a(buf ^ 1, x0, x1);
+      __syncthreads();
+    };
+    pipeline<kDepth, GS>(G, issue, consume);
+
+  #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i < nrb) {
-        const uint4* ap = reinterpret_cast<const uint4*>(&As[buf][(16 * i + ln) * kRowDw + kb * 8]);
-        const OperandT<WFMT> aop = a_operand_staged<WFMT>(ap[0], ap[1]);
-#pragma unroll
-        for (int j = 0; j < CB; ++j) accumulate<WFMT>(acc[i][j], aop, bop[j], sg[j]);
+        v4f blk[CB];
+  #pragma unroll
+        for (int j = 0; j < CB; ++j) blk[j] = acc[i][j];
+        store_block<WFMT, EPI, CB>(blk, i, ti.row0, ti.rows, [a_s](int p, int) { return a_s[p]; }, srow,
+                                   col, ln, kb, N, out, out_f32);
       }
     }
-    if (more) store_a(buf ^ 1, x0, x1);
-    __syncthreads();
   };
-  pipeline<kDepth, GS>(G, issue, consume);
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (i < nrb) {
-      v4f blk[CB];
-#pragma unroll
-      for (int j = 0; j < CB; ++j) blk[j] = acc[i][j];
-      store_block<WFMT, EPI, CB>(blk, i, ti.row0, ti.rows, [a_s](int p, int) { return a_s[p]; }, srow,
-                                 col, ln, kb, N, out, out_f32);
-    }
-  }
+  if (ti.shared_w) body(std::integral_constant<int, kCpKeep>());
+  else body(std::integral_constant<int, kCpStream>());
 }
 
 template <int WFMT, int EPI, int GS>
