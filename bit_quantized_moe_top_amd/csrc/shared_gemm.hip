@@ -1,6 +1,7 @@
 // Dense bf16 GEMM for the shared experts: out = epilogue(a @ w^T), fp32 accumulate,
-// on v_mfma_f32_16x16x32_bf16.  Two tilings: the large-tile kernel below for
-// prefill-sized M, the small-tile one for small M or shapes it does not cover.
+// on v_mfma_f32_16x16x32_bf16.  Three tilings: 256-row tiles (shared_gemm_wide.hip)
+// when they give every CU a workgroup, the 128-row large-tile kernel below for
+// other prefill-sized M, the small-tile one for small M or shapes neither covers.
 //
 // Workgroup tile: 128 rows of a x 128 rows of w (the weight rows: for EPI_NONE
 // the 128 output columns nt*128.., for EPI_SILU_MUL the 64 gate rows nt*64..

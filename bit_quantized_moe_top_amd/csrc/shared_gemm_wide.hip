@@ -247,7 +247,9 @@ hipError_t launch_wide(const uint16_t* a, const uint16_t* w, int M, int N, int K
 }  // namespace
 
 int shared_wide_bn(int M, int N, int K) {
-  if (M <= 0 || K % kBKs != 0) return 0;
+  // (the buffer loads address a tile's rows with 32-bit offsets: at most 256
+  // rows of 2 K bytes, so K stays below 2^21)
+  if (M <= 0 || K % kBKs != 0 || K >= (1 << 21)) return 0;
   // 256 x 256 tiles when they give every CU a workgroup, else 256 x 128
   const int64_t mtiles = (M + kBMw - 1) / kBMw;
   if (N % 256 == 0 && mtiles * (N / 256) >= 256) return 256;
