@@ -49,8 +49,17 @@ __host__ __device__ constexpr int ring_slots() { return BN == 256 ? 2 : 3; }
 template <int BN>
 __host__ __device__ constexpr size_t wide_lds_bytes() { return size_t(ring_slots<BN>()) * slot_bytes<BN>(); }
 
-// position of 16-byte chunk c of row r: c ^ swz(r), swz over r mod 16
-__device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
+// Position of 16-byte chunk c of row r: c ^ swz(r), swz(r) = (r mod 16) / 2.
+// An operand read takes chunk kq (the lane's K quarter, kq = lane / 16) of rows
+// ln = lane % 16.  The LDS serves a 16-byte read 32 lanes at a time over
+// 128 banks (512 bytes): lanes 0..31 (kq 0, 1) and 32..63 (kq 2, 3) must then
+// address distinct 16-byte slots modulo 512 bytes, i.e. rows ln, ln + 4,
+// ln + 8, ln + 12 (same slot group) must differ in swz(r) / 2 -- which r / 2
+// does.  (Measured: swz(r) = (r ^ (r / 8)) mod 8, distinct only over 16
+// consecutive lanes, cost 4 bank-conflict cycles per read, doubling each
+// read's LDS time; the 64-byte rows of a 32-K slot with
+// swz = ((r / 2) ^ (r / 4)) mod 4 had none.)
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base) {
   // word 3: 32-bit data format (untyped access); offsets stay below 2^31
@@ -93,15 +102,16 @@ shared_gemm_wide_kernel(const uint16_t* __restrict__ a, const uint16_t* __restri
   const int ln = lane & 15, kq = lane >> 4;
 
   // loads: lane -> row lr = lane / 8 of an 8-row load (row group g), LDS chunk
-  // lane % 8, which holds K chunk (lane % 8) ^ swz(8 g + lr); swz(8 g + lr) is
-  // lr ^ (g & 1).  Wave v loads A row groups AJ v + j (rows past M re-read the
-  // last row: their results are never stored) and B-tile row groups BJ v + j.
+  // lane % 8, which holds K chunk (lane % 8) ^ swz(8 g + lr), i.e. swz(lr) for
+  // even g and swz(8 + lr) for odd g.  Wave v loads A row groups AJ v + j
+  // (rows past M re-read the last row: their results are never stored) and
+  // B-tile row groups BJ v + j.
   // The first BN/2 B-tile rows are weight rows lo_row.., the rest hi_row..
   // (with EPI_SILU_MUL the gate rows and the matching up rows): waves 0..3
   // load lo rows, waves 4..7 hi rows.
   const int lr = lane >> 3;
-  const uint32_t chunk0 = uint32_t(((lane & 7) ^ lr) * 16);        // even row groups
-  const uint32_t chunk1 = uint32_t(((lane & 7) ^ lr ^ 1) * 16);    // odd row groups
+  const uint32_t chunk0 = uint32_t(((lane & 7) ^ swz(lr)) * 16);       // even row groups
+  const uint32_t chunk1 = uint32_t(((lane & 7) ^ swz(8 + lr)) * 16);   // odd row groups
   const uint32_t row_bytes = uint32_t(K) * 2u;
   const int a_rows = min(kBMw, M - m0);
   const __amdgpu_buffer_rsrc_t ares = rows_rsrc(a + int64_t(m0) * K);
