@@ -176,6 +176,26 @@ def touch(*tensors):
             torch.sum(t.view(torch.uint8), dtype=torch.int64)
 
 
+SETTLE_S = 0.2
+
+
+def settle(run, n_sets, seconds=SETTLE_S):
+    """Untimed: runs the step function run(i) for about `seconds`, in chunks of 50
+    steps between synchronizations, before the W warm-up steps.  Over the first
+    tenths of a second of sustained work the clocks ramp up and per-step times
+    fall (measured at T = 4: 68.0 us per step over the first 200 steps, 66.1 us
+    over 2000), so a short timed region taken right after weight generation
+    would depend on how long the warm-up is."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(50):
+            run(i % n_sets)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def time_layer(cfg, n_sets, steps, warmup, dev, graph=False, split_events=False, layers=None):
     """Times `steps` layer passes; returns timings and the per-call launch times
     (with split_events the expert MLP's three calls are timed one by one).
@@ -193,9 +213,13 @@ def time_layer(cfg, n_sets, steps, warmup, dev, graph=False, split_events=False,
         distinct.append(len(torch.unique(ids)))
     torch.cuda.synchronize()
 
-    # Warm up, then time `steps` whole-layer passes (wall clock between device
-    # synchronizations) and, in a second identical pass, each call's launch
+    # Settle, warm up, then time `steps` whole-layer passes (wall clock between
+    # device synchronizations) and, in a second identical pass, each call's launch
     # duration with events on the stream it runs on (the current torch stream).
+    def run(i):
+        layer, inp = layers[i]
+        layer.forward(inp["x"], inp["logits"], inp["bias"])
+    settle(run, n_sets)
     for i in range(warmup):
         layer, inp = layers[i % n_sets]
         layer.forward(inp["x"], inp["logits"], inp["bias"])
@@ -313,6 +337,11 @@ def time_hybrid(cfg, n_sets, steps, warmup, dev):
         nh = len(touched & hot)
         n_hot_touched.append(nh)
         step_bytes.append(nh * hot_b + (len(touched) - nh) * cold_b + book_b)
+
+    def run(i):
+        layer, inp, _ = layers[i]
+        layer.forward(inp["x"], inp["logits"], inp["bias"])
+    settle(run, n_sets)
     for i in range(warmup):
         layer, inp, _ = layers[i % n_sets]
         layer.forward(inp["x"], inp["logits"], inp["bias"])
@@ -596,7 +625,7 @@ def main():
         "metric": METRIC,
         "value": round(gbs if cfg.name == "decode" else tflops, 3),
         "unit": "GB/s" if cfg.name == "decode" else "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_s": SETTLE_S,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8e4m3 x int4->e4m3, fp32 accumulate",

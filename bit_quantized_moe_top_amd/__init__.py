@@ -128,6 +128,19 @@ def _req(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None):
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
 
 
+def _out(o: dict, name: str, shape: tuple, dtype, dev: torch.device) -> torch.Tensor:
+    """o[name]: the caller's tensor, checked against the shape and dtype the call
+    writes, or a new one (allocated only when o has none)."""
+    t = o.get(name)
+    if t is None:
+        t = o[name] = torch.empty(shape, dtype=dtype, device=dev)
+    elif (t.dtype != dtype or t.shape != shape or t.device != dev or
+          not t.is_contiguous()):
+        raise ValueError(f"out[{name!r}] must be a contiguous {dtype} tensor of shape {shape} "
+                         f"on {dev}, got {t.dtype} {tuple(t.shape)} on {t.device}")
+    return t
+
+
 def _weight_bytes(t: torch.Tensor, name: str) -> torch.Tensor:
     """Packed INT4 weights as bytes: uint8 [..., K/2] as they are, or the checkpoint's
     int32 [..., K/8] .weight_packed words viewed as their little-endian bytes."""
@@ -291,13 +304,16 @@ def moe_route_quant_permute(logits: torch.Tensor, x: torch.Tensor, k: int,
     if bias is not None:
         _req(bias, "bias", torch.float32, 1)
     o = dict(out) if out is not None else {}
-    o.setdefault("ids", torch.empty(T, k, dtype=torch.int32, device=dev))
-    o.setdefault("w", torch.empty(T, k, dtype=torch.float32, device=dev))
-    o.setdefault("x_q", torch.empty(T, H, dtype=torch.uint8, device=dev))
-    o.setdefault("x_s", torch.empty(T, dtype=torch.float32, device=dev))
-    o.setdefault("plan", torch.empty((moe_plan_size(E, R) + 3) // 4, dtype=torch.int32, device=dev))
-    o.setdefault("xp_q", torch.empty(R, H, dtype=torch.uint8, device=dev))
-    o.setdefault("xp_s", torch.empty(R, dtype=torch.float32, device=dev))
+    _out(o, "ids", (T, k), torch.int32, dev)
+    _out(o, "w", (T, k), torch.float32, dev)
+    _out(o, "x_q", (T, H), torch.uint8, dev)
+    _out(o, "x_s", (T,), torch.float32, dev)
+    if o.get("plan") is None:
+        o["plan"] = torch.empty((moe_plan_size(E, R) + 3) // 4, dtype=torch.int32, device=dev)
+    else:
+        _req(o["plan"], "out['plan']", torch.int32, 1)
+    _out(o, "xp_q", (R, H), torch.uint8, dev)
+    _out(o, "xp_s", (R,), torch.float32, dev)
     dt = MOEQ_BF16 if x.dtype == torch.bfloat16 else MOEQ_F32
     _check("moe_route_quant_permute", lib.moe_route_quant_permute(
         _ptr(logits), _ptr(bias), T, E, k, 1 if renormalize else 0, _ptr(x), dt, H, _ptr(o["ids"]),
@@ -541,10 +557,10 @@ def _expert_mlp(fn_name: str, xp_q, xp_s, plan, E, w13, s13, w2, s2, H, I, out):
         raise ValueError("xp_q has the wrong H")
     dev = xp_q.device
     o = dict(out) if out is not None else {}
-    o.setdefault("h", torch.empty(R, I, dtype=torch.bfloat16, device=dev))
-    o.setdefault("h_q", torch.empty(R, I, dtype=torch.uint8, device=dev))
-    o.setdefault("h_s", torch.empty(R, dtype=torch.float32, device=dev))
-    o.setdefault("o", torch.empty(R, H, dtype=torch.bfloat16, device=dev))
+    _out(o, "h", (R, I), torch.bfloat16, dev)
+    _out(o, "h_q", (R, I), torch.uint8, dev)
+    _out(o, "h_s", (R,), torch.float32, dev)
+    _out(o, "o", (R, H), torch.bfloat16, dev)
     fn = getattr(lib, fn_name)
     _check(fn_name, fn(_ptr(xp_q), _ptr(xp_s), _ptr(plan), plan.numel() * 4, E, R, _ptr(w13),
                        _ptr(s13), _ptr(w2), _ptr(s2), H, I, _ptr(o["h"]), _ptr(o["h_q"]),
