@@ -283,18 +283,27 @@ def time_layer(cfg, n_sets, steps, warmup, dev, graph=False, split_events=False,
              out=b["h"])
     for i in range(warmup):
         gate_up(i)
+    # one event pair per launch (the launch's own duration: the host issues the
+    # launches faster than the device runs them, so no host time falls inside a
+    # pair) and one pair around all of them (the period, with the gaps between
+    # consecutive launches)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
     s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s_ev.record()
     for i in range(steps):
+        evs[i][0].record()
         gate_up(i)
+        evs[i][1].record()
     e_ev.record()
     torch.cuda.synchronize()
-    gate_up_us = 1e3 * s_ev.elapsed_time(e_ev) / steps
+    gate_up_period_us = 1e3 * s_ev.elapsed_time(e_ev) / steps
+    gate_up_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / steps
     steps_distinct = [distinct[i % n_sets] for i in range(steps)]
     return {"wall_s": wall, "ms_per_step": 1e3 * wall / steps,
             "graph_ms_per_step": graph_ms,
             "per_call_us": per_call_us, "split_call_us": split_us,
-            "gate_up_back_to_back_us": gate_up_us,
+            "gate_up_back_to_back_us": gate_up_us, "gate_up_period_us": gate_up_period_us,
             "distinct_mean": sum(steps_distinct) / steps, "distinct_per_set": distinct,
             "layers": layers}
 
@@ -643,7 +652,10 @@ def main():
                      "traffic": (traffic or {}).get("bytes_per_launch"),
                      "traffic_detail": traffic,
                      "avg_launch_us": round(dom_us, 3),
-                     "timing": "events around back-to-back launches on the launch stream",
+                     "launch_period_us": round(res["gate_up_period_us"], 3),
+                     "timing": "an event pair around each of `steps` back-to-back launches on the "
+                               "launch stream (launch_period_us: one pair around all of them, "
+                               "with the gaps between launches)",
                      "bytes_per_launch": dom_bytes},
         "layer_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "launch_mode": "hip graph replay" if ms_graph and ms_graph <= ms_eager else "eager",
