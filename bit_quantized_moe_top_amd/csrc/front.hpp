@@ -223,6 +223,72 @@ struct RowQuant {
   }
 };
 
+// A row quantized by the four waves of a 256-thread workgroup: wave q takes the
+// quarter [q K/4, (q + 1) K/4) (K % 32 == 0, K/4 <= 512 CPQ), lane l its 8-element
+// chunks l, l + 64, ...; the four waves' partial maxima meet in LDS at one
+// barrier.  The maximum of the partial maxima is the row maximum, so the scale
+// and codes equal RowQuant's; a row's work is spread over four waves, which
+// keeps four times as many of them, and their loads and stores, in flight.
+template <typename XT, int CPQ>
+struct QuarterRowQuant {
+  XChunk<XT> xc[CPQ];
+  uint2 codes[CPQ];
+  float scale;
+  int c0, chunks;          // the quarter's first element and its 8-element chunks
+  __device__ __forceinline__ void load(const XT* row, int K, int q, int lane) {
+    const int qlen = K >> 2;
+    c0 = q * qlen;
+    chunks = qlen >> 3;
+#pragma unroll
+    for (int i = 0; i < CPQ; ++i)
+      if (lane + kWave * i < chunks) xc[i].load(row + c0 + (lane + kWave * i) * 8);
+  }
+  // called by every thread of the workgroup (one barrier); part: 4 floats of LDS
+  __device__ __forceinline__ void finish(int q, int lane, float* part) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPQ; ++i) {
+      if (lane + kWave * i < chunks) {
+        float v[8];
+        xc[i].values(v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      }
+    }
+    amax = wave_max(amax);
+    if (lane == 0) part[q] = amax;
+    __syncthreads();
+    scale = fp8_scale(fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3])));
+#pragma unroll
+    for (int i = 0; i < CPQ; ++i) {
+      if (lane + kWave * i < chunks) {
+        float v[8];
+        xc[i].values(v);
+        codes[i] = fp8_codes8(v, scale);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* q_row, int lane) const {
+#pragma unroll
+    for (int i = 0; i < CPQ; ++i)
+      if (lane + kWave * i < chunks)
+        *reinterpret_cast<uint2*>(q_row + c0 + (lane + kWave * i) * 8) = codes[i];
+  }
+};
+
+// 8-element chunks per lane of a quarter row (QuarterRowQuant), 0 where rows of K
+// take RowQuant instead: the quarters need K % 32 == 0, and for K below 1024 a
+// quarter leaves most lanes of its wave idle.  (Used where each row is stored
+// k + 1 times, the quantization fused with the scatter: there the four waves'
+// stores in flight pay -- 35.1 against 36.9 us for the T = 2048 front end --
+// while the plain quantization of h, one store per row, ran slower this way:
+// 23.9 against 20.4 us for 12288 rows of 2048.)
+__host__ __device__ inline int quarter_quant_cpq(int K) {
+  if (K % 32 != 0 || K < 1024) return 0;
+  const int c = (K / 4 + 8 * kWave - 1) / (8 * kWave);
+  return c <= 1 ? 1 : c <= 2 ? 2 : 0;
+}
+
 // chunks per lane for a row of K elements held by one wave (0: K too large)
 __host__ __device__ inline int row_quant_cpl(int K) {
   const int c = (K + 8 * kWave - 1) / (8 * kWave);

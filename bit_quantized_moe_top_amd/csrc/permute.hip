@@ -169,7 +169,8 @@ place_gather_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
 }
 
 // Quantization of x fused with the scatter (moe_route_quant_permute at larger
-// T): one wave per token quantizes its row in registers (RowQuant), writes the
+// T), for rows the quarter form below does not take: one wave per token
+// quantizes its row in registers (RowQuant), writes the
 // codes and scale to x_q / x_s and to the k plan positions of the token's
 // rows.  kPlace: the positions are placed here (chunk base + rank, after
 // chunk_rank_kernel and plan_scan_kernel); otherwise the plan is complete and
@@ -198,6 +199,36 @@ quant_scatter_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
     if (p < 0) continue;
     rq.store(xp_q + int64_t(p) * H, H, lane);
     if (lane == 0) xp_s[p] = rq.scale;
+  }
+}
+
+// The same with one 256-thread workgroup per token, each wave quantizing and
+// scattering a quarter of the row (QuarterRowQuant): four times the waves, and
+// their stores, in flight.  Wave 0 places (or reads) the k positions, after its
+// loads are issued.
+template <typename XT, int CPQ, bool kPlace>
+__global__ void __launch_bounds__(256)
+quant_scatter_quarter_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                             int32_t* __restrict__ plan, const XT* __restrict__ x, int H,
+                             uint8_t* __restrict__ x_q, float* __restrict__ x_s,
+                             uint8_t* __restrict__ xp_q, float* __restrict__ xp_s) {
+  __shared__ float part[4];
+  __shared__ int s_pos[MOEQ_MAX_TOPK];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = blockIdx.x;
+  PlanView pv = plan_view(plan, E, T * k);
+  QuarterRowQuant<XT, CPQ> rq;
+  rq.load(x + int64_t(t) * H, H, w, lane);
+  if (w == 0 && lane < k)
+    s_pos[lane] = kPlace ? place_row(ids, t * k + lane, E, pv) : pv.row_pos[t * k + lane];
+  rq.finish(w, lane, part);               // its barrier also publishes s_pos
+  rq.store(x_q + int64_t(t) * H, lane);
+  if (threadIdx.x == 0) x_s[t] = rq.scale;
+  for (int j = 0; j < k; ++j) {
+    const int p = s_pos[j];
+    if (p < 0) continue;
+    rq.store(xp_q + int64_t(p) * H, lane);
+    if (threadIdx.x == 0) xp_s[p] = rq.scale;
   }
 }
 
@@ -264,6 +295,25 @@ hipError_t launch_permute_quant(const int32_t* ids, int T, int k, int E, const v
                        stream, T, k, E, p);
   }
   if ((err = hipGetLastError()) != hipSuccess || T == 0) return err;
+  if (const int cpq = quarter_quant_cpq(H)) {
+    auto go = [&](auto xt, auto cpq_tag) {
+      using XT = typename decltype(xt)::type;
+      constexpr int CPQ = decltype(cpq_tag)::value;
+      const XT* xx = static_cast<const XT*>(x);
+      if (place)
+        hipLaunchKernelGGL((quant_scatter_quarter_kernel<XT, CPQ, true>), dim3(unsigned(T)),
+                           dim3(256), 0, stream, ids, T, k, E, p, xx, H, x_q, x_s, xp_q, xp_s);
+      else
+        hipLaunchKernelGGL((quant_scatter_quarter_kernel<XT, CPQ, false>), dim3(unsigned(T)),
+                           dim3(256), 0, stream, ids, T, k, E, p, xx, H, x_q, x_s, xp_q, xp_s);
+      return hipGetLastError();
+    };
+    struct Bf16 { using type = uint16_t; };
+    struct F32 { using type = float; };
+    if (x_dtype == MOEQ_BF16)
+      return cpq == 1 ? go(Bf16{}, SlotsTag<1>{}) : go(Bf16{}, SlotsTag<2>{});
+    return cpq == 1 ? go(F32{}, SlotsTag<1>{}) : go(F32{}, SlotsTag<2>{});
+  }
   const dim3 grid(unsigned((T + 3) / 4));
   return with_row_quant_cpl(H, [&](auto cpl) {
     constexpr int CPL = decltype(cpl)::value;

@@ -101,3 +101,17 @@ def test_expert_mlp_argument_errors():
     with pytest.raises(ValueError):                     # packed rows not in the tiled order
         mq.moe_expert_mlp_w4a8(z, s, plan, torch.zeros(8, 256, 64, dtype=torch.uint8,
                                                        device=_dev()), s13, w2, s2)
+    # output buffers the caller passes are checked, not trusted
+    for bad in ({"h": torch.empty(4, 64, dtype=torch.bfloat16, device=_dev())},      # shape
+                {"h_q": torch.empty(4, 128, dtype=torch.int8, device=_dev())},        # dtype
+                {"o": torch.empty(128, 4, dtype=torch.bfloat16, device=_dev()).t()},  # strides
+                {"h_s": torch.empty(4)}):                                             # host
+        with pytest.raises(ValueError):
+            mq.moe_expert_mlp_w4a8(z, s, plan, w13, s13, w2, s2, out=bad)
+    logits = torch.zeros(1, 8, device=_dev())
+    x = torch.zeros(1, 128, dtype=torch.bfloat16, device=_dev())
+    with pytest.raises(ValueError):
+        mq.moe_route_quant_permute(logits, x, 4, out={"xp_q": torch.empty(4, 64, dtype=torch.uint8,
+                                                                         device=_dev())})
+    with pytest.raises(TypeError):                     # a float plan buffer
+        mq.moe_route_quant_permute(logits, x, 4, out={"plan": torch.empty(8, device=_dev())})
