@@ -318,8 +318,13 @@ def test_permute_plan_only_and_empty():
 # one-wave plan (R <= 64) with the plan wave outside (T = 4, 5) or inside (T = 8)
 # the quantizing waves, workgroup plan (R > 64), a row narrower than a wave
 # (H = 48), the largest fused rows (T = 16, H = 2048), the separate-kernel
-# fallbacks (T > 16, or rows too long), a single expert, a hot expert, no tokens
+# fallbacks (T > 16, or rows too long), a single expert, a hot expert, no tokens;
+# T > 16 with H % 32 == 0 and H >= 1024 takes the quarter-row quantization and
+# scatter: bf16 and fp32 x, one and two chunks per lane (H = 3072: a partial
+# second chunk), the plan built in one workgroup (R <= 1024) or placed per row
 @pytest.mark.parametrize("T,E,k,H,dtype,hot", [
+    (40, 64, 6, 2048, torch.bfloat16, False), (33, 100, 4, 1024, torch.float32, False),
+    (200, 256, 6, 4096, torch.float32, True), (1100, 16, 1, 3072, torch.bfloat16, False),
     (4, 256, 6, 4096, torch.bfloat16, False), (1, 8, 2, 256, torch.float32, False),
     (5, 256, 6, 4096, torch.float32, False), (8, 256, 6, 4096, torch.bfloat16, False),
     (16, 1000, 8, 512, torch.bfloat16, False), (8, 64, 8, 48, torch.bfloat16, False),
