@@ -146,7 +146,17 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
   constexpr int CB = Shape::CB;
   constexpr int BN = 64 * CB;                           // weight rows per workgroup
   __shared__ uint32_t As[2][MOEQ_TILE_M * kRowDw];
-  __shared__ float Ss[Shape::kLdsScales ? GS * 4 * 16 * CB : 1];
+  // The group scales (staged once, read by every group of the sweep) and, after
+  // the sweep's last barrier, the workgroup's bf16 output tile in the same LDS:
+  // OC columns (the SiLU-gated product has half as many as the weight rows),
+  // rows OS bytes apart (16 bytes of padding spread the rows over the banks).
+  constexpr int kSsFloats = Shape::kLdsScales ? GS * 4 * 16 * CB : 1;
+  constexpr int OC = (EPI == MOEQ_EPI_SILU_MUL) ? BN / 2 : BN;
+  constexpr int OS = OC * 2 + 16;
+  constexpr int kOsFloats = MOEQ_TILE_M * OS / 4;
+  __shared__ __align__(16) float SsOs[kSsFloats > kOsFloats ? kSsFloats : kOsFloats];
+  float* const Ss = SsOs;
+  uint8_t* const Os = reinterpret_cast<uint8_t*>(SsOs);
 
   // Consecutive block ids go to XCDs round-robin; within each run of
   // 8 * n_ntiles ids, XCD x takes the n_ntiles N-tiles of one row tile, so every
@@ -284,6 +294,49 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
     };
     pipeline<kDepth, GS>(G, issue, consume);
 
+    if (!out_f32 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+      // bf16 output: each value as store_block forms it, parked in LDS (over
+      // the group scales, which the sweep's last barrier has retired), then
+      // the tile's rows written 16 bytes per lane (a lane holds one column of
+      // four rows per block, which stored directly is a 2-byte store each)
+      float rs[CB];
+      row_scales<WFMT, CB>(srow, rs);
+      const int oc0 = EPI == MOEQ_EPI_SILU_MUL ? nt * (BN / 2) : nt * BN;   // first output column
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < nrb) {
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int r_in = 16 * i + 4 * kb + v;
+            if (r_in >= ti.rows) continue;
+            const float sa = a_s[ti.row0 + r_in];
+            uint16_t* orow = reinterpret_cast<uint16_t*>(Os + r_in * OS);
+            if constexpr (EPI == MOEQ_EPI_SILU_MUL) {
+  #pragma unroll
+              for (int j = 0; j < CB / 2; ++j) {
+                const float v0 = sa * acc[i][j][v] * rs[j];
+                const float v1 = sa * acc[i][j + CB / 2][v] * rs[j + CB / 2];
+                orow[col[j] - oc0 + ln] = f32_to_bf16(silu_f32(v0) * v1);
+              }
+            } else {
+  #pragma unroll
+              for (int j = 0; j < CB; ++j)
+                orow[col[j] - oc0 + ln] = f32_to_bf16(sa * acc[i][j][v] * rs[j]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      constexpr int CPR = OC * 2 / 16;               // 16-byte chunks of an output row
+      const int ldo = EPI == MOEQ_EPI_SILU_MUL ? N / 2 : N;
+      uint16_t* o16 = static_cast<uint16_t*>(out);
+      for (int idx = tid; idx < ti.rows * CPR; idx += kThreads) {
+        const int r = idx / CPR, c = idx - r * CPR;
+        *reinterpret_cast<uint4*>(o16 + int64_t(ti.row0 + r) * ldo + oc0 + 8 * c) =
+            *reinterpret_cast<const uint4*>(Os + r * OS + 16 * c);
+      }
+      return;
+    }
   #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i < nrb) {
