@@ -158,19 +158,47 @@ gemm_tile_kernel(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s,
   float* const Ss = SsOs;
   uint8_t* const Os = reinterpret_cast<uint8_t*>(SsOs);
 
-  // Consecutive block ids go to XCDs round-robin; within each run of
-  // 8 * n_ntiles ids, XCD x takes the n_ntiles N-tiles of one row tile, so every
-  // XCD gets an equal share of the (device-side, unknown here) real tiles.
+  // Work items are (row tile, N-tile) pairs of the plan's tiles.  Consecutive
+  // block ids go to XCDs round-robin (block b to XCD b % 8); XCD x takes a
+  // contiguous run of the items, so an expert's row tiles run on one XCD and
+  // read its weight slices through one L2 instead of once per tile from HBM.
+  // Runs differ by at most one item, and XCD x has at least as many blocks as
+  // items (the grid holds n_ntiles blocks per possible tile).
   const int n_ntiles = N / BN;
-  const int total = n_ntiles * plan_max_tiles(E, R);
-  const int run = kXcds * n_ntiles;
-  const int bid = blockIdx.x;
-  const int logical = (bid / run) * run + (bid % kXcds) * n_ntiles + (bid / kXcds) % n_ntiles;
-  if (logical >= total) return;
-  const int tile = logical / n_ntiles;
-  const int nt = logical - tile * n_ntiles;
+  const PlanView pv = plan_view(const_cast<int32_t*>(plan), E, R);
+  const int n_real = min(max(plan[kPlanTiles], 0), pv.max_tiles);
+  const int items = n_real * n_ntiles;
+  const int x = int(blockIdx.x) % kXcds, i = int(blockIdx.x) / kXcds;
+  const int q = items / kXcds, rem = items - q * kXcds;
+  if (i >= q + (x < rem ? 1 : 0)) return;       // workgroup-uniform
+  const int idx = x * q + min(x, rem) + i;
+  const int tb = idx / n_ntiles;
+  int nt;
   TileInfo ti;
-  if (!tile_info(plan, E, R, tile, ti)) return;   // workgroup-uniform
+  {
+    // Inside an expert's items the N-tile is the major index and the row tile
+    // the minor one: the row tiles that read one weight slice are neighbours in
+    // issue order and stream it together.  The expert's first tile t0 and tile
+    // count m follow from its row offsets (its tiles are consecutive in the list,
+    // 64 rows each from offsets[e] on).
+    const int e = min(max(pv.tile_expert[tb], 0), E - 1);
+    const int r_tb = pv.tile_row0[tb];
+    const int base = min(max(pv.offsets[e], 0), R);
+    const int end = min(max(pv.offsets[e + 1], base), R);
+    const int m = max(1, (end - base + MOEQ_TILE_M - 1) / MOEQ_TILE_M);
+    const int t0 = tb - min(max((r_tb - base) / MOEQ_TILE_M, 0), tb);
+    // (clamps: a plan built for other sizes yields wrong rows, never an access
+    // outside the buffers)
+    const int local = min(max(idx - t0 * n_ntiles, 0), m * n_ntiles - 1);
+    nt = local / m;
+    ti.e = e;
+    ti.row0 = min(base + MOEQ_TILE_M * (local - nt * m), R);
+    ti.rows = max(0, min(MOEQ_TILE_M, end - ti.row0));
+    ti.shared_w = m > 1;
+    // (no exit for a tile without rows, which only a plan built for other sizes
+    // has: it stages and stores nothing, and a late exit test makes the
+    // compiler spill the unrolled sweep)
+  }
   const int nrb = (ti.rows + 15) >> 4;
   // Weight loads: an expert with one tile is the only reader of its weight
   // slice, which is streamed past L2 (kCpStream); the slices of an expert with
@@ -367,9 +395,9 @@ hipError_t launch_kernels(const uint8_t* a_q, const float* a_s, const void* plan
   } else {
     auto tile = [&](auto cb) {
       constexpr int CB = decltype(cb)::value;
-      const int64_t run = int64_t(kXcds) * (N / (64 * CB));
-      const int64_t total = int64_t(N / (64 * CB)) * plan_max_tiles(E, R);
-      const int64_t grid = (total + run - 1) / run * run;
+      // one block per possible work item (the plan's tile count is known on the
+      // device only)
+      const int64_t grid = int64_t(N / (64 * CB)) * plan_max_tiles(E, R);
       hipLaunchKernelGGL((gemm_tile_kernel<WFMT, EPI, GS, CB>), dim3(unsigned(grid)),
                          dim3(kThreads), 0, stream, a_q, a_s, p, E, R, w, w_scale, N, K, out,
                          out_f32);
