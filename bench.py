@@ -573,7 +573,7 @@ def copy_ceiling(dev, nbytes=2 << 30, reps=5):
 
 
 def sclk_mhz():
-    """Current shader clock (MHz) of the GPU(s) from the driver's DPM table, if readable."""
+    """Current shader clock (MHz) of the GPU(s) from the amdgpu kernel driver's DPM table, if readable."""
     import glob
     vals = []
     for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):

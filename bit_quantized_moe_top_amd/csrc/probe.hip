@@ -5,7 +5,7 @@
 // streamed weight loads -- and stores the XOR of everything it read, one word
 // per wave, so the loads cannot be dropped.  Its bytes per second are the
 // device's practical HBM read ceiling against which the grouped GEMMs' weight
-// streams are judged.
+// streams are measured.
 #include "common.hpp"
 #include "kernels.hpp"
 
