@@ -431,7 +431,10 @@ def test_w4a8_integer_exact(T, k, E, N, K, hot):
                                            (4, 6, 24, 512, 4096, None),
                                            # prefill tile kernels (R > 192): K = 4096 and 2048,
                                            # N a multiple of 256, an expert with 5 row tiles
-                                           (300, 2, 6, 512, 4096, 1), (260, 3, 7, 256, 2048, 3)])
+                                           (300, 2, 6, 512, 4096, 1), (260, 3, 7, 256, 2048, 3),
+                                           # 128-row weight tiles (N % 256 != 0), looped K sweep,
+                                           # 40 experts split over the 8 per-XCD runs
+                                           (400, 4, 40, 384, 1024, 5)])
 def test_grouped_gemm_random(fmt, T, k, E, N, K, hot):
     rng = np.random.default_rng(E + N + K + T)
     ids = _case_ids(T, k, E, rng, hot)
