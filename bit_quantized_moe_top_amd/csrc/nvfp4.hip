@@ -22,8 +22,11 @@
 // listed by hot_ids and cold ones as AQLM); tiles of such experts are skipped,
 // so the rows they own are left to the other format's kernel.
 //
-// Structure: the wave kernel of the INT4 path (gemm.hip) -- one wave per (plan
-// tile, 32 weight rows), 128-K chunks through a register ring; lane (n, kb)
+// Structure: the K-split units of the INT4 path's wave kernel (gemm.hip) -- one
+// workgroup per (plan tile, 32 weight rows), wave q sweeping K quarter q in
+// 128-K chunks through a register ring, the quarters summed in LDS in a fixed
+// order and stored by wave 0 (a few hot experts make few units: splitting K
+// puts four times the loads in flight); lane (n, kb)
 // holds K [32 kb, 32 kb + 32) of its row per chunk (16 bytes of codes and the
 // two block scales, one 16-bit load) and feeds four MFMAs of K = 32 (lane kb's
 // 8 K-slots of MFMA j are the chunk's K 32 kb + 8 j .. + 8; the activation
@@ -64,19 +67,20 @@ __global__ void __launch_bounds__(kThreads, 3)
 gemm_nvfp4_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int E, int R,
                   const int32_t* slab_of, int S, const uint8_t* w, const uint8_t* w_bs,
                   const float* w_scale2, int N, int K, void* out, int out_f32) {
-  const int lane = threadIdx.x & 63;
+  __shared__ v4f red[3 * 2 * kWave];            // quarter sums of waves 1..3
+  const int lane = threadIdx.x & 63, q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15, kb = lane >> 4;
   const int units_per_tile = N / 32;
-  const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6));
-  const int tile = unit / units_per_tile;
-  const int u = unit - tile * units_per_tile;
+  const int tile = blockIdx.x / units_per_tile;
+  const int u = blockIdx.x - tile * units_per_tile;
   TileInfo ti;
-  if (!tile_info(plan, E, R, tile, ti)) return;   // wave-uniform
+  if (!tile_info(plan, E, R, tile, ti)) return;   // workgroup-uniform
   // weight slab of the tile's expert; experts stored in another format are skipped
   const int slab = slab_of ? slab_of[ti.e] : ti.e;
-  if (slab < 0 || slab >= S) return;                    // wave-uniform
+  if (slab < 0 || slab >= S) return;                    // workgroup-uniform
   const float scale2 = w_scale2[slab];
   const int G = K >> 7;
+  const int g0 = quarter_g0(G, q), gq = quarter_groups(G, q);   // this wave's K quarter
 
   int col[2];
   unit_columns<EPI, 2>(N, u, col);
@@ -85,14 +89,14 @@ gemm_nvfp4_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int64_t n_glob = int64_t(slab) * N + col[j] + ln;
-    wrow[j] = w + n_glob * (K >> 1);
-    srow[j] = w_bs + n_glob * (K >> 4);
+    wrow[j] = w + n_glob * (K >> 1) + g0 * 64;
+    srow[j] = w_bs + n_glob * (K >> 4) + g0 * 8;
   }
 
   const int nrb = (ti.rows + 15) >> 4;
   for (int rb = 0; rb < nrb; ++rb) {
     const bool a_ok = 16 * rb + ln < ti.rows;
-    const uint8_t* a_src = a_q + int64_t(ti.row0 + (a_ok ? 16 * rb + ln : 0)) * K + kb * 32;
+    const uint8_t* a_src = a_q + int64_t(ti.row0 + (a_ok ? 16 * rb + ln : 0)) * K + g0 * 128 + kb * 32;
     v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
     NvStage st[kNvDepth];
 #pragma unroll
@@ -137,10 +141,12 @@ gemm_nvfp4_kernel(const uint8_t* a_q, const float* a_s, const int32_t* plan, int
 #pragma unroll
       for (int j = 0; j < 2; ++j) pin(acc[j]);
     };
-    pipeline<kNvDepth, 0>(G, issue, consume);
-    store_block<kNvfp4, EPI>(acc, rb, ti.row0, ti.rows,
-                             [a_s, scale2](int p, int) { return a_s[p] * scale2; }, srow, col, ln, kb,
-                             N, out, out_f32);
+    pipeline<kNvDepth, 0>(gq, issue, consume);
+    quarter_reduce<2>(acc, red, q, lane, rb + 1 < nrb);
+    if (q == 0)
+      store_block<kNvfp4, EPI>(acc, rb, ti.row0, ti.rows,
+                               [a_s, scale2](int p, int) { return a_s[p] * scale2; }, srow, col, ln,
+                               kb, N, out, out_f32);
   }
 }
 
@@ -154,7 +160,7 @@ hipError_t launch_grouped_gemm_nvfp4(const uint8_t* a_q, const float* a_s, const
   if (R == 0) return hipSuccess;
   const int out_f32 = out_dtype == MOEQ_F32 ? 1 : 0;
   const int64_t units = int64_t(plan_max_tiles(E, R)) * (N / 32);
-  const dim3 grid(unsigned((units + 3) / 4));
+  const dim3 grid{static_cast<unsigned>(units)};         // one workgroup per unit
   const int32_t* p = static_cast<const int32_t*>(plan);
   if (epilogue == MOEQ_EPI_SILU_MUL)
     hipLaunchKernelGGL(gemm_nvfp4_kernel<MOEQ_EPI_SILU_MUL>, grid, dim3(kThreads), 0, stream, a_q,
